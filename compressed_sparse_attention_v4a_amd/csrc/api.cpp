@@ -1,0 +1,292 @@
+// C ABI of libv4a.so: argument validation, workspace sizing, dispatch.
+// Declarations and their documentation are in include/v4a.h.
+#include "../../include/v4a.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_policy{0};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return V4A_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(V4A_EIO, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_attn_common(const void* q, const void* kv_comp, const void* out, int n_h, int c,
+                      int rope_dims, int w, v4a_dtype dt, int batch, float eps) {
+  REQUIRE(q && kv_comp && out, V4A_EINVAL, "null q, kv_comp or out");
+  REQUIRE(batch >= 1, V4A_EINVAL, "batch must be >= 1 (got %d)", batch);
+  REQUIRE(n_h >= 1, V4A_EINVAL, "n_h must be >= 1 (got %d)", n_h);
+  REQUIRE(c >= 2 && c % 2 == 0, V4A_EINVAL, "c must be even and >= 2 (got %d)", c);
+  REQUIRE(c <= 1024, V4A_ENOTSUP, "c > 1024 is not supported (got %d)", c);
+  REQUIRE(rope_dims >= 0 && rope_dims % 2 == 0 && rope_dims <= c, V4A_EINVAL,
+          "rope_dims must be even and in [0, c] (got %d)", rope_dims);
+  REQUIRE(w >= 1, V4A_EINVAL, "w must be >= 1 (got %d)", w);
+  REQUIRE(dt == V4A_F32 || dt == V4A_BF16, V4A_ENOTSUP, "attention dtype must be F32 or BF16");
+  REQUIRE(eps >= 0.0f && std::isfinite(eps), V4A_EINVAL, "eps must be finite and >= 0");
+  return V4A_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* v4a_last_error(void) { return g_err; }
+
+const char* v4a_version(void) { return "v4a 0.1.0 gfx950"; }
+
+int v4a_set_kernel_policy(int policy) {
+  if (policy != 0 && policy != 1) return g_policy.load();
+  return g_policy.exchange(policy);
+}
+
+int v4a_visibility(int64_t t0, int T, int m, int k, int w, int32_t* E, int32_t* cnt,
+                   int32_t* win_lo, int32_t* win_len, void* stream) {
+  REQUIRE(t0 >= 0 && T >= 0, V4A_EINVAL, "t0 and T must be >= 0");
+  REQUIRE(m >= 1 && w >= 1, V4A_EINVAL, "m and w must be >= 1");
+  REQUIRE(t0 + T <= INT32_MAX, V4A_EINVAL, "t0 + T must fit int32");
+  return hip_status(v4a::launch_visibility(t0, T, m, k, w, E, cnt, win_lo, win_len,
+                                           (hipStream_t)stream),
+                    "v4a_visibility");
+}
+
+int v4a_compress(const void* C, const void* Z, v4a_dtype in_dt, const float* B, int batch,
+                 int64_t n_buf, int64_t tok_base, int64_t t0, int T, int c, int m, int overlap,
+                 const float* gamma, float eps, int rope_dims, float rope_base, void* out,
+                 void* out_scale, v4a_dtype out_dt, int64_t E_cap, void* stream) {
+  REQUIRE(C && Z && B && out, V4A_EINVAL, "null C, Z, B or out");
+  REQUIRE(batch >= 1, V4A_EINVAL, "batch must be >= 1");
+  REQUIRE(c >= 2 && c % 2 == 0, V4A_EINVAL, "c must be even and >= 2 (got %d)", c);
+  REQUIRE(m >= 1, V4A_EINVAL, "m must be >= 1");
+  REQUIRE(overlap == 0 || overlap == 1, V4A_EINVAL, "overlap must be 0 or 1");
+  REQUIRE(T >= 0 && t0 >= 0 && n_buf >= 0 && tok_base >= 0, V4A_EINVAL,
+          "T, t0, n_buf, tok_base must be >= 0");
+  REQUIRE(rope_dims >= 0 && rope_dims % 2 == 0 && rope_dims <= c, V4A_EINVAL,
+          "rope_dims must be even and in [0, c]");
+  REQUIRE(eps >= 0.0f && std::isfinite(eps), V4A_EINVAL, "eps must be finite and >= 0");
+  REQUIRE(in_dt == V4A_F32 || in_dt == V4A_BF16, V4A_ENOTSUP, "in_dt must be F32 or BF16");
+  const int vec = in_dt == V4A_F32 ? 4 : 8;
+  REQUIRE(c % vec == 0, V4A_ENOTSUP, "c must be a multiple of %d for this input dtype", vec);
+  REQUIRE(c / vec <= 256, V4A_ENOTSUP, "c too large (max %d for this input dtype)", 256 * vec);
+  REQUIRE(out_dt == V4A_F32 || out_dt == V4A_BF16 || out_dt == V4A_FP8_E4M3 ||
+              out_dt == V4A_MXFP4,
+          V4A_ENOTSUP, "unknown out_dt");
+  REQUIRE(out_dt != V4A_MXFP4 || c % 32 == 0, V4A_EINVAL, "MXFP4 output needs c %% 32 == 0");
+  REQUIRE((out_dt != V4A_FP8_E4M3 && out_dt != V4A_MXFP4) || out_scale, V4A_EINVAL,
+          "out_scale is required for FP8/MXFP4 output");
+  REQUIRE(aligned(C, 16) && aligned(Z, 16), V4A_EINVAL, "C and Z must be 16-byte aligned");
+  const int64_t i_begin = t0 / m, i_end = (t0 + T) / m;
+  REQUIRE(E_cap >= i_end, V4A_EINVAL, "E_cap (%lld) < last entry + 1 (%lld)", (long long)E_cap,
+          (long long)i_end);
+  if (i_end > i_begin) {
+    const int64_t first = (overlap && i_begin > 0) ? (int64_t)m * (i_begin - 1) : (int64_t)m * i_begin;
+    REQUIRE(tok_base <= first, V4A_EINVAL,
+            "buffer starts at position %lld but entry %lld pools position %lld", (long long)tok_base,
+            (long long)i_begin, (long long)first);
+    REQUIRE(tok_base + n_buf >= (int64_t)m * i_end, V4A_EINVAL,
+            "buffer ends at position %lld but entry %lld needs position %lld",
+            (long long)(tok_base + n_buf), (long long)(i_end - 1), (long long)(m * i_end - 1));
+  }
+  v4a::CompressArgs a{};
+  a.C = C; a.Z = Z; a.B = B; a.gamma = gamma; a.out = out; a.out_scale = out_scale;
+  a.n_buf = n_buf; a.tok_base = tok_base; a.i_begin = i_begin; a.E_cap = E_cap;
+  a.n_entries = (int)(i_end - i_begin); a.batch = batch; a.c = c; a.m = m; a.overlap = overlap;
+  a.rope_dims = rope_dims; a.in_dt = in_dt; a.out_dt = out_dt; a.eps = eps; a.rope_base = rope_base;
+  return hip_status(v4a::launch_compress(a, (hipStream_t)stream), "v4a_compress");
+}
+
+static int indexer_check(const void* qI, const void* qI_scale, const void* KI,
+                         const void* KI_scale, v4a_dtype dt, const float* wI, int batch, int T,
+                         int64_t t0, int n_hI, int cI, int m, int k, int64_t E_cap,
+                         const int32_t* idx, const int32_t* cnt) {
+  REQUIRE(qI && KI && wI && idx && cnt, V4A_EINVAL, "null qI, KI, wI, topk_idx or topk_cnt");
+  REQUIRE(batch >= 1 && T >= 1, V4A_EINVAL, "batch and T must be >= 1");
+  REQUIRE(t0 >= 0 && t0 + T <= INT32_MAX, V4A_EINVAL, "t0 out of range");
+  REQUIRE(n_hI >= 1 && cI >= 1 && m >= 1 && k >= 1, V4A_EINVAL, "n_hI, cI, m, k must be >= 1");
+  REQUIRE(dt == V4A_F32 || dt == V4A_BF16 || dt == V4A_FP8_E4M3 || dt == V4A_MXFP4, V4A_ENOTSUP,
+          "unknown indexer dtype");
+  REQUIRE(cI <= 1024 && (int64_t)n_hI * cI <= 16384, V4A_ENOTSUP,
+          "indexer query too large (cI <= 1024, n_hI*cI <= 16384)");
+  REQUIRE(dt != V4A_MXFP4 || cI % 32 == 0, V4A_EINVAL, "MXFP4 needs cI %% 32 == 0");
+  REQUIRE((dt != V4A_FP8_E4M3 && dt != V4A_MXFP4) || (qI_scale && KI_scale), V4A_EINVAL,
+          "scales are required for FP8/MXFP4");
+  REQUIRE(E_cap >= (t0 + T) / m, V4A_EINVAL, "E_cap smaller than the visible entries");
+  return V4A_OK;
+}
+
+size_t v4a_indexer_topk_workspace(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k,
+                                  v4a_dtype dt) {
+  if (batch < 1 || T < 1 || m < 1 || k < 1 || t0 < 0) return 0;
+  return v4a::indexer_plan(batch, T, t0, n_hI, cI, m, k, dt, g_policy.load()).total;
+}
+
+int v4a_indexer_topk(const void* qI, const void* qI_scale, const void* KI, const void* KI_scale,
+                     v4a_dtype dt, const float* wI, int batch, int T, int64_t t0, int n_hI, int cI,
+                     int m, int k, int64_t E_cap, int32_t* topk_idx, int32_t* topk_cnt,
+                     float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  int rc = indexer_check(qI, qI_scale, KI, KI_scale, dt, wI, batch, T, t0, n_hI, cI, m, k, E_cap,
+                         topk_idx, topk_cnt);
+  if (rc != V4A_OK) return rc;
+  const v4a::IndexerPlan p = v4a::indexer_plan(batch, T, t0, n_hI, cI, m, k, dt, g_policy.load());
+  REQUIRE(ws_bytes >= p.total, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, p.total);
+  REQUIRE(p.total == 0 || (ws && aligned(ws, 256)), V4A_EINVAL, "workspace must be 256-byte aligned");
+  v4a::IndexerArgs a{};
+  a.qI = qI; a.qI_scale = qI_scale; a.KI = KI; a.KI_scale = KI_scale; a.wI = wI;
+  a.topk_idx = topk_idx; a.topk_cnt = topk_cnt; a.topk_score = topk_score;
+  a.t0 = t0; a.E_cap = E_cap; a.batch = batch; a.T = T; a.n_hI = n_hI; a.cI = cI; a.m = m;
+  a.k = k; a.dt = dt;
+  return hip_status(v4a::launch_indexer_topk(a, p, ws, (hipStream_t)stream), "v4a_indexer_topk");
+}
+
+static v4a::AttnArgs attn_args(const void* q, const void* kv_comp, const void* kv_local,
+                               void* kv_ring, const void* kv_new, const int32_t* idx,
+                               const int32_t* cnt, const float* sink, const float* q_gamma,
+                               const float* kv_gamma, float eps, int rope_dims, float rope_base,
+                               float scale, int batch, int64_t t0, int T, int n_h, int c, int k,
+                               int w, int m_prime, int64_t E_cap, int64_t loc_base, int64_t n_loc,
+                               void* out, v4a_dtype dt, int mode, int num_splits) {
+  v4a::AttnArgs a{};
+  a.q = q; a.kv_comp = kv_comp; a.kv_local = kv_local; a.kv_ring = kv_ring; a.kv_new = kv_new;
+  a.idx = idx; a.cnt = cnt; a.sink = sink; a.q_gamma = q_gamma; a.kv_gamma = kv_gamma;
+  a.out = out; a.loc_base = loc_base; a.n_loc = n_loc; a.t0 = t0; a.E_cap = E_cap;
+  a.batch = batch; a.T = T; a.n_h = n_h; a.c = c; a.k = k; a.w = w; a.m_prime = m_prime;
+  a.rope_dims = rope_dims; a.dt = dt; a.mode = mode; a.num_splits = num_splits;
+  a.eps = eps; a.rope_base = rope_base; a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c);
+  return a;
+}
+
+size_t v4a_sparse_mqa_prefill_workspace(int batch, int64_t t0, int T, int64_t loc_base,
+                                        int64_t n_loc, int n_h, int c, int k, int w, v4a_dtype dt) {
+  v4a::AttnArgs a = attn_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, 0, 0, 0, 0, batch, t0, T, n_h, c, k, w, 0,
+                              0, loc_base, n_loc, nullptr, dt, v4a::kModeCSA, 1);
+  return v4a::attn_workspace(a, g_policy.load());
+}
+
+int v4a_sparse_mqa_prefill(const void* q, const void* kv_comp, const void* kv_local,
+                           int64_t loc_base, int64_t n_loc, const int32_t* topk_idx,
+                           const int32_t* topk_cnt, const float* sink, const float* q_gamma,
+                           const float* kv_gamma, float eps, int rope_dims, float rope_base,
+                           float scale, int batch, int64_t t0, int T, int n_h, int c, int k, int w,
+                           int64_t E_cap, void* out, v4a_dtype dt, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_attn_common(q, kv_comp, out, n_h, c, rope_dims, w, dt, batch, eps);
+  if (rc != V4A_OK) return rc;
+  REQUIRE(kv_local && topk_idx && topk_cnt, V4A_EINVAL, "null kv_local, topk_idx or topk_cnt");
+  REQUIRE(T >= 1 && t0 >= 0 && k >= 1 && E_cap >= 1, V4A_EINVAL, "T, k, E_cap must be >= 1");
+  const int64_t need_lo = t0 - w + 1 > 0 ? t0 - w + 1 : 0;
+  REQUIRE(loc_base >= 0 && loc_base <= need_lo && loc_base + n_loc >= t0 + T, V4A_EINVAL,
+          "local rows [%lld, %lld) do not cover the windows [%lld, %lld)", (long long)loc_base,
+          (long long)(loc_base + n_loc), (long long)need_lo, (long long)(t0 + T));
+  v4a::AttnArgs a = attn_args(q, kv_comp, kv_local, nullptr, nullptr, topk_idx, topk_cnt, sink,
+                              q_gamma, kv_gamma, eps, rope_dims, rope_base, scale, batch, t0, T,
+                              n_h, c, k, w, 0, E_cap, loc_base, n_loc, out, dt, v4a::kModeCSA, 1);
+  const size_t need = v4a::attn_workspace(a, g_policy.load());
+  REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
+  REQUIRE(need == 0 || (ws && aligned(ws, 256)), V4A_EINVAL, "workspace must be 256-byte aligned");
+  return hip_status(v4a::launch_attention(a, ws, g_policy.load(), (hipStream_t)stream),
+                    "v4a_sparse_mqa_prefill");
+}
+
+static int decode_splits(int batch, int num_splits, int k, int w) {
+  if (num_splits > 0) return num_splits;
+  // enough workgroups to cover the chip: about 2 per CU over batch * head-groups
+  int s = 1;
+  while (batch * s < 128 && s * 64 < k + w) s *= 2;
+  return s;
+}
+
+size_t v4a_sparse_mqa_decode_workspace(int batch, int n_h, int c, int k, int w, int num_splits,
+                                       v4a_dtype dt) {
+  v4a::AttnArgs a = attn_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, 0, 0, 0, 0, batch, 0, 1, n_h, c, k, w, 0,
+                              0, 0, 0, nullptr, dt, v4a::kModeDecode,
+                              decode_splits(batch, num_splits, k, w));
+  return v4a::attn_workspace(a, g_policy.load());
+}
+
+int v4a_sparse_mqa_decode(const void* q, const void* kv_comp, void* kv_ring, const void* kv_new,
+                          int64_t t, const int32_t* topk_idx, const int32_t* topk_cnt,
+                          const float* sink, const float* q_gamma, const float* kv_gamma,
+                          float eps, int rope_dims, float rope_base, float scale, int batch,
+                          int n_h, int c, int k, int w, int64_t E_cap, int num_splits, void* out,
+                          v4a_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn_common(q, kv_comp, out, n_h, c, rope_dims, w, dt, batch, eps);
+  if (rc != V4A_OK) return rc;
+  REQUIRE(kv_ring && topk_idx && topk_cnt, V4A_EINVAL, "null kv_ring, topk_idx or topk_cnt");
+  REQUIRE(t >= 0 && k >= 1 && E_cap >= 1, V4A_EINVAL, "t must be >= 0, k and E_cap >= 1");
+  REQUIRE(num_splits >= 0 && num_splits <= 64, V4A_EINVAL, "num_splits must be in [0, 64]");
+  const int ns = decode_splits(batch, num_splits, k, w);
+  v4a::AttnArgs a = attn_args(q, kv_comp, kv_ring, kv_ring, kv_new, topk_idx, topk_cnt, sink,
+                              q_gamma, kv_gamma, eps, rope_dims, rope_base, scale, batch, t, 1, n_h,
+                              c, k, w, 0, E_cap, 0, 0, out, dt, v4a::kModeDecode, ns);
+  const size_t need = v4a::attn_workspace(a, g_policy.load());
+  REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
+  REQUIRE(need == 0 || (ws && aligned(ws, 256)), V4A_EINVAL, "workspace must be 256-byte aligned");
+  return hip_status(v4a::launch_attention(a, ws, g_policy.load(), (hipStream_t)stream),
+                    "v4a_sparse_mqa_decode");
+}
+
+size_t v4a_hca_attn_workspace(int batch, int64_t t0, int T, int64_t loc_base, int64_t n_loc,
+                              int n_h, int c, int m_prime, int w, v4a_dtype dt) {
+  v4a::AttnArgs a = attn_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, 0, 0, 0, 0, batch, t0, T, n_h, c, 0, w,
+                              m_prime, 0, loc_base, n_loc, nullptr, dt, v4a::kModeHCA, 1);
+  return v4a::attn_workspace(a, g_policy.load());
+}
+
+int v4a_hca_attn(const void* q, const void* kv_comp, const void* kv_local, int64_t loc_base,
+                 int64_t n_loc, const float* sink, const float* q_gamma, const float* kv_gamma,
+                 float eps, int rope_dims, float rope_base, float scale, int batch, int64_t t0,
+                 int T, int n_h, int c, int m_prime, int w, int64_t E_cap, void* out, v4a_dtype dt,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn_common(q, kv_comp, out, n_h, c, rope_dims, w, dt, batch, eps);
+  if (rc != V4A_OK) return rc;
+  REQUIRE(kv_local, V4A_EINVAL, "null kv_local");
+  REQUIRE(T >= 1 && t0 >= 0 && m_prime >= 1, V4A_EINVAL, "T, m_prime must be >= 1, t0 >= 0");
+  REQUIRE(E_cap >= (t0 + T) / m_prime, V4A_EINVAL, "E_cap smaller than the visible entries");
+  const int64_t need_lo = t0 - w + 1 > 0 ? t0 - w + 1 : 0;
+  REQUIRE(loc_base >= 0 && loc_base <= need_lo && loc_base + n_loc >= t0 + T, V4A_EINVAL,
+          "local rows do not cover the windows");
+  v4a::AttnArgs a = attn_args(q, kv_comp, kv_local, nullptr, nullptr, nullptr, nullptr, sink,
+                              q_gamma, kv_gamma, eps, rope_dims, rope_base, scale, batch, t0, T,
+                              n_h, c, 0, w, m_prime, E_cap, loc_base, n_loc, out, dt,
+                              v4a::kModeHCA, 1);
+  const size_t need = v4a::attn_workspace(a, g_policy.load());
+  REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
+  REQUIRE(need == 0 || (ws && aligned(ws, 256)), V4A_EINVAL, "workspace must be 256-byte aligned");
+  return hip_status(v4a::launch_attention(a, ws, g_policy.load(), (hipStream_t)stream),
+                    "v4a_hca_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,246 @@
+// Lightning indexer score and per-query top-k ("CSA And HCA: Definition,
+// State, And Cost Model", section 3.1):
+//   I[t][s] = sum_h wI[t][h] * max(0, qI[t][h] . KI[s])   for s < floor((t+1)/m)
+// followed by TopK over those s, ties to the lower index.
+//
+// General path (any dtype and shape):
+//   1. index_scores_kernel: one lane per entry s, all heads of one query; the
+//      query's decoded rows sit in LDS and are read as broadcasts.  Scores go to
+//      a float32 workspace [batch][T][ld].
+//   2. topk_tile_kernel: per (query, tile of entries) an exact radix select in
+//      LDS-resident histograms keeps min(k, tile) candidates (key + index, in
+//      index order).  With one tile per query this writes the final result.
+//   3. topk_merge_kernel: per query, the same select over the tiles' candidates.
+// The MFMA paths for the production shapes live in indexer_mfma.hip and reuse
+// the two top-k kernels.
+#include "device_common.h"
+#include "internal.h"
+#include "topk.h"
+
+namespace v4a {
+
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kHeadChunk = 32;
+
+__device__ __forceinline__ float load_elem(const void* base, int64_t i, int dt) {
+  if (dt == kF32) return reinterpret_cast<const float*>(base)[i];
+  if (dt == kBF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
+  if (dt == kFP8) return e4m3_to_f32(reinterpret_cast<const uint8_t*>(base)[i]);
+  const uint8_t byte = reinterpret_cast<const uint8_t*>(base)[i >> 1];
+  return e2m1_to_f32((i & 1) ? (byte >> 4) : (byte & 15u));
+}
+
+// One block per (entry tile, query, sequence).
+__global__ __launch_bounds__(kScoreThreads) void index_scores_kernel(IndexerArgs a, float* scores,
+                                                                      int64_t ld) {
+  extern __shared__ float sq[];  // [n_hI][cI] decoded query, then [n_hI] weights
+  const int j = blockIdx.x, b = blockIdx.z;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t s = (int64_t)blockIdx.y * kScoreThreads + threadIdx.x;
+  const int nh = a.n_hI, cI = a.cI;
+  float* sw = sq + (size_t)nh * cI;
+  const int64_t qrow0 = ((int64_t)b * a.T + j) * nh;
+  if ((int64_t)blockIdx.y * kScoreThreads >= E) {
+    // whole tile beyond the visible entries: nothing to score
+    return;
+  }
+  for (int e = threadIdx.x; e < nh * cI; e += kScoreThreads) {
+    const int h = e / cI, d = e % cI;
+    const int64_t qi = (qrow0 + h) * cI + d;
+    float v = load_elem(a.qI, qi, a.dt);
+    if (a.dt == kFP8) v *= reinterpret_cast<const float*>(a.qI_scale)[qrow0 + h];
+    if (a.dt == kMXFP4)
+      v *= e8m0_to_f32(reinterpret_cast<const uint8_t*>(a.qI_scale)[(qrow0 + h) * (cI / 32) + d / 32]);
+    sq[e] = v;
+  }
+  for (int h = threadIdx.x; h < nh; h += kScoreThreads) sw[h] = a.wI[qrow0 + h];
+  __syncthreads();
+  if (s >= E) return;
+  const int64_t krow = (int64_t)b * a.E_cap + s;
+  float ks = 1.0f;
+  if (a.dt == kFP8) ks = reinterpret_cast<const float*>(a.KI_scale)[krow];
+  float score = 0.0f;
+  for (int h0 = 0; h0 < nh; h0 += kHeadChunk) {
+    float acc[kHeadChunk];
+#pragma unroll
+    for (int h = 0; h < kHeadChunk; ++h) acc[h] = 0.0f;
+    for (int d = 0; d < cI; ++d) {
+      float kv = load_elem(a.KI, krow * cI + d, a.dt);
+      if (a.dt == kMXFP4)
+        kv *= e8m0_to_f32(reinterpret_cast<const uint8_t*>(a.KI_scale)[krow * (cI / 32) + d / 32]);
+#pragma unroll
+      for (int h = 0; h < kHeadChunk; ++h)
+        if (h0 + h < nh) acc[h] = fmaf(sq[(h0 + h) * cI + d], kv, acc[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < kHeadChunk; ++h)
+      if (h0 + h < nh) score = fmaf(sw[h0 + h], fmaxf(acc[h] * ks, 0.0f), score);
+  }
+  scores[((int64_t)b * a.T + j) * ld + s] = score;
+}
+
+struct TopkOut {
+  int32_t* idx;
+  int32_t* cnt;
+  float* score;
+};
+
+// Stage A: per (tile, query, sequence).  n_tiles == 1: final output.
+__global__ __launch_bounds__(256) void topk_tile_kernel(IndexerArgs a, const float* scores,
+                                                        int64_t ld, int tile, int n_tiles, int kc,
+                                                        uint32_t* cand_key, int32_t* cand_idx) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[16];
+  const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t s0 = (int64_t)tl * tile;
+  const int N = (int)max((int64_t)0, min((int64_t)tile, E - s0));
+  const int64_t q = (int64_t)b * a.T + j;
+  const float* srow = scores + q * ld + s0;
+  auto get = [&](int i) { return score_key(srow[i]); };
+  if (n_tiles == 1) {
+    const int k = a.k;
+    int32_t* oidx = a.topk_idx + q * k;
+    float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
+    auto emit = [&](int pos, int i, uint32_t key) {
+      oidx[pos] = (int32_t)(s0 + i);
+      if (osc) osc[pos] = key_score(key);
+    };
+    const int n = min(N, k);
+    if (N <= k) {
+      block_emit_all(get, N, emit);
+    } else {
+      const Selection sel = block_radix_select(get, N, k, hist, sh);
+      block_select_emit(get, N, k, sel, sh, emit);
+    }
+    for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
+      oidx[p] = -1;
+      if (osc) osc[p] = 0.0f;
+    }
+    if (threadIdx.x == 0) a.topk_cnt[q] = n;
+    return;
+  }
+  uint32_t* ck = cand_key + (q * n_tiles + tl) * kc;
+  int32_t* ci = cand_idx + (q * n_tiles + tl) * kc;
+  auto emit = [&](int pos, int i, uint32_t key) {
+    ck[pos] = key;
+    ci[pos] = (int32_t)(s0 + i);
+  };
+  const int n = min(N, kc);
+  if (N <= kc) {
+    block_emit_all(get, N, emit);
+  } else {
+    const Selection sel = block_radix_select(get, N, kc, hist, sh);
+    block_select_emit(get, N, kc, sel, sh, emit);
+  }
+  for (int p = n + threadIdx.x; p < kc; p += blockDim.x) {
+    ck[p] = 0u;  // below every real score's key
+    ci[p] = -1;
+  }
+}
+
+// Stage B: per (query, sequence): select among n_tiles * kc candidates.
+__global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_tiles, int kc,
+                                                          const uint32_t* cand_key,
+                                                          const int32_t* cand_idx) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[40];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t q = (int64_t)b * a.T + j;
+  const int k = a.k;
+  const int n = (int)min((int64_t)k, E);
+  const int N = n_tiles * kc;
+  const uint32_t* ck = cand_key + q * N;
+  const int32_t* ci = cand_idx + q * N;
+  int32_t* oidx = a.topk_idx + q * k;
+  float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
+  auto get = [&](int i) { return ck[i]; };
+  auto emit = [&](int pos, int i, uint32_t key) {
+    oidx[pos] = ci[i];
+    if (osc) osc[pos] = key_score(key);
+  };
+  if (n > 0) {
+    // exactly n real candidates are wanted; padding keys (0) rank below all of them
+    const Selection sel = block_radix_select(get, N, n, hist, sh);
+    block_select_emit(get, N, n, sel, sh, emit);
+  }
+  for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
+    oidx[p] = -1;
+    if (osc) osc[p] = 0.0f;
+  }
+  if (threadIdx.x == 0) a.topk_cnt[q] = n;
+}
+
+}  // namespace
+
+// MFMA paths (indexer_mfma.hip)
+bool indexer_mfma_supported(int T, int n_hI, int cI, int dt);
+hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
+                                      hipStream_t s);
+
+IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k, int dt,
+                         int policy) {
+  IndexerPlan p{};
+  const int64_t Emax = (t0 + T) / m;
+  p.ld = (Emax + 63) / 64 * 64;
+  if (p.ld < 64) p.ld = 64;
+  p.tile = 4096;
+  if (k > p.tile) p.tile = (k + 4095) / 4096 * 4096;
+  p.n_tiles = (int)((Emax + p.tile - 1) / p.tile);
+  if (p.n_tiles < 1) p.n_tiles = 1;
+  p.kc = k < p.tile ? k : p.tile;
+  p.fused = false;
+  (void)policy;
+  (void)n_hI;
+  (void)cI;
+  (void)dt;
+  p.score_bytes = ((size_t)batch * T * p.ld * sizeof(float) + 255) / 256 * 256;
+  p.cand_bytes = p.n_tiles > 1 ? (size_t)batch * T * p.n_tiles * p.kc * 8 : 0;
+  p.total = p.score_bytes + p.cand_bytes;
+  return p;
+}
+
+hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void* ws,
+                               hipStream_t s) {
+  float* scores = reinterpret_cast<float*>(ws);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.score_bytes);
+  int32_t* ci = reinterpret_cast<int32_t*>(ck + (size_t)a.batch * a.T * p.n_tiles * p.kc);
+  const int64_t Emax = (a.t0 + a.T) / a.m;
+  hipError_t err;
+  if (Emax > 0) {
+    if (indexer_mfma_supported(a.T, a.n_hI, a.cI, a.dt)) {
+      err = launch_indexer_scores_mfma(a, scores, p.ld, s);
+    } else {
+      dim3 grid((unsigned)a.T, (unsigned)((Emax + kScoreThreads - 1) / kScoreThreads),
+                (unsigned)a.batch);
+      const size_t shmem = ((size_t)a.n_hI * a.cI + a.n_hI) * sizeof(float);
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipFuncSetAttribute((const void*)index_scores_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((16384 + 1024) * sizeof(float)));
+        attr_set = true;
+      }
+      hipLaunchKernelGGL(index_scores_kernel, grid, dim3(kScoreThreads), shmem, s, a, scores, p.ld);
+      err = hipGetLastError();
+    }
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(topk_tile_kernel, dim3((unsigned)a.T, (unsigned)p.n_tiles, (unsigned)a.batch),
+                     dim3(256), 0, s, a, scores, p.ld, p.tile, p.n_tiles, p.kc, ck, ci);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.n_tiles > 1) {
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.T, (unsigned)a.batch), dim3(1024), 0, s,
+                       a, p.n_tiles, p.kc, ck, ci);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace v4a

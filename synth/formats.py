@@ -74,22 +74,17 @@ def fp8_e4m3_rows(x) -> tuple[np.ndarray, np.ndarray]:
     return code.astype(np.uint8), scale
 
 
-_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])  # midpoints of the E2M1 grid
 
 
 def _e2m1_encode_abs(a: np.ndarray) -> np.ndarray:
-    """|value| -> 3-bit E2M1 magnitude code, round to nearest, ties to even code, saturate at 6."""
+    """|value| -> 3-bit E2M1 magnitude code: nearest grid value, ties to the even code,
+    saturating at 6."""
     a = np.minimum(a, 6.0)
-    # distance to each grid point; ties resolved towards the even code (even mantissa bit)
-    d = np.abs(a[..., None] - _E2M1_GRID)
-    best = d.min(axis=-1, keepdims=True)
-    cand = d == best
-    codes = np.arange(8)
-    # among tied candidates prefer even code (mantissa bit 0)
-    pref = np.where(cand, (codes % 2) * 2 + (codes // 8), 99)  # even codes score 0
-    # if two even candidates tie (cannot happen on this grid) the lower one wins
-    choice = np.argmin(pref * 16 + codes, axis=-1)
-    return choice.astype(np.uint8)
+    code = np.searchsorted(_E2M1_MID, a, side="left")  # a on a midpoint -> the lower code
+    on_mid = (code < 7) & (a == _E2M1_MID[np.minimum(code, 6)])
+    code = np.where(on_mid & (code % 2 == 1), code + 1, code)
+    return code.astype(np.uint8)
 
 
 def mxfp4_rows(x) -> tuple[np.ndarray, np.ndarray]:

@@ -1,0 +1,144 @@
+"""The C ABI library loads, exports every symbol include/v4a.h declares, and
+rejects invalid arguments on the host before any device work (no GPU needed)."""
+import ctypes as ct
+import os
+import re
+import subprocess
+
+import pytest
+
+from compressed_sparse_attention_v4a_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "v4a.h")
+
+EINVAL, ENOTSUP, ENOSPC = -22, -95, -28
+P = ct.c_void_p(4096)  # a non-null, aligned fake device address: validation never dereferences it
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"V4A_API\s+[\w\s\*]*?\b(v4a_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libv4a.so is not built")
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared()
+    assert len(names) == 13, names
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (v4a_\w+)", out))
+    assert set(names) == exported
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_policy(lib):
+    assert "gfx950" in B.v4a_version()
+    prev = B.v4a_set_kernel_policy(1)
+    assert B.v4a_set_kernel_policy(prev) == 1
+    assert B.v4a_set_kernel_policy(7) == prev  # invalid policy: unchanged
+
+
+def test_visibility_validation(lib):
+    assert lib.v4a_visibility(-1, 4, 4, 2, 3, None, None, None, None, None) == EINVAL
+    assert lib.v4a_visibility(0, 4, 0, 2, 3, None, None, None, None, None) == EINVAL
+    assert lib.v4a_visibility(0, 4, 4, 2, 0, None, None, None, None, None) == EINVAL
+    assert "m and w" in B.v4a_last_error()
+
+
+def _compress(lib, **kw):
+    a = dict(C=P, Z=P, in_dt=1, B=P, batch=1, n_buf=16, tok_base=0, t0=0, T=16, c=64, m=4,
+             overlap=1, gamma=None, eps=1e-6, rope_dims=0, rope_base=10000.0, out=P,
+             out_scale=None, out_dt=1, E_cap=4, stream=None)
+    a.update(kw)
+    return lib.v4a_compress(*a.values())
+
+
+def test_compress_validation(lib):
+    assert _compress(lib, C=None) == EINVAL
+    assert _compress(lib, overlap=2) == EINVAL
+    assert _compress(lib, m=0) == EINVAL
+    assert _compress(lib, c=63) == EINVAL
+    assert _compress(lib, rope_dims=3) == EINVAL
+    assert _compress(lib, rope_dims=66) == EINVAL
+    assert _compress(lib, E_cap=3) == EINVAL                    # entries 0..3 need E_cap 4
+    assert _compress(lib, n_buf=15) == EINVAL                   # last block not in the buffer
+    assert _compress(lib, tok_base=5, n_buf=11, t0=8, T=8) == EINVAL  # entry 2 pools block 1 (pos 4..7)
+    assert _compress(lib, in_dt=2) == ENOTSUP                   # fp8 input
+    assert _compress(lib, out_dt=9) == ENOTSUP
+    assert _compress(lib, out_dt=2) == EINVAL                   # fp8 output needs out_scale
+    assert _compress(lib, c=48, out_dt=3, out_scale=P) == EINVAL  # MXFP4 needs c % 32
+    assert _compress(lib, C=ct.c_void_p(4098)) == EINVAL        # misaligned
+    assert _compress(lib, c=4096) == ENOTSUP
+    assert "E_cap" in B.v4a_last_error() or B.v4a_last_error() != ""
+
+
+def _indexer(lib, **kw):
+    a = dict(qI=P, qI_scale=None, KI=P, KI_scale=None, dt=1, wI=P, batch=1, T=8, t0=0, n_hI=4,
+             cI=32, m=4, k=2, E_cap=2, idx=P, cnt=P, score=None, ws=P, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.v4a_indexer_topk(*a.values())
+
+
+def test_indexer_validation(lib):
+    assert _indexer(lib, qI=None) == EINVAL
+    assert _indexer(lib, T=0) == EINVAL
+    assert _indexer(lib, k=0) == EINVAL
+    assert _indexer(lib, E_cap=1) == EINVAL
+    assert _indexer(lib, dt=2) == EINVAL          # FP8 needs scales
+    assert _indexer(lib, dt=3, cI=48, qI_scale=P, KI_scale=P) == EINVAL
+    assert _indexer(lib, dt=7) == ENOTSUP
+    assert _indexer(lib, ws_bytes=16) == ENOSPC
+    assert _indexer(lib, ws=ct.c_void_p(4096 + 64)) == EINVAL  # workspace alignment
+    need = lib.v4a_indexer_topk_workspace(1, 8192, 0, 64, 128, 4, 512, 1)
+    assert need >= 8192 * 2048 * 4
+
+
+def test_attention_validation(lib):
+    def pre(**kw):
+        a = dict(q=P, kv_comp=P, kv_local=P, loc_base=0, n_loc=16, idx=P, cnt=P, sink=None,
+                 q_gamma=None, kv_gamma=None, eps=1e-6, rope_dims=0, rope_base=1e4, scale=0.0,
+                 batch=1, t0=0, T=16, n_h=4, c=64, k=4, w=4, E_cap=4, out=P, dt=1, ws=P,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.v4a_sparse_mqa_prefill(*a.values())
+    assert pre(q=None) == EINVAL
+    assert pre(c=63) == EINVAL
+    assert pre(c=2048) == ENOTSUP
+    assert pre(dt=2) == ENOTSUP
+    assert pre(rope_dims=66) == EINVAL
+    assert pre(w=0) == EINVAL
+    assert pre(n_loc=15) == EINVAL                      # local rows miss the last query
+    assert pre(t0=20, loc_base=18, n_loc=16) == EINVAL  # window of t0=20 starts at 17
+    assert pre(eps=-1.0) == EINVAL
+
+    def dec(**kw):
+        a = dict(q=P, kv_comp=P, ring=P, kv_new=None, t=100, idx=P, cnt=P, sink=None,
+                 q_gamma=None, kv_gamma=None, eps=1e-6, rope_dims=0, rope_base=1e4, scale=0.0,
+                 batch=2, n_h=4, c=64, k=4, w=4, E_cap=32, num_splits=0, out=P, dt=1, ws=P,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.v4a_sparse_mqa_decode(*a.values())
+    assert dec(ring=None) == EINVAL
+    assert dec(t=-1) == EINVAL
+    assert dec(num_splits=65) == EINVAL
+    assert dec(num_splits=4, ws_bytes=8) == ENOSPC
+
+    def hca(**kw):
+        a = dict(q=P, kv_comp=P, kv_local=P, loc_base=0, n_loc=256, sink=None, q_gamma=None,
+                 kv_gamma=None, eps=1e-6, rope_dims=0, rope_base=1e4, scale=0.0, batch=1, t0=0,
+                 T=256, n_h=4, c=64, m_prime=128, w=16, E_cap=2, out=P, dt=1, ws=P,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.v4a_hca_attn(*a.values())
+    assert hca(E_cap=1) == EINVAL
+    assert hca(m_prime=0) == EINVAL
+    assert hca(kv_local=None) == EINVAL
