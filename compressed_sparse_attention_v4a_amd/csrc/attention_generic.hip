@@ -300,6 +300,8 @@ size_t generic_smem(int c) {
 
 }  // namespace
 
+hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s);
+
 size_t attn_generic_workspace(const AttnArgs& a) {
   if (a.mode != kModeDecode || a.num_splits <= 1) return 0;
   return (size_t)a.batch * a.num_splits * a.n_h * (a.c + 2) * sizeof(float);
@@ -323,12 +325,15 @@ hipError_t launch_attention_generic(const AttnArgs& a, void* ws, hipStream_t s) 
                      reinterpret_cast<float*>(ws));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.mode == kModeDecode && a.num_splits > 1) {
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.n_h, (unsigned)a.batch), dim3(256), 0,
-                       s, a, reinterpret_cast<const float*>(ws));
-    err = hipGetLastError();
-  }
+  if (a.mode == kModeDecode && a.num_splits > 1)
+    err = launch_attention_merge(a, reinterpret_cast<const float*>(ws), s);
   return err;
+}
+
+hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s) {
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.n_h, (unsigned)a.batch), dim3(256), 0, s,
+                     a, part);
+  return hipGetLastError();
 }
 
 }  // namespace v4a

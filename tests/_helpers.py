@@ -30,9 +30,10 @@ def assert_close(got, ref, *, atol=0.0, rtol=0.0, what=""):
                              f"{i}: got {got[i]!r} ref {ref[i]!r} err {err[i]:.3g} bound {bound[i]:.3g}")
 
 
-def assert_bf16_close(got, ref, ulps=1.0, atol=1e-7, what=""):
-    """|got - ref| <= ulps * ulp_bf16(ref) + atol: the fp32 result rounded to bf16 may land on
-    either neighbour of the exact value."""
+def assert_bf16_close(got, ref, ulps=1.0, atol=4e-6, what=""):
+    """|got - ref| <= ulps * ulp_bf16(ref) + atol.  The float32 result rounded to bf16 may land
+    on either neighbour of the exact value (1 ulp); atol covers float32 accumulation over up to
+    128 pooled positions of unit-RMS rows, which dominates where the exact value is tiny."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     err = np.abs(got - ref)
