@@ -85,11 +85,17 @@ def main():
     wI3 = T["wI"].view(1, n, n_hI)
     loc3 = T["local"].view(1, n, c)
 
-    def step(ev=None):
+    def step(ev=None, stages=None):
+        if stages is not None:
+            stages[0].record(stream)
         B.v4a_compress(T["C"], T["Z"], B.BF16, T["B"], 1, n, 0, 0, n, c, m, 1, T["gamma"], 1e-6,
                        64, 10000.0, kv, None, B.BF16, E, stream)
+        if stages is not None:
+            stages[1].record(stream)
         B.v4a_compress(T["CI"], T["ZI"], B.BF16, T["BI"], 1, n, 0, 0, n, cI, m, 1, T["gammaI"],
                        1e-6, 0, 10000.0, KI, None, B.BF16, E, stream)
+        if stages is not None:
+            stages[2].record(stream)
         B.v4a_indexer_topk(qI4, None, KI, None, B.BF16, wI3, 1, n, 0, n_hI, cI, m, k, E, idx, cnt,
                            None, ws_i, ws_i_bytes, stream)
         if ev is not None:
@@ -119,6 +125,15 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
     attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    # one extra, separately timed step for the per-stage split (not part of the timed region)
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev_extra = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    step(ev_extra, st)
+    torch.cuda.synchronize()
+    stages_ms = {"compress_main": round(st[0].elapsed_time(st[1]), 4),
+                 "compress_index": round(st[1].elapsed_time(st[2]), 4),
+                 "indexer_topk": round(st[2].elapsed_time(ev_extra[0]), 4),
+                 "sparse_mqa": round(ev_extra[0].elapsed_time(ev_extra[1]), 4)}
 
     counts = costmodel.csa_prefill_counts(n, m, k, w, n_h, c, n_hI, cI)
     attn_tflops = counts["attn_flops"] / (attn_ms * 1e-3) / 1e12
@@ -150,6 +165,7 @@ def main():
             "algorithmic_flops_per_launch": counts["attn_flops"],
             "avg_launch_ms": round(attn_ms, 4),
         },
+        "stages_ms": stages_ms,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
@@ -191,9 +207,9 @@ def cpu_baseline(d, cfg, target_s):
                               kv_norm=True, rope_dims=64)
         return time.perf_counter() - t0
 
-    tp = run(8, 8)
-    S = int(max(64, min(n, 64 * (target_s - t_fixed) / max(tp, 1e-3))))
-    G = max(8, S // 16)
+    tp = run(16, 16)  # probe: 256 queries
+    S = int(max(256, min(n, 256 * (target_s - t_fixed) / max(tp, 1e-3))))
+    G = max(16, S // 16)
     ts = run(16, G)
     S = 16 * G
     # per-token cost = sampled query cost + the compressor work amortised over all n tokens

@@ -51,6 +51,8 @@ int check_attn_common(const void* q, const void* kv_comp, const void* out, int n
   REQUIRE(c <= 1024, V4A_ENOTSUP, "c > 1024 is not supported (got %d)", c);
   REQUIRE(rope_dims >= 0 && rope_dims % 2 == 0 && rope_dims <= c, V4A_EINVAL,
           "rope_dims must be even and in [0, c] (got %d)", rope_dims);
+  REQUIRE(rope_dims <= v4a::kMaxRopeDims, V4A_ENOTSUP, "rope_dims > %d is not supported",
+          v4a::kMaxRopeDims);
   REQUIRE(w >= 1, V4A_EINVAL, "w must be >= 1 (got %d)", w);
   REQUIRE(dt == V4A_F32 || dt == V4A_BF16, V4A_ENOTSUP, "attention dtype must be F32 or BF16");
   REQUIRE(eps >= 0.0f && std::isfinite(eps), V4A_EINVAL, "eps must be finite and >= 0");
@@ -58,6 +60,14 @@ int check_attn_common(const void* q, const void* kv_comp, const void* out, int n
 }
 
 }  // namespace
+
+namespace v4a {
+void rope_table(RopeTab& tab, int rope_dims, float rope_base) {
+  for (int i = 0; i < kMaxRopeDims / 2; ++i)
+    tab.inv_freq[i] = (2 * i < rope_dims) ? std::pow((double)rope_base, -2.0 * (double)i / (double)rope_dims)
+                                           : 0.0;
+}
+}  // namespace v4a
 
 extern "C" {
 
@@ -93,6 +103,10 @@ int v4a_compress(const void* C, const void* Z, v4a_dtype in_dt, const float* B, 
           "T, t0, n_buf, tok_base must be >= 0");
   REQUIRE(rope_dims >= 0 && rope_dims % 2 == 0 && rope_dims <= c, V4A_EINVAL,
           "rope_dims must be even and in [0, c]");
+  REQUIRE(rope_dims <= v4a::kMaxRopeDims, V4A_ENOTSUP, "rope_dims > %d is not supported",
+          v4a::kMaxRopeDims);
+  REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 0.0f), V4A_EINVAL,
+          "rope_base must be finite and > 0");
   REQUIRE(eps >= 0.0f && std::isfinite(eps), V4A_EINVAL, "eps must be finite and >= 0");
   REQUIRE(in_dt == V4A_F32 || in_dt == V4A_BF16, V4A_ENOTSUP, "in_dt must be F32 or BF16");
   const int vec = in_dt == V4A_F32 ? 4 : 8;
@@ -122,6 +136,7 @@ int v4a_compress(const void* C, const void* Z, v4a_dtype in_dt, const float* B, 
   a.n_buf = n_buf; a.tok_base = tok_base; a.i_begin = i_begin; a.E_cap = E_cap;
   a.n_entries = (int)(i_end - i_begin); a.batch = batch; a.c = c; a.m = m; a.overlap = overlap;
   a.rope_dims = rope_dims; a.in_dt = in_dt; a.out_dt = out_dt; a.eps = eps; a.rope_base = rope_base;
+  v4a::rope_table(a.rope, rope_dims, rope_base);
   return hip_status(v4a::launch_compress(a, (hipStream_t)stream), "v4a_compress");
 }
 
@@ -182,6 +197,7 @@ static v4a::AttnArgs attn_args(const void* q, const void* kv_comp, const void* k
   a.batch = batch; a.T = T; a.n_h = n_h; a.c = c; a.k = k; a.w = w; a.m_prime = m_prime;
   a.rope_dims = rope_dims; a.dt = dt; a.mode = mode; a.num_splits = num_splits;
   a.eps = eps; a.rope_base = rope_base; a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c);
+  v4a::rope_table(a.rope, rope_dims, rope_base);
   return a;
 }
 

@@ -34,8 +34,8 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i, int dt) {
 // Load one row of c elements with one wave into dst (LDS), optionally RMS-
 // normalising with gamma and rotating the last rope_dims channels at pos.
 __device__ void wave_load_row(const void* src, int64_t off, int dt, int c, float* dst,
-                              bool norm, const float* gamma, float eps, int rope_dims, float base,
-                              double pos, float mul) {
+                              bool norm, const float* gamma, float eps, int rope_dims,
+                              const RopeTab& rope, double pos, float mul) {
   const int lane = threadIdx.x & 63;
   float ss = 0.0f;
   // lane owns channel pairs (2*lane + 128*i, +1)
@@ -56,7 +56,7 @@ __device__ void wave_load_row(const void* src, int64_t off, int dt, int c, float
     }
     if (rope_dims > 0 && d >= r0) {
       float cs, sn;
-      rope_cs(pos, (d - r0) >> 1, rope_dims, base, cs, sn);
+      rope_cs(pos, rope.inv_freq[(d - r0) >> 1], cs, sn);
       const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
       x0 = y0;
       x1 = y1;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
     const int h = h0 + hh;
     if (h < a.n_h)
       wave_load_row(a.q, (qrow + h) * c, a.dt, c, qs + hh * c, a.q_gamma != nullptr, a.q_gamma,
-                    a.eps, a.rope_dims, a.rope_base, (double)t, qmul);
+                    a.eps, a.rope_dims, a.rope, (double)t, qmul);
     else
       for (int d = lane; d < c; d += 64) qs[hh * c + d] = 0.0f;
   }
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
         int64_t e = idx ? (int64_t)idx[u] : u;
         e = min(max(e, (int64_t)0), a.E_cap - 1);  // out-of-range indices must not fault
         wave_load_row(a.kv_comp, ((int64_t)b * a.E_cap + e) * c, a.dt, c, kvs + r * cp, false,
-                      nullptr, 0.0f, 0, 0.0f, 0.0, 1.0f);
+                      nullptr, 0.0f, 0, a.rope, 0.0, 1.0f);
       } else {
         const int64_t jj = lo + (u - ncomp);
         const void* src;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
           off = ((int64_t)b * a.n_loc + (jj - a.loc_base)) * c;
         }
         wave_load_row(src, off, a.dt, c, kvs + r * cp, a.kv_gamma != nullptr, a.kv_gamma, a.eps,
-                      a.rope_dims, a.rope_base, (double)jj, 1.0f);
+                      a.rope_dims, a.rope, (double)jj, 1.0f);
       }
     }
     __syncthreads();
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
       const float other = __shfl_xor(x, 1, 64);
       if (a.rope_dims > 0 && d < c && d >= r0) {
         float cs, sn;
-        rope_cs(-(double)t, (d - r0) >> 1, a.rope_dims, a.rope_base, cs, sn);
+        rope_cs(-(double)t, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
         x = (d & 1) ? other * sn + x * cs : x * cs - other * sn;
       }
       if (h < a.n_h && d < c) {
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, const float
     x1 *= inv;
     if (a.rope_dims > 0 && d >= r0) {
       float cs, sn;
-      rope_cs(-(double)t, (d - r0) >> 1, a.rope_dims, a.rope_base, cs, sn);
+      rope_cs(-(double)t, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
       const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
       x0 = y0;
       x1 = y1;

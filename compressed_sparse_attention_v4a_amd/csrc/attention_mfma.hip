@@ -16,10 +16,13 @@
 //     [16v, 16v+16) against all 64 candidates of the chunk with its 16 query heads
 //     resident in registers (RMS-normalised, rotated at t, pre-scaled by
 //     scale*log2 e), so each wave owns complete softmax rows.
-//   * Online softmax with a lazy reference maximum: probabilities are
-//     exp2(s - m_ref) with m_ref moved (and O rescaled) only when a row maximum
-//     grows by more than 2^8; they are rounded to bf16 and written to LDS in the
-//     order the PV operands need.
+//   * Softmax with a fixed reference maximum per row (the first chunk's maximum):
+//     probabilities are exp2(s - m_ref), at most 2^64, so O needs no rescaling;
+//     if a later row maximum exceeds the reference by more than that, the
+//     workgroup restarts its candidate loop with the larger reference (exact in
+//     every case, and never triggered for normalised queries and rows).  The
+//     probabilities are rounded to bf16 and written to LDS in the order the PV
+//     operands need.
 //   * O += P V: wave v owns 128 output channels (16-channel tiles interleaved
 //     across the waves) of all 64 heads
 //     (fp32 accumulators in registers), reading P from LDS and V straight from
@@ -50,7 +53,12 @@ constexpr int kNC = 64;        // candidates per chunk
 constexpr int kRowBytes = kC * 2;
 constexpr int kThreads = 256;
 constexpr int kMaxCand = 2048; // candidate-list capacity of one workgroup (k + w)
-constexpr float kLazy = 8.0f;  // O is rescaled only when a row max grows by more than 2^8
+// Probabilities are exp2(s - m_ref) with m_ref fixed after the first chunk.  They
+// stay below 2^kLazy; O (|v| < 2^6, at most 2^11 candidates) stays below 2^81, far
+// from float32 overflow.  A row max that grows further restarts the candidate loop
+// with the larger reference, so O is never rescaled and never leaves the
+// accumulation registers.
+constexpr float kLazy = 64.0f;
 
 // XOR applied to the 16-byte chunk index of row r (keeps the chunk in its row).
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
@@ -91,6 +99,7 @@ struct MqaArgs {
   int64_t t0, E_cap, lrow_base, n_lrows;
   int T, n_h, k, w, m_prime, rope_dims, mode, splits, split_len;
   float eps, rope_base, qscale;
+  RopeTab rope;
 };
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
@@ -108,7 +117,6 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kNC * kRowBytes];  // double buffer
   __shared__ __attribute__((aligned(16))) char ps[kHG * kNC * 2];  // P, [head][slot] bf16
   __shared__ int rowid_s[MODE == kModeHCA ? 1 : kMaxCand];
-  __shared__ float alpha_s[kHG];
   __shared__ int rescale_s[4];
   __shared__ float fin_m[kHG], fin_l[kHG];
 
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       // pairs in k-steps 14, 15 (channels 448..511) when rope_dims == 64
       const int d = 8 * kchunk(14 + p / 4, g) + 2 * (p % 4);
       if (a.rope_dims > 0 && d >= r0) {
-        rope_cs((double)t, (d - r0) >> 1, a.rope_dims, a.rope_base, cs[p], sn[p]);
+        rope_cs((double)t, a.rope.inv_freq[(d - r0) >> 1], cs[p], sn[p]);
       } else {
         cs[p] = 1.0f;
         sn[p] = 0.0f;
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   const int pbase0 = j * 128 + (((0 + g) ^ (j & 7)) << 4);
   const int pbase1 = j * 128 + (((4 + g) ^ (j & 7)) << 4);
 
-  for (int64_t c = 0; c < nchunks; ++c) {
+  for (int64_t c = 0; c < nchunks;) {
     const int64_t r0 = c * kNC;
     const int cur = (int)(c & 1) * (kNC * kRowBytes);
     const char* buf = kvbuf + cur;
@@ -287,23 +295,34 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     f32x4 S[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) S[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // k-steps are software-pipelined two deep: the reads of step ks + 2 are issued
+    // before the MFMAs of step ks (program order pinned by scheduling barriers)
+    bf16x8 ka[3][4];
+    auto kread = [&](int ks, bf16x8* dst) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        dst[ct] = lds_read_b128(buf, ((ks & 1) ? sbase1 : sbase0) + ct * 16 * kRowBytes + 128 * (ks >> 1));
+    };
+    kread(0, ka[0]);
+    kread(1, ka[1]);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      bf16x8 ka[4];
+      if (ks + 2 < 16) kread(ks + 2, ka[(ks + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
-        ka[ct] = lds_read_b128(buf, ((ks & 1) ? sbase1 : sbase0) + ct * 16 * kRowBytes + 128 * (ks >> 1));
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        S[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ct], qb[ks], S[ct], 0, 0, 0);
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        S[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % 3][ct], qb[ks], S[ct], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // mask candidates past the end of the list
+    // mask candidates past the end of the list (last chunk only)
+    if (c + 1 == nchunks) {
+      const int lim = (int)(nrows - r0);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (r0 + 16 * ct + 4 * g + i >= nrows) S[ct][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i)
+          if (16 * ct + 4 * g + i >= lim) S[ct][i] = -INFINITY;
+    }
     float cmax = -INFINITY;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
@@ -311,13 +330,13 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[ct][i]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    // lazy reference max: P = exp2(S - m_ref) stays <= 2^8 without touching O
-    float al = 1.0f;
-    bool resc = false;
-    if (cmax > m_ref + kLazy) {
-      al = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - cmax);
+    // reference maximum: set by the first chunk, moved only through a restart
+    bool restart = false;
+    if (c == 0 && m_ref == -INFINITY) {
       m_ref = cmax;
-      resc = c > 0;
+    } else if (cmax > m_ref + kLazy) {
+      m_ref = cmax;
+      restart = true;
     }
     {
       float ls = 0.0f;
@@ -331,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           ls += p;
           pv[ct * 4 + i] = p;
         }
-      l_run = l_run * al + ls;
+      l_run += ls;
       const int head = wv * 16 + j;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -341,44 +360,56 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
                           pk_bf16(p0[6], p0[7])};
         *reinterpret_cast<u32x4*>(ps + head * 128 + (((4 * kk + g) ^ (head & 7)) << 4)) = pk;
       }
-      if (g == 0) alpha_s[head] = al;
-      const bool any = __ballot(resc) != 0;
+      const bool any = __ballot(restart) != 0;
       if (lane == 0) rescale_s[wv] = any ? 1 : 0;
     }
     __builtin_amdgcn_s_barrier();
 
-    // O[64 heads][channels of wave wv] += P V  (rescaled first only when a reference max moved)
     if (rescale_s[0] | rescale_s[1] | rescale_s[2] | rescale_s[3]) {
+      // a reference maximum moved: drop the partial sums and start the list again
+      wait_vmcnt<0>();
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float al = alpha_s[16 * mt + 4 * g + i];
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) O[mt][nt][i] *= al;
-        }
+        for (int nt = 0; nt < 8; ++nt) O[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      l_run = 0.0f;
+      c = 0;
+      __builtin_amdgcn_s_barrier();  // every wave is done with both buffers
+      fill(kvbuf, 0);
+      continue;
     }
+
+    // O[64 heads][channels of wave wv] += P V
     __builtin_amdgcn_sched_barrier(0);
+    // PV: P fragments per 32-candidate step, V fragments read two tiles ahead
+    bf16x8 pa[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 pa[4];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        pa[mt] = *reinterpret_cast<const bf16x8*>(ps + (kk ? pbase1 : pbase0) + mt * 16 * 128);
+        pa[kk][mt] = *reinterpret_cast<const bf16x8*>(ps + (kk ? pbase1 : pbase0) + mt * 16 * 128);
+    auto vread = [&](int it) -> bf16x8 {
+      // it = kk * 8 + nt: rows 32 kk + trow and +16, output channels ochan(wv, nt) .. +15
+      const int toff = tbase + (it >> 3) * 32 * kRowBytes + (it & 7) * 128;
+      const u32x2 v1 = lds_read_tr(buf, toff);
+      const u32x2 v2 = lds_read_tr(buf, toff + 16 * kRowBytes);
+      const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
+      return __builtin_bit_cast(bf16x8, cat);
+    };
+    bf16x8 vb[3];
+    vb[0] = vread(0);
+    vb[1] = vread(1);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        // rows 32 kk + trow and +16, output channels ochan(wv, nt) .. +15
-        const int toff = tbase + kk * 32 * kRowBytes + nt * 128;
-        const u32x2 v1 = lds_read_tr(buf, toff);
-        const u32x2 v2 = lds_read_tr(buf, toff + 16 * kRowBytes);
-        const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, cat);
+    for (int it = 0; it < 16; ++it) {
+      if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kk = it >> 3, nt = it & 7;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          O[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, O[mt][nt], 0, 0, 0);
-        if ((nt & 1) == 1) __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int mt = 0; mt < 4; ++mt)
+        O[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk][mt], vb[it % 3], O[mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    ++c;
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -421,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   for (int nt = 0; nt < 8; ++nt) {
     const int d = ochan(wv, nt) + j;
     if (a.rope_dims > 0 && d >= r0) {
-      rope_cs(-(double)t, (d - r0) >> 1, a.rope_dims, a.rope_base, cs8[nt], sn8[nt]);
+      rope_cs(-(double)t, a.rope.inv_freq[(d - r0) >> 1], cs8[nt], sn8[nt]);
     } else {
       cs8[nt] = 1.0f;
       sn8[nt] = 0.0f;
@@ -465,6 +496,7 @@ struct LocalPrepArgs {
   int64_t lrow_base, loc_base, n_loc, n_lrows, t;
   int w, rope_dims, decode;
   float eps, rope_base;
+  RopeTab rope;
 };
 
 __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
@@ -507,7 +539,7 @@ __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
     float y0 = x[e], y1 = x[e + 1];
     if (a.rope_dims > 0 && d >= r0) {
       float cs, sn;
-      rope_cs((double)pos, (d - r0) >> 1, a.rope_dims, a.rope_base, cs, sn);
+      rope_cs((double)pos, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
       const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
       y0 = z0;
       y1 = z1;
@@ -561,6 +593,7 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   lp.rope_dims = a.rope_dims;
   lp.eps = a.eps;
   lp.rope_base = a.rope_base;
+  lp.rope = a.rope;
   lp.w = a.w;
   if (a.mode == kModeDecode) {
     lp.src = reinterpret_cast<const uint16_t*>(a.kv_local);
@@ -606,6 +639,7 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   m.eps = a.eps;
   m.rope_base = a.rope_base;
   m.qscale = a.scale * kLog2e;
+  m.rope = a.rope;
   const unsigned hgroups = (unsigned)(a.n_h / kHG);
   if (a.mode == kModeDecode) {
     m.splits = a.num_splits > 1 ? a.num_splits : 1;

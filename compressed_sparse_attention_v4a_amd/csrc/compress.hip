@@ -125,6 +125,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   }
   __syncthreads();
   float x[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) x[v] = 0.0f;
   const bool owner = tid < G;  // lanes with p == 0 finish the entry
   float ss = 0.0f;
   if (owner) {
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
       const int ch = g * VEC + v;
       if (ch >= r0) {
         float cs, sn;
-        rope_cs(pos, (ch - r0) >> 1, a.rope_dims, a.rope_base, cs, sn);
+        rope_cs(pos, a.rope.inv_freq[(ch - r0) >> 1], cs, sn);
         const float x0 = x[v], x1 = x[v + 1];
         x[v] = x0 * cs - x1 * sn;
         x[v + 1] = x0 * sn + x1 * cs;

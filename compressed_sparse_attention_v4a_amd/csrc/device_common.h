@@ -90,16 +90,16 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 // ------------------------------------------------------------------- RoPE --
 
-// cos/sin of the rotation of pair i (of rope_dims/2) at position pos.  The angle
-// is formed and reduced in float64 so that positions up to 2^31 keep their
-// precision; only the final cos/sin are rounded to float32.
-__device__ __forceinline__ void rope_cs(double pos, int i, int rope_dims, float base, float& cs,
-                                        float& sn) {
-  const double theta = pow((double)base, -2.0 * (double)i / (double)rope_dims);
-  double s, c;
-  sincos(pos * theta, &s, &c);
-  cs = (float)c;
-  sn = (float)s;
+// cos/sin of a RoPE rotation by angle pos * inv_freq.  The angle is formed and
+// reduced modulo 2 pi in float64 (Cody-Waite, two-part 2 pi) so that positions up
+// to 2^31 keep their precision; only the reduced angle goes through float32
+// sincos.  inv_freq = base^(-2i/rope_dims) is computed once on the host.
+__device__ __forceinline__ void rope_cs(double pos, double inv_freq, float& cs, float& sn) {
+  const double ang = pos * inv_freq;
+  const double k = rint(ang * 0.15915494309189535);
+  double r = fma(-k, 6.283185307179586, ang);
+  r = fma(-k, 2.4492935982947064e-16, r);
+  sincosf((float)r, &sn, &cs);
 }
 
 // ------------------------------------------------------------- reductions --

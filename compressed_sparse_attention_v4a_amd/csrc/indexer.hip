@@ -180,6 +180,8 @@ __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_t
 }  // namespace
 
 // MFMA paths (indexer_mfma.hip)
+bool indexer_fused_supported(int64_t Emax, int n_hI, int cI, int dt);
+hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s);
 bool indexer_mfma_supported(int T, int n_hI, int cI, int dt);
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
                                       hipStream_t s);
@@ -195,11 +197,12 @@ IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, 
   p.n_tiles = (int)((Emax + p.tile - 1) / p.tile);
   if (p.n_tiles < 1) p.n_tiles = 1;
   p.kc = k < p.tile ? k : p.tile;
-  p.fused = false;
-  (void)policy;
-  (void)n_hI;
-  (void)cI;
-  (void)dt;
+  p.fused = policy == 0 && indexer_fused_supported(Emax, n_hI, cI, dt);
+  p.mfma_scan = policy == 0 && indexer_mfma_supported(T, n_hI, cI, dt);
+  if (p.fused) {
+    p.score_bytes = p.cand_bytes = p.total = 0;
+    return p;
+  }
   p.score_bytes = ((size_t)batch * T * p.ld * sizeof(float) + 255) / 256 * 256;
   p.cand_bytes = p.n_tiles > 1 ? (size_t)batch * T * p.n_tiles * p.kc * 8 : 0;
   p.total = p.score_bytes + p.cand_bytes;
@@ -212,9 +215,10 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
   uint32_t* ck = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.score_bytes);
   int32_t* ci = reinterpret_cast<int32_t*>(ck + (size_t)a.batch * a.T * p.n_tiles * p.kc);
   const int64_t Emax = (a.t0 + a.T) / a.m;
+  if (p.fused) return launch_indexer_fused(a, Emax, s);
   hipError_t err;
   if (Emax > 0) {
-    if (indexer_mfma_supported(a.T, a.n_hI, a.cI, a.dt)) {
+    if (p.mfma_scan) {
       err = launch_indexer_scores_mfma(a, scores, p.ld, s);
     } else {
       dim3 grid((unsigned)a.T, (unsigned)((Emax + kScoreThreads - 1) / kScoreThreads),

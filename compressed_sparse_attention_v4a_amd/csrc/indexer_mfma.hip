@@ -1,17 +1,393 @@
-// Matrix-core paths of the lightning indexer (filled in below as they land).
+// Matrix-core lightning indexer ("CSA And HCA: Definition, State, And Cost
+// Model", section 3.1):  I[t][s] = sum_h wI[t][h] * max(0, qI[t][h] . KI[s]) over
+// the completed entries s < floor((t+1)/m), then TopK (ties to the lower index).
+//
+// Prefill form, bf16 operands, c^I = 128, heads in multiples of 64 (one pass per
+// 64 heads is fused here for n_hI = 64):
+//   * One workgroup = 4 consecutive queries, one per wave; they share every K^I
+//     tile, which streams through LDS 64 entries at a time (double-buffered
+//     direct global->LDS loads, 16-byte chunks XOR-swizzled by entry).
+//   * S = Q K^T on v_mfma_f32_16x16x32_bf16 with heads as rows: each lane holds 16
+//     (head, entry) products of one entry, so the ReLU * w head reduction is 16
+//     in-register multiply-adds plus two cross-row shuffles per 16 entries.
+//   * Scores never leave LDS: after the scan each wave runs an exact radix select
+//     (4 x 8-bit passes, LDS histograms, ballot-based order-preserving compaction)
+//     for its query and writes the selected entry indices in ascending order.
+// Workgroups are issued longest-first (late queries see the most entries).
+#include "device_common.h"
 #include "internal.h"
 
 namespace v4a {
 
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((address_space(3))) void* lds_void;
+
+constexpr int kCI = 128;             // indexer key width
+constexpr int kRowB = kCI * 2;       // 256 bytes per bf16 key
+constexpr int kNE = 64;              // entries per K tile
+constexpr int kQ = 4;                // queries per workgroup (one per wave)
+constexpr int kHeads = 64;
+
+// 16-byte chunk (of 16 per key) read by lane group g in k-step s (s < 4); the step
+// index sits above the swizzle bits so per-step addresses are immediates.
+__device__ __forceinline__ int kchunk(int s, int g) { return 8 * (s >> 1) + 2 * g + (s & 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Exact top-k of one query over its scores sc[0..E) by one wave; writes the
+// selected indices in ascending order, -1 padding, the count and the scores.
+__device__ void wave_topk(const float* sc, int E, int k, uint32_t* hist, int* sh, int32_t* oidx,
+                          float* osc, int32_t* ocnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int n = E < k ? E : k;
+  if (E <= k) {
+    for (int i = lane; i < E; i += 64) {
+      oidx[i] = i;
+      if (osc) osc[i] = sc[i];
+    }
+  } else {
+    uint32_t prefix = 0, pmask = 0;
+    int rem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < E; i += 64) {
+        const uint32_t key = score_key(sc[i]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                     c3 = hist[4 * lane + 3];
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      uint32_t suf = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += v;
+      }
+      uint32_t above = suf - mine;
+      const uint32_t cs[4] = {c0, c1, c2, c3};
+      int found_d = -1, found_above = 0;
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (above < (uint32_t)rem && above + cs[q] >= (uint32_t)rem) {
+          found_d = 4 * lane + q;
+          found_above = (int)above;
+        }
+        above += cs[q];
+      }
+      const uint64_t who = __ballot(found_d >= 0);
+      const int src = __ffsll((unsigned long long)who) - 1;
+      const int d = __shfl(found_d, src, 64);
+      const int ab = __shfl(found_above, src, 64);
+      prefix |= (uint32_t)d << shift;
+      pmask |= 255u << shift;
+      rem -= ab;
+    }
+    const uint32_t kth = prefix;
+    const int need_eq = rem;
+    int base_sel = 0, base_eq = 0;
+    for (int i0 = 0; i0 < E && base_sel < k; i0 += 64) {
+      const int i = i0 + lane;
+      const bool valid = i < E;
+      const float s = valid ? sc[i] : 0.0f;
+      const uint32_t key = valid ? score_key(s) : 0u;
+      const bool gt = valid && key > kth;
+      const bool eq = valid && key == kth;
+      const uint64_t beq = __ballot(eq);
+      const int eq_pre = __popcll(beq & lt);
+      const bool take = gt || (eq && base_eq + eq_pre < need_eq);
+      const uint64_t bt = __ballot(take);
+      if (take) {
+        const int pos = base_sel + __popcll(bt & lt);
+        oidx[pos] = i;
+        if (osc) osc[pos] = s;
+      }
+      base_eq += __popcll(beq);
+      base_sel += __popcll(bt);
+    }
+  }
+  for (int p = n + lane; p < k; p += 64) {
+    oidx[p] = -1;
+    if (osc) osc[p] = 0.0f;
+  }
+  if (lane == 0) *ocnt = n;
+  (void)sh;
+}
+
+template <int CAP>
+__global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16_kernel(IndexerArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * kNE * kRowB];
+  __shared__ float sc[kQ][CAP];
+  __shared__ uint32_t hist[kQ][256];
+  __shared__ int shw[kQ][4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, jj = lane & 15;
+  const int nblk = (a.T + kQ - 1) / kQ;
+  const int blk = nblk - 1 - (int)blockIdx.x;  // longest workgroups first
+  const int b = blockIdx.y;
+  const int j = blk * kQ + wv;                 // this wave's query row
+  const bool qvalid = j < a.T;
+  const int jlast = min(blk * kQ + kQ, a.T) - 1;
+  const int64_t Ewg = (a.t0 + jlast + 1) / a.m;  // entries any query of the block sees
+  const int64_t Eq = qvalid ? (a.t0 + j + 1) / a.m : 0;
+  const char* kb = reinterpret_cast<const char*>(a.KI) + (int64_t)b * a.E_cap * kRowB;
+
+  // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them
+  auto fill = [&](char* buf, int64_t s0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ins = 4 * wv + r;          // entries 4 ins .. 4 ins + 3
+      const int e = 4 * ins + (lane >> 4);
+      int64_t se = s0 + e;
+      if (se >= Ewg) se = Ewg - 1;         // padding rows: any visible entry (masked later)
+      const int ch = (lane & 15) ^ (e & 7);
+      __builtin_amdgcn_global_load_lds(kb + se * kRowB + ch * 16, (lds_void)(buf + ins * 1024), 16, 0,
+                                       0);
+    }
+  };
+  const int nchunks = (int)((Ewg + kNE - 1) / kNE);
+  if (nchunks > 0) fill(kbuf, 0);
+
+  // resident query rows (A operand, heads as rows) and head weights
+  bf16x8 qa[4][4];  // [mt][ks]
+  float wgt[4][4];  // [mt][i] -> head 16 mt + 4 g + i
+  {
+    const int jq = qvalid ? j : 0;
+    const int64_t qrow = ((int64_t)b * a.T + jq) * a.n_hI;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.qI);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qp + (qrow + 16 * mt + jj) * kCI + 8 * kchunk(ks, g));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wgt[mt][i] = a.wI[qrow + 16 * mt + 4 * g + i];
+  }
+  const int bb0 = jj * kRowB + (((2 * g) ^ (jj & 7)) << 4);
+  const int bb1 = jj * kRowB + (((2 * g + 1) ^ (jj & 7)) << 4);
+  float* scw = sc[wv];
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int cur = (c & 1) * (kNE * kRowB);
+    const char* buf = kbuf + cur;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (c + 1 < nchunks) fill(kbuf + (kNE * kRowB - cur), (int64_t)(c + 1) * kNE);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int et = 0; et < 4; ++et) {
+      f32x4 S[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) S[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(buf + ((ks & 1) ? bb1 : bb0) + et * 16 * kRowB +
+                                                          128 * (ks >> 1));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv, S[mt], 0, 0, 0);
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(wgt[mt][i], fmaxf(S[mt][i], 0.0f), acc);
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      const int64_t s = (int64_t)c * kNE + 16 * et + jj;
+      if (g == 0 && s < Eq) scw[s] = acc;
+    }
+  }
+
+  // per-query top-k by its own wave (no workgroup barrier needed from here on)
+  if (qvalid) {
+    const int64_t q = (int64_t)b * a.T + j;
+    wave_topk(scw, (int)Eq, a.k, hist[wv], shw[wv], a.topk_idx + q * a.k,
+              a.topk_score ? a.topk_score + q * a.k : nullptr, a.topk_cnt + q);
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Scan form for long key lists (decode, or prefill beyond the fused capacity):
+// one workgroup scores one query against 1024 consecutive entries, streaming the
+// keys from HBM straight into MFMA operand registers (each key byte is used by
+// exactly one wave, so no LDS), and writes float32 scores for the two-stage
+// top-k kernels.
+//   FP8 E4M3 : v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales; the
+//              per-row scales are positive, so I = sK_s * sum_h (w_h sQ_h) ReLU(raw).
+//   MXFP4    : the same instruction with E2M1 operands and the E8M0 block scales
+//              of both operands applied by the hardware, one scale per lane.
+//   BF16     : v_mfma_f32_16x16x32_bf16, four k-steps.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+constexpr int kScanEntries = 1024;  // per workgroup (4 waves x 16 tiles x 16 entries)
+
+template <int DT>
+__global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerArgs a, float* scores, int64_t ld) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, jj = lane & 15;
+  const int j = blockIdx.y, b = blockIdx.z;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t e0 = (int64_t)blockIdx.x * kScanEntries + wv * (kScanEntries / 4);
+  if (e0 >= E) return;
+  const int64_t q = (int64_t)b * a.T + j;
+  const int64_t qrow = q * kHeads;
+  float wq[4][4];  // w_h (times the FP8 row scale of q): head 16 mt + 4 g + i
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * mt + 4 * g + i;
+      float w = a.wI[qrow + h];
+      if (DT == kFP8) w *= reinterpret_cast<const float*>(a.qI_scale)[qrow + h];
+      wq[mt][i] = w;
+    }
+  // query operand: lane (g, jj) holds head 16 mt + jj, k-block g (32 elements)
+  i32x8 qa[4];
+  int qs[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t h = qrow + 16 * mt + jj;
+    if (DT == kFP8) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.qI) + h * kCI + 32 * g);
+      const uint4 x0 = p[0], x1 = p[1];
+      qa[mt] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      qs[mt] = 127;
+    } else if (DT == kMXFP4) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.qI) + h * (kCI / 2) + 16 * g);
+      qa[mt] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+      qs[mt] = reinterpret_cast<const uint8_t*>(a.qI_scale)[h * (kCI / 32) + g];
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.qI) + h * kCI + 32 * g);
+      const uint4 x0 = p[0], x1 = p[1];  // channels 32 g .. 32 g + 15 (two k-steps' worth)
+      const uint4* p2 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.qI) + h * kCI + 32 * g + 16);
+      const uint4 x2 = p2[0], x3 = p2[1];
+      // bf16: k-step s uses channels 32 g + 8 s .. +7 of this lane's 32-channel block
+      qa[mt] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      qs[mt] = (int)0;
+      (void)x2; (void)x3;
+    }
+  }
+  i32x8 qa_hi[4];  // bf16 only: channels 32 g + 16 .. 32 g + 31
+  if (DT == kBF16) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t h = qrow + 16 * mt + jj;
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.qI) + h * kCI + 32 * g + 16);
+      const uint4 x0 = p[0], x1 = p[1];
+      qa_hi[mt] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    }
+  }
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.KI);
+  float* srow = scores + q * ld;
+  const int64_t kbase = (int64_t)b * a.E_cap;
+#pragma unroll 2
+  for (int tile = 0; tile < kScanEntries / 4 / 16; ++tile) {
+    const int64_t s0 = e0 + 16 * tile;
+    if (s0 >= E) break;
+    int64_t s = s0 + jj;
+    const bool sval = s < E;
+    if (!sval) s = E - 1;
+    const int64_t row = kbase + s;
+    f32x4 S[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) S[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float ks = 1.0f;
+    if (DT == kFP8) {
+      const uint4* p = reinterpret_cast<const uint4*>(kb + row * kCI + 32 * g);
+      const uint4 x0 = p[0], x1 = p[1];
+      const i32x8 kv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      ks = reinterpret_cast<const float*>(a.KI_scale)[row];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        S[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, S[mt], 0, 0, 0, 127, 0, 127);
+    } else if (DT == kMXFP4) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(kb + row * (kCI / 2) + 16 * g);
+      const i32x8 kv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+      const int ksc = reinterpret_cast<const uint8_t*>(a.KI_scale)[row * (kCI / 32) + g];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        S[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, S[mt], 4, 4, 0, qs[mt], 0, ksc);
+    } else {
+      const uint16_t* kr = reinterpret_cast<const uint16_t*>(kb) + row * kCI + 32 * g;
+      const uint4 x0 = reinterpret_cast<const uint4*>(kr)[0], x1 = reinterpret_cast<const uint4*>(kr)[1];
+      const uint4 x2 = reinterpret_cast<const uint4*>(kr + 16)[0], x3 = reinterpret_cast<const uint4*>(kr + 16)[1];
+      const uint4 kx[4] = {x0, x1, x2, x3};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint4 kk = kx[st];
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kk);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const i32x8 src = st < 2 ? qa[mt] : qa_hi[mt];
+          const uint4 qq = (st & 1) ? uint4{(unsigned)src[4], (unsigned)src[5], (unsigned)src[6], (unsigned)src[7]}
+                                    : uint4{(unsigned)src[0], (unsigned)src[1], (unsigned)src[2], (unsigned)src[3]};
+          S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qq), kv, S[mt], 0, 0, 0);
+        }
+      }
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(wq[mt][i], fmaxf(S[mt][i], 0.0f), acc);
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (g == 0 && sval) srow[s] = acc * ks;
+  }
+}
+
+}  // namespace
+
+// The fused prefill kernel covers bf16 keys of 128 channels, 64 heads, and up to
+// 4096 visible entries per query.
+bool indexer_fused_supported(int64_t Emax, int n_hI, int cI, int dt) {
+  return dt == kBF16 && cI == kCI && n_hI == kHeads && Emax <= 4096;
+}
+
+hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s) {
+  const unsigned nblk = (unsigned)((a.T + kQ - 1) / kQ);
+  if (Emax <= 2048)
+    hipLaunchKernelGGL(indexer_prefill_bf16_kernel<2048>, dim3(nblk, (unsigned)a.batch), dim3(256), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL(indexer_prefill_bf16_kernel<4096>, dim3(nblk, (unsigned)a.batch), dim3(256), 0,
+                       s, a);
+  return hipGetLastError();
+}
+
 bool indexer_mfma_supported(int T, int n_hI, int cI, int dt) {
-  (void)T; (void)n_hI; (void)cI; (void)dt;
-  return false;
+  (void)T;
+  return n_hI == kHeads && cI == kCI && (dt == kFP8 || dt == kMXFP4 || dt == kBF16);
 }
 
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
                                       hipStream_t s) {
-  (void)a; (void)scores; (void)ld; (void)s;
-  return hipErrorNotSupported;
+  const int64_t Emax = (a.t0 + a.T) / a.m;
+  dim3 grid((unsigned)((Emax + kScanEntries - 1) / kScanEntries), (unsigned)a.T, (unsigned)a.batch);
+  if (a.dt == kFP8)
+    hipLaunchKernelGGL(indexer_scan_kernel<kFP8>, grid, dim3(256), 0, s, a, scores, ld);
+  else if (a.dt == kMXFP4)
+    hipLaunchKernelGGL(indexer_scan_kernel<kMXFP4>, grid, dim3(256), 0, s, a, scores, ld);
+  else
+    hipLaunchKernelGGL(indexer_scan_kernel<kBF16>, grid, dim3(256), 0, s, a, scores, ld);
+  return hipGetLastError();
 }
 
 }  // namespace v4a

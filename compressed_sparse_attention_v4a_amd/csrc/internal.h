@@ -10,6 +10,13 @@ namespace v4a {
 
 enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
 
+// RoPE inverse frequencies base^(-2i/rope_dims), i < rope_dims/2 (rope_dims <= 64).
+constexpr int kMaxRopeDims = 64;
+struct RopeTab {
+  double inv_freq[kMaxRopeDims / 2];
+};
+void rope_table(RopeTab& tab, int rope_dims, float rope_base);
+
 struct CompressArgs {
   const void* C;
   const void* Z;
@@ -21,6 +28,7 @@ struct CompressArgs {
   int n_entries, batch, c, m, overlap, rope_dims;
   int in_dt, out_dt;
   float eps, rope_base;
+  RopeTab rope;
 };
 
 struct IndexerArgs {
@@ -43,6 +51,7 @@ struct IndexerPlan {
   int n_tiles;       // tiles per query
   int kc;            // candidates kept per tile = min(k, tile)
   bool fused;        // MFMA fused score + top-k path (no score buffer)
+  bool mfma_scan;    // MFMA score scan into the score buffer (else the general kernel)
   size_t score_bytes, cand_bytes, total;
 };
 
@@ -61,6 +70,7 @@ struct AttnArgs {
   int64_t loc_base, n_loc, t0, E_cap;
   int batch, T, n_h, c, k, w, m_prime, rope_dims, dt, mode, num_splits;
   float eps, rope_base, scale;
+  RopeTab rope;
 };
 
 enum AttnMode : int { kModeCSA = 0, kModeDecode = 1, kModeHCA = 2 };

@@ -98,8 +98,15 @@ def test_indexer_validation(lib):
     assert _indexer(lib, dt=7) == ENOTSUP
     assert _indexer(lib, ws_bytes=16) == ENOSPC
     assert _indexer(lib, ws=ct.c_void_p(4096 + 64)) == EINVAL  # workspace alignment
-    need = lib.v4a_indexer_topk_workspace(1, 8192, 0, 64, 128, 4, 512, 1)
-    assert need >= 8192 * 2048 * 4
+    # the fused bf16 prefill path keeps scores on chip; the general path needs a score buffer
+    assert lib.v4a_indexer_topk_workspace(1, 8192, 0, 64, 128, 4, 512, 1) == 0
+    prev = B.v4a_set_kernel_policy(1)
+    try:
+        assert lib.v4a_indexer_topk_workspace(1, 8192, 0, 64, 128, 4, 512, 1) >= 8192 * 2048 * 4
+    finally:
+        B.v4a_set_kernel_policy(prev)
+    # decode scan (fp8 keys, 32768 entries): scores plus stage-A candidates
+    assert lib.v4a_indexer_topk_workspace(32, 1, 131071, 64, 128, 4, 512, 2) >= 32 * 32768 * 4
 
 
 def test_attention_validation(lib):

@@ -203,6 +203,31 @@ def test_indexer_bf16_chunks(t0, T, k):
                gpu_scores=sc[0].cpu().numpy(), what="bf16")
 
 
+@pytest.mark.parametrize("t0,T,k", [(0, 300, 64), (37, 1001, 200), (20000, 24, 512)])
+def test_indexer_mfma_paths_bf16(t0, T, k):
+    """n_hI = 64, c^I = 128: the fused LDS-resident path (up to 4096 visible entries)
+    and the scan path beyond it."""
+    rng = np.random.default_rng(t0 + 7 * T)
+    n_hI, cI, m = 64, 128, 4
+    E = (t0 + T) // m
+    qI = synth.formats.bf16_bits(rng.standard_normal((T, n_hI, cI)))
+    KI = synth.formats.bf16_bits(rng.standard_normal((E + 9, cI)))
+    wI = rng.random((T, n_hI)).astype(np.float32)
+    log(f"indexer mfma bf16 t0={t0} T={T} k={k} E={E}")
+    idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(min(T, 12)), np.arange(max(0, T - 12), T),
+                                     np.random.default_rng(3).integers(0, T, 24)]))
+    Kd = f64(KI, "bf16")
+    for r in rows:
+        Er = (t0 + r + 1) // m
+        ref = _oracle_scores(f64(qI[r:r + 1], "bf16"), Kd[:max(Er, 1)],
+                             wI[r:r + 1].astype(np.float64), t0 + int(r), m, Er)
+        check_topk(idx[0, r:r + 1].cpu().numpy(), cnt[0, r:r + 1].cpu().numpy(), ref,
+                   t0=t0 + int(r), m=m, k=k, gpu_scores=sc[0, r:r + 1].cpu().numpy(),
+                   what=f"row {r}")
+
+
 def test_indexer_flash_prefill_sampled(csa8k):
     cfg, d = csa8k
     log("indexer flash n=8192 k=512 (all queries on GPU, sampled rows checked)")
