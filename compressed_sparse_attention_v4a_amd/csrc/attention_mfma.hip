@@ -7,33 +7,37 @@
 // row serving as key and value of every head, a sink logit in the denominator,
 // and inverse RoPE at t on the output.
 //
-// Work decomposition (one workgroup = one query position x 64 heads, 4 waves):
+// Work decomposition (one workgroup = one query position x 64 heads, 4 waves,
+// all products on v_mfma_f32_32x32x16_bf16):
 //   * Candidate rows (1 KiB each) stream through LDS 64 at a time, double
 //     buffered, gathered with direct global->LDS 16-byte loads (one row per
-//     instruction).  The 16-byte chunks of a row are XOR-swizzled by a function
-//     of the row so that both read patterns below are bank-conflict free.
-//   * Scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16: wave v computes heads
-//     [16v, 16v+16) against all 64 candidates of the chunk with its 16 query heads
-//     resident in registers (RMS-normalised, rotated at t, pre-scaled by
-//     scale*log2 e), so each wave owns complete softmax rows.
-//   * Softmax with a fixed reference maximum per row (the first chunk's maximum):
-//     probabilities are exp2(s - m_ref), at most 2^64, so O needs no rescaling;
-//     if a later row maximum exceeds the reference by more than that, the
+//     instruction, row address in scalar registers).  The 16-byte chunks of a
+//     row are XOR-swizzled by a function of the row so that both read patterns
+//     below are bank-conflict free.
+//   * Scores S^T = K Q^T: wave w = 2 hh + cc computes head tile hh (32 heads)
+//     against candidate block cc (32 rows) of the chunk, with its 32 query heads
+//     resident in registers as B fragments (RMS-normalised, rotated at t,
+//     pre-scaled by scale * log2 e).  Each K byte is read from LDS twice.
+//   * Softmax with a fixed reference maximum per head (the first chunk's
+//     maximum): probabilities are exp2(s - m_ref) < 2^64, so O is never rescaled;
+//     if a later chunk maximum exceeds the reference by more than that, the
 //     workgroup restarts its candidate loop with the larger reference (exact in
 //     every case, and never triggered for normalised queries and rows).  The
-//     probabilities are rounded to bf16 and written to LDS in the order the PV
-//     operands need.
-//   * O += P V: wave v owns 128 output channels (16-channel tiles interleaved
-//     across the waves) of all 64 heads
-//     (fp32 accumulators in registers), reading P from LDS and V straight from
-//     the row-major tile with the gfx950 transposing LDS read.
+//     score accumulator layout of the 32x32 tile is already the A-operand layout
+//     of P V (candidate k-slots permuted identically on both sides), so each
+//     wave packs its P to bf16 and stores it to LDS as ready-made fragments.
+//   * O += P V: wave w owns output channel tiles 32 (w + 4 nt), nt < 4, of all
+//     64 heads (8 accumulator tiles), reading P fragments from LDS and V straight
+//     from the row-major chunk with the gfx950 transposing LDS read.
 //   * Epilogue: normalisation (+ sink), inverse RoPE, bf16 output staged through
 //     LDS for coalesced 16-byte stores; the decode form writes float32 partial
-//     states (unnormalised O, running max, running sum) for the merge kernel.
+//     states (unnormalised O, reference max, sum) for the merge kernel.
 // Local window rows are normalised and rotated once by a pre-pass into a bf16
 // workspace, so every candidate is a plain row gather.
 #include "device_common.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace v4a {
 
@@ -41,7 +45,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -51,33 +55,40 @@ constexpr int kC = 512;        // channels per row
 constexpr int kHG = 64;        // heads per workgroup
 constexpr int kNC = 64;        // candidates per chunk
 constexpr int kRowBytes = kC * 2;
+constexpr int kChunkBytes = kNC * kRowBytes;
 constexpr int kThreads = 256;
 constexpr int kMaxCand = 2048; // candidate-list capacity of one workgroup (k + w)
 // Probabilities are exp2(s - m_ref) with m_ref fixed after the first chunk.  They
 // stay below 2^kLazy; O (|v| < 2^6, at most 2^11 candidates) stays below 2^81, far
-// from float32 overflow.  A row max that grows further restarts the candidate loop
-// with the larger reference, so O is never rescaled and never leaves the
-// accumulation registers.
+// from float32 overflow.  A chunk maximum that grows further restarts the candidate
+// loop with the larger reference, so O is never rescaled.
 constexpr float kLazy = 64.0f;
 
-// XOR applied to the 16-byte chunk index of row r (keeps the chunk in its row).
+// XOR applied to the low three bits of the 16-byte chunk index of row r.  Eight
+// consecutive rows get eight different values (score reads: eight lanes, eight
+// rows, one chunk column), and rows 4h..4h+3 get values in four different chunk
+// pairs (transposing V reads: four rows x two adjacent chunks per 16 lanes).
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// 16-byte chunk of a row read by lane group g in score k-step s (8 channels).  The
-// step's high bits sit above the swizzle bits, so each lane's addresses for all
-// steps are two base registers plus immediate offsets.
-__device__ __forceinline__ int kchunk(int s, int g) { return 8 * (s >> 1) + 2 * g + (s & 1); }
-
-// First output channel of PV tile nt of wave wv: tiles of 16 channels interleave
-// across waves (chunk pair 2wv + 8nt), keeping the tile index above the swizzle bits.
-__device__ __forceinline__ int ochan(int wv, int nt) { return 16 * wv + 64 * nt; }
-
-// Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
+// Workgroup barrier that neither waits for outstanding memory operations (the
+// next chunk's gather stays in flight) nor lets the compiler move memory
+// accesses across it.  Callers wait for the counters they need first.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Two floats -> packed bf16 pair (round to nearest even, hardware conversion).
@@ -112,21 +123,39 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* base, int off) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Operand and accumulator layouts of v_mfma_f32_32x32x16_bf16 used below (lane l,
+// half hl = l >> 5, l32 = l & 31):
+//   A: row l32, k-slots 8 hl .. 8 hl + 7      B: column l32, k-slots 8 hl .. 8 hl + 7
+//   C: column l32, element i in row 8 (i >> 2) + 4 hl + (i & 3)
+// Candidate <-> k-slot map of one P V step (16 candidates): slot 8 hl + 4 e + r holds
+// candidate 8 e + 4 hl + r.  A score tile's elements 8 p' .. 8 p' + 7 are then exactly
+// the A fragment of P V step p' of its 32-row block.
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kNC * kRowBytes];  // double buffer
-  __shared__ __attribute__((aligned(16))) char ps[kHG * kNC * 2];  // P, [head][slot] bf16
+  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kChunkBytes];  // double buffer
+  __shared__ __attribute__((aligned(16))) char pbuf[2 * 4 * 64 * 16];     // P [head tile][step][lane]
   __shared__ int rowid_s[MODE == kModeHCA ? 1 : kMaxCand];
-  __shared__ int rescale_s[4];
-  __shared__ float fin_m[kHG], fin_l[kHG];
+  __shared__ float mx_s[4][32];   // chunk maximum per (wave, head of its tile)
+  __shared__ float lsum_s[4][32]; // softmax sums per (wave, head of its tile)
+  __shared__ int flag_s[4];
+  __shared__ __attribute__((aligned(16))) float den_s[kHG];
+  __shared__ float mref_s[kHG];
+  __shared__ __attribute__((aligned(16))) float rope_c[kMaxRopeDims / 2], rope_s[kMaxRopeDims / 2];
+  __shared__ __attribute__((aligned(16))) float qg_s[kC];  // query RMSNorm weights
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int g = lane >> 4, j = lane & 15;
+  const int hh = wv >> 1, cc = wv & 1;
+  const int hl = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.z;
   const int hgrp = blockIdx.y;
   const bool decode = MODE == kModeDecode;
-  const int qi = decode ? 0 : blockIdx.x;            // query row within the chunk
+  // prefill: the longest candidate lists (latest positions) are dispatched first
+  const int qi = decode ? 0 : (int)(a.T - 1 - (int)blockIdx.x);
   const int split = decode ? blockIdx.x : 0;
   const int64_t t = decode ? a.t0 : a.t0 + qi;
   const int nq = decode ? 1 : a.T;
@@ -148,338 +177,400 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   }
   const int64_t nrows = ue - ub;
   const int pad_id = -1 - (int)(t - a.lrow_base);  // the query's own window row
-  // row id of candidate u: entry index (>= 0) or -(1 + window workspace row)
+  // RoPE angles at t for the 32 frequencies (the inverse rotation of the output uses
+  // -sin); the frequency is picked with uniform indices so it comes from scalar loads
+  if (a.rope_dims > 0 && tid < kMaxRopeDims / 2) {
+    double f = 0.0;
+#pragma unroll
+    for (int i = 0; i < kMaxRopeDims / 2; ++i) f = tid == i ? a.rope.inv_freq[i] : f;
+    float cs, sn;
+    rope_cs_fast((double)t, f, cs, sn);
+    rope_c[tid] = cs;
+    rope_s[tid] = sn;
+  }
+  // candidate indices: all loads issued before anything waits on them
+  constexpr int kIdPer = MODE == kModeHCA ? 1 : kMaxCand / kThreads;
+  int idv[kIdPer];
   if (MODE != kModeHCA) {
     const int32_t* idx = a.idx + ((int64_t)b * nq + qi) * a.k;
-    for (int64_t r = tid; r < nrows; r += kThreads) {
-      const int64_t u = ub + r;
-      int id;
-      if (u < ncomp) {
-        int64_t e = idx[u];
-        id = (int)min(max(e, (int64_t)0), a.E_cap - 1);  // out-of-range indices must not fault
-      } else {
-        id = -1 - (int)(lo + (u - ncomp) - a.lrow_base);
-      }
-      rowid_s[r] = id;
+#pragma unroll
+    for (int it = 0; it < kIdPer; ++it) {
+      // unconditional loads at a clamped (valid) position, so none waits on a branch
+      const int64_t u = min(ub + it * kThreads + tid, (int64_t)a.k - 1);
+      idv[it] = idx[u];
     }
-    __syncthreads();
   }
+
+  // ---- query rows: all 32 fragment loads of this lane in flight at once -------
+  // lane (hl, l32): head 32 hh + l32, k-step s covers channels 16 s + 8 hl .. +7
+  uint4 qraw[32];
+  {
+    const int64_t qrow = ((int64_t)b * nq + qi) * a.n_h + (int64_t)hgrp * kHG + 32 * hh + l32;
+    const uint16_t* qr = a.q + qrow * kC + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qr + 16 * s);
+  }
+  if (a.q_gamma) {
+    const float2 g = *reinterpret_cast<const float2*>(a.q_gamma + 2 * tid);
+    *reinterpret_cast<float2*>(qg_s + 2 * tid) = g;
+  }
+  // row id of candidate u: entry index (>= 0) or -(1 + window workspace row)
+  if (MODE != kModeHCA) {
+#pragma unroll
+    for (int it = 0; it < kIdPer; ++it) {
+      const int r = it * kThreads + tid;
+      if (r < nrows) {
+        const int64_t u = ub + r;
+        rowid_s[r] = u < ncomp ? (int)min(max((int64_t)idv[it], (int64_t)0), a.E_cap - 1)  // no faults
+                               : -1 - (int)(lo + (u - ncomp) - a.lrow_base);
+      }
+    }
+  }
+  wait_lgkmcnt<0>();
+  block_sync();  // row ids and angles visible; the query loads stay in flight
   const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)b * a.E_cap * kC);
   const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)b * a.n_lrows * kC);
-  const int lane_off = lane << 4;
 
-  // wave wv gathers rows [16 wv, 16 wv + 16) of chunk starting at candidate offset r0
-  auto fill = [&](char* buf, int64_t r0) {
+  // wave wv gathers rows [16 wv, 16 wv + 16) of the chunk starting at candidate r0;
+  // lane i of a row load carries chunk i of the global row into LDS chunk i ^ swz.
+  auto fill = [&](char* dst, int64_t r0) {
+    // lane j < 16 forms the address of row 16 wv + j; each row load then takes it
+    // from that lane into scalar registers (the lane offset stays a 32-bit vector
+    // operand of the scalar-base form of the load)
     int myid = pad_id;
-    const int64_t rr = r0 + 16 * wv + j;
+    const int64_t rr = r0 + 16 * wv + (lane & 15);
     if (MODE == kModeHCA) {
       const int64_t u = ub + rr;
       if (rr < nrows) myid = u < ncomp ? (int)u : -1 - (int)(lo + (u - ncomp) - a.lrow_base);
     } else if (rr < nrows) {
       myid = rowid_s[rr];
     }
+    const uint64_t myaddr = myid >= 0 ? (uint64_t)kvc_b + (uint64_t)myid * kRowBytes
+                                      : (uint64_t)kvl_b + (uint64_t)(-1 - myid) * kRowBytes;
+    const uint32_t alo = (uint32_t)myaddr, ahi = (uint32_t)(myaddr >> 32);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int id = __builtin_amdgcn_readlane(myid, r);
-      const int R = 16 * wv + r;
-      const char* rowp = id >= 0 ? kvc_b + (int64_t)id * kRowBytes : kvl_b + (int64_t)(-1 - id) * kRowBytes;
-      __builtin_amdgcn_global_load_lds(rowp + (lane_off ^ (swz(R) << 4)), (lds_void)(buf + R * kRowBytes),
-                                       16, 0, 0);
+      // readlane returns int: go through uint32_t so the low half is not sign-extended
+      const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ahi, r) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(alo, r);
+      const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;  // rows 16 wv + r share swz(r)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(ra) + voff,
+                                       (lds_void)(dst + (16 * wv + r) * kRowBytes), 16, 0, 0);
     }
   };
 
   const int64_t nchunks = (nrows + kNC - 1) / kNC;
   if (nchunks > 0) fill(kvbuf, 0);
 
-  // ---- resident query heads (B operand of S^T = K Q^T) -----------------
-  // lane (g, j) holds head 16 wv + j, channels 32 ks + 8 g .. +7
-  bf16x8 qb[16];
+  // ---- resident query heads: B fragments of S^T = K Q^T ------------------
+  // RMS-normalised, rotated at t on the last 64 channels (k-steps 28..31), scaled
+  bf16x8 qb[32];
   {
-    const int64_t qrow0 = ((int64_t)b * nq + qi) * a.n_h + (int64_t)hgrp * kHG + wv * 16;
-    float cs[8], sn[8];
-    const int r0 = kC - a.rope_dims;
+    float ss = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      // pairs in k-steps 14, 15 (channels 448..511) when rope_dims == 64
-      const int d = 8 * kchunk(14 + p / 4, g) + 2 * (p % 4);
-      if (a.rope_dims > 0 && d >= r0) {
-        rope_cs((double)t, a.rope.inv_freq[(d - r0) >> 1], cs[p], sn[p]);
-      } else {
-        cs[p] = 1.0f;
-        sn[p] = 0.0f;
+    for (int s = 0; s < 32; ++s) {
+      const uint32_t wds[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(wds[e] << 16), x1 = __uint_as_float(wds[e] & 0xFFFF0000u);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
       }
     }
-    {
-      const uint16_t* qr = a.q + (qrow0 + j) * kC;
-      // pass 1: sum of squares of the head row (4 lanes share a row)
-      float ss = 0.0f;
-#pragma unroll 4
-      for (int ks = 0; ks < 16; ++ks) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qr + 8 * kchunk(ks, g));
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+    float inv = a.qscale;
+    if (a.q_gamma) {
+      ss += __shfl_xor(ss, 32, 64);
+      inv = a.qscale / sqrtf(ss / (float)kC + a.eps);
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = __uint_as_float(wds[e] << 16), x1 = __uint_as_float(wds[e] & 0xFFFF0000u);
-          ss = fmaf(x0, x0, ss);
-          ss = fmaf(x1, x1, ss);
-        }
+    for (int s = 0; s < 32; ++s) {
+      const uint32_t wds[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[2 * e] = __uint_as_float(wds[e] << 16);
+        y[2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
       }
-      float inv = a.qscale;
       if (a.q_gamma) {
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        inv = a.qscale / sqrtf(ss / (float)kC + a.eps);
+        const float4 g0 = *reinterpret_cast<const float4*>(qg_s + 16 * s + 8 * hl);
+        const float4 g1 = *reinterpret_cast<const float4*>(qg_s + 16 * s + 8 * hl + 4);
+        y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
+        y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
       }
-      // pass 2: normalise, rotate, scale, round to bf16
+      if (s >= 28 && a.rope_dims > 0) {
+        // pairs (16 s + 8 hl + 2 j, +1) use frequency 8 (s - 28) + 4 hl + j
+        const float4 c4 = *reinterpret_cast<const float4*>(rope_c + 8 * (s - 28) + 4 * hl);
+        const float4 s4 = *reinterpret_cast<const float4*>(rope_s + 8 * (s - 28) + 4 * hl);
+        const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qr + 8 * kchunk(ks, g));
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[2 * e] = __uint_as_float(wds[e] << 16);
-          y[2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
+        for (int j = 0; j < 4; ++j) {
+          const float y0 = y[2 * j], y1 = y[2 * j + 1];
+          y[2 * j] = y0 * cj[j] - y1 * sj[j];
+          y[2 * j + 1] = y0 * sj[j] + y1 * cj[j];
         }
-        if (a.q_gamma) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] *= a.q_gamma[8 * kchunk(ks, g) + e];
-        }
-        if (ks >= 14) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const int p = (ks - 14) * 4 + e / 2;
-            const float y0 = y[e], y1 = y[e + 1];
-            y[e] = y0 * cs[p] - y1 * sn[p];
-            y[e + 1] = y0 * sn[p] + y1 * cs[p];
-          }
-        }
-        const u32x4 pk = {pk_bf16(y[0] * inv, y[1] * inv), pk_bf16(y[2] * inv, y[3] * inv),
-                          pk_bf16(y[4] * inv, y[5] * inv), pk_bf16(y[6] * inv, y[7] * inv)};
-        qb[ks] = __builtin_bit_cast(bf16x8, pk);
       }
+      const u32x4 pk = {pk_bf16(y[0] * inv, y[1] * inv), pk_bf16(y[2] * inv, y[3] * inv),
+                        pk_bf16(y[4] * inv, y[5] * inv), pk_bf16(y[6] * inv, y[7] * inv)};
+      qb[s] = __builtin_bit_cast(bf16x8, pk);
     }
   }
 
-  // ---- main loop ----------------------------------------------------------
-  f32x4 O[4][8];
+  // ---- per-lane LDS byte offsets (everything step-dependent is an immediate) --
+  // score reads: row 32 cc + l32, chunk 2 s + hl = 8 (s >> 2) + (2 (s & 3) + hl), swizzled
+  const int srow = 32 * cc + l32;
+  int sb[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) O[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_ref = -INFINITY;
-  float l_run = 0.0f;
+  for (int u = 0; u < 4; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4);
+  // transposing V reads, 16-lane group G = lane >> 4, J = lane & 15 = 4 i + q:
+  //   row 16 p + 8 e + 4 (G >> 1) + i, channels 32 T + 16 (G & 1) + 4 q .. +3, T = wv + 4 nt
+  int vbase;
+  {
+    const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
+    const int x = 2 * (G & 1) + (q >> 1);
+    const int y = (i << 1) | (G >> 1);  // swz of the row
+    vbase = (4 * (G >> 1) + i) * kRowBytes + 128 * (wv >> 1) + (((4 * (wv & 1) + x) ^ y) << 4) + 8 * (q & 1);
+  }
+  const int pbase = lane * 16;
 
-  // Per-lane LDS byte offsets; everything step-dependent below is an immediate.
-  //   score reads: row 16 ct + j, chunk kchunk(s, g) ^ swz(j) = 8 (s >> 1) + ((2g + (s & 1)) ^ swz(j))
-  const int sbase0 = j * kRowBytes + (((2 * g) ^ swz(j)) << 4);
-  const int sbase1 = j * kRowBytes + (((2 * g + 1) ^ swz(j)) << 4);
-  //   transposed V reads: row 32 kk + 4 g + (j >> 2) (+16), chunk (2 wv + 8 nt + h) ^ swz(row)
-  const int trow = 4 * g + (j >> 2);
-  const int tbase = trow * kRowBytes + (((2 * wv + ((j & 3) >> 1)) ^ swz(trow)) << 4) + 8 * (j & 1);
-  //   P reads: head 16 mt + j, slot chunk (4 kk + g) ^ (j & 7)
-  const int pbase0 = j * 128 + (((0 + g) ^ (j & 7)) << 4);
-  const int pbase1 = j * 128 + (((4 + g) ^ (j & 7)) << 4);
+  // ---- candidate passes -------------------------------------------------------
+  // kLazyPass: reference maximum from the first chunk; returns false (abandoning
+  //   the pass) when a later chunk maximum exceeds it by more than kLazy.
+  // kMaxPass: scores only, exact maximum over the whole list (fallback).
+  // kFixedPass: P V with the exact maximum (fallback, cannot abandon).
+  constexpr int kLazyPass = 0, kMaxPass = 1, kFixedPass = 2;
+  float m_ref = -INFINITY;  // head 32 hh + l32 (log2 units)
 
-  for (int64_t c = 0; c < nchunks;) {
-    const int64_t r0 = c * kNC;
-    const int cur = (int)(c & 1) * (kNC * kRowBytes);
-    const char* buf = kvbuf + cur;
-    char* nbuf = kvbuf + ((kNC * kRowBytes) - cur);
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // chunk c landed for every wave; chunk c-1 fully consumed
-    if (c + 1 < nchunks) fill(nbuf, r0 + kNC);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // S^T tiles: [ct] -> lane (g, j): head 16 wv + j, candidates 16 ct + 4 g + i
-    f32x4 S[4];
+  auto run = [&](auto pass_tag, f32x16 (&O)[2][4], float& l_part) -> bool {
+    constexpr int PASS = decltype(pass_tag)::value;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) S[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // k-steps are software-pipelined two deep: the reads of step ks + 2 are issued
-    // before the MFMAs of step ks (program order pinned by scheduling barriers)
-    bf16x8 ka[3][4];
-    auto kread = [&](int ks, bf16x8* dst) {
+    for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        dst[ct] = lds_read_b128(buf, ((ks & 1) ? sbase1 : sbase0) + ct * 16 * kRowBytes + 128 * (ks >> 1));
-    };
-    kread(0, ka[0]);
-    kread(1, ka[1]);
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks + 2 < 16) kread(ks + 2, ka[(ks + 2) % 3]);
+        for (int i = 0; i < 16; ++i) O[ht][nt][i] = 0.0f;
+    l_part = 0.0f;
+    float m_run = -INFINITY;
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int64_t r0 = c * kNC;
+      const char* buf = kvbuf + (int)(c & 1) * kChunkBytes;
+      char* nbuf = kvbuf + kChunkBytes - (int)(c & 1) * kChunkBytes;
+      wait_vmcnt<0>();
+      block_sync();  // chunk c landed for every wave; chunk c - 1 fully consumed
+      if (c + 1 < nchunks) fill(nbuf, r0 + kNC);
       __builtin_amdgcn_sched_barrier(0);
+
+      // scores: 32 k-steps, fragment reads two steps ahead
+      f32x16 S;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        S[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % 3][ct], qb[ks], S[ct], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // mask candidates past the end of the list (last chunk only)
-    if (c + 1 == nchunks) {
-      const int lim = (int)(nrows - r0);
+      for (int i = 0; i < 16; ++i) S[i] = 0.0f;
+      bf16x8 ka[3];
+      ka[0] = lds_read_b128(buf, sb[0]);
+      ka[1] = lds_read_b128(buf, sb[1]);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int s = 0; s < 32; ++s) {
+        if (s + 2 < 32) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 3] + 128 * ((s + 2) >> 2));
+        __builtin_amdgcn_sched_barrier(0);
+        S = mfma32(ka[s % 3], qb[s], S);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // candidates past the end of the list (last chunk only)
+      if (__builtin_expect(r0 + kNC > nrows, 0)) {
+        asm volatile("" ::: "memory");  // keep this a branch: only the last chunk is partial
+        const int lim = (int)(nrows - r0) - 32 * cc - 4 * hl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * ct + 4 * g + i >= lim) S[ct][i] = -INFINITY;
-    }
-    float cmax = -INFINITY;
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) >= lim) S[i] = -INFINITY;
+      }
+      float lmax = S[0];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, S[ct][i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    // reference maximum: set by the first chunk, moved only through a restart
-    bool restart = false;
-    if (c == 0 && m_ref == -INFINITY) {
-      m_ref = cmax;
-    } else if (cmax > m_ref + kLazy) {
-      m_ref = cmax;
-      restart = true;
-    }
-    {
-      float ls = 0.0f;
-      float pv[16];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float z = S[ct][i];
-          const float p = (z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - m_ref);
-          ls += p;
-          pv[ct * 4 + i] = p;
+      for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, S[i]);
+      lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+      if (PASS == kMaxPass) {
+        m_run = fmaxf(m_run, lmax);
+        continue;
+      }
+      bool restart = false;
+      if (PASS == kLazyPass) {
+        if (hl == 0) mx_s[wv][l32] = lmax;
+        if (c == 0) {
+          // reference maximum: this chunk's maximum over both candidate blocks
+          wait_lgkmcnt<0>();
+          block_sync();
+          m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
+          if (m_ref == -INFINITY) m_ref = 0.0f;
+        } else {
+          restart = lmax > m_ref + kLazy;
         }
-      l_run += ls;
-      const int head = wv * 16 + j;
+      }
+      float pr[16];
+      float ls = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // slots 32 kk + 8 g .. +7 hold candidates 32 kk + {4g .. 4g+3, 16+4g .. 16+4g+3}
-        const float* p0 = pv + 8 * kk;
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(S[i] - m_ref);
+        ls += pr[i];
+      }
+      l_part += ls;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const float* p0 = pr + 8 * pp;
         const u32x4 pk = {pk_bf16(p0[0], p0[1]), pk_bf16(p0[2], p0[3]), pk_bf16(p0[4], p0[5]),
                           pk_bf16(p0[6], p0[7])};
-        *reinterpret_cast<u32x4*>(ps + head * 128 + (((4 * kk + g) ^ (head & 7)) << 4)) = pk;
+        *reinterpret_cast<u32x4*>(pbuf + ((hh * 4 + 2 * cc + pp) * 64) * 16 + pbase) = pk;
       }
-      const bool any = __ballot(restart) != 0;
-      if (lane == 0) rescale_s[wv] = any ? 1 : 0;
-    }
-    __builtin_amdgcn_s_barrier();
+      if (PASS == kLazyPass) {
+        const bool any = __ballot(restart) != 0;
+        if (lane == 0) flag_s[wv] = any ? 1 : 0;
+      }
+      wait_lgkmcnt<0>();
+      block_sync();  // P (and flags) of every wave visible
+      if (PASS == kLazyPass && (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3])) return false;
 
-    if (rescale_s[0] | rescale_s[1] | rescale_s[2] | rescale_s[3]) {
-      // a reference maximum moved: drop the partial sums and start the list again
-      wait_vmcnt<0>();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) O[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      l_run = 0.0f;
-      c = 0;
-      __builtin_amdgcn_s_barrier();  // every wave is done with both buffers
-      fill(kvbuf, 0);
-      continue;
-    }
-
-    // O[64 heads][channels of wave wv] += P V
-    __builtin_amdgcn_sched_barrier(0);
-    // PV: P fragments per 32-candidate step, V fragments read two tiles ahead
-    bf16x8 pa[2][4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        pa[kk][mt] = *reinterpret_cast<const bf16x8*>(ps + (kk ? pbase1 : pbase0) + mt * 16 * 128);
-    auto vread = [&](int it) -> bf16x8 {
-      // it = kk * 8 + nt: rows 32 kk + trow and +16, output channels ochan(wv, nt) .. +15
-      const int toff = tbase + (it >> 3) * 32 * kRowBytes + (it & 7) * 128;
-      const u32x2 v1 = lds_read_tr(buf, toff);
-      const u32x2 v2 = lds_read_tr(buf, toff + 16 * kRowBytes);
-      const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
-      return __builtin_bit_cast(bf16x8, cat);
-    };
-    bf16x8 vb[3];
-    vb[0] = vread(0);
-    vb[1] = vread(1);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
+      // O[64 heads][channel tiles of wave wv] += P V over 4 steps of 16 candidates
       __builtin_amdgcn_sched_barrier(0);
-      const int kk = it >> 3, nt = it & 7;
+      auto vread = [&](int it) -> bf16x8 {
+        // it = 4 p + nt
+        const int off = vbase + 16384 * (it >> 2) + 256 * (it & 3);
+        const u32x2 v1 = lds_read_tr(buf, off);
+        const u32x2 v2 = lds_read_tr(buf, off + 8 * kRowBytes);
+        const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
+        return __builtin_bit_cast(bf16x8, cat);
+      };
+      bf16x8 pa[2][2];
+      bf16x8 vb[3];
+      pa[0][0] = lds_read_b128(pbuf, pbase);
+      pa[0][1] = lds_read_b128(pbuf, pbase + 4 * 1024);
+      vb[0] = vread(0);
+      vb[1] = vread(1);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        O[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk][mt], vb[it % 3], O[mt][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0; it < 16; ++it) {
+        const int p = it >> 2, nt = it & 3;
+        if (nt == 0 && p + 1 < 4) {
+          pa[(p + 1) & 1][0] = lds_read_b128(pbuf, pbase + (p + 1) * 1024);
+          pa[(p + 1) & 1][1] = lds_read_b128(pbuf, pbase + 4 * 1024 + (p + 1) * 1024);
+        }
+        if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        O[0][nt] = mfma32(pa[p & 1][0], vb[it % 3], O[0][nt]);
+        O[1][nt] = mfma32(pa[p & 1][1], vb[it % 3], O[1][nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    ++c;
-  }
+    if (PASS == kMaxPass) {
+      // exact maximum over both candidate blocks of the head tile
+      if (hl == 0) mx_s[wv][l32] = m_run;
+      wait_lgkmcnt<0>();
+      block_sync();
+      m_ref = fmaxf(m_run, mx_s[wv ^ 1][l32]);
+      if (m_ref == -INFINITY) m_ref = 0.0f;
+    }
+    return true;
+  };
 
   // ---- epilogue -------------------------------------------------------------
-  {
-    float l = l_run;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const int head = wv * 16 + j;
-    if (g == 0) {
-      fin_l[head] = l;
-      fin_m[head] = m_ref;
+  auto finish = [&](f32x16 (&O)[2][4], float l_part) {
+    {
+      const float l = l_part + __shfl_xor(l_part, 32, 64);
+      if (hl == 0) {
+        lsum_s[wv][l32] = l;
+        if (cc == 0) mref_s[32 * hh + l32] = m_ref;
+      }
     }
-  }
-  __syncthreads();
-
-  if (decode && a.splits > 1) {
-    // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
+    __syncthreads();  // sums visible; every wave is done with the chunk buffers
+    const bool partial = decode && a.splits > 1;
+    if (tid < kHG) {
+      const int ht = tid >> 5, h = tid & 31;
+      const float l = lsum_s[2 * ht][h] + lsum_s[2 * ht + 1][h];
+      if (partial) {
+        den_s[tid] = l;
+      } else {
+        float den = l;
+        if (a.sink) den += __builtin_amdgcn_exp2f(a.sink[hgrp * kHG + tid] * kLog2e - mref_s[tid]);
+        den_s[tid] = 1.0f / den;
+      }
+    }
+    if (partial) {
+      // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
+      float* pg = a.part + (((int64_t)b * a.splits + split) * a.n_h + (int64_t)hgrp * kHG) * (kC + 2);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int head = 16 * mt + 4 * g + i;
-        const int64_t hglob = (int64_t)hgrp * kHG + head;
-        float* pr = a.part + (((int64_t)b * a.splits + split) * a.n_h + hglob) * (kC + 2);
+        for (int i = 0; i < 16; ++i) {
+          const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
+          float* prow = pg + (int64_t)head * (kC + 2);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) pr[ochan(wv, nt) + j] = O[mt][nt][i];
-        if (wv == 0 && j == 0) {
-          pr[kC] = fin_m[head];
-          pr[kC + 1] = fin_l[head];
+          for (int nt = 0; nt < 4; ++nt) prow[32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
+        }
+      if (tid < kHG) {
+        float* prow = pg + (int64_t)tid * (kC + 2);
+        prow[kC] = mref_s[tid];
+        prow[kC + 1] = den_s[tid];
+      }
+      return;
+    }
+    // stage O as float32 [64 heads][512] in the chunk buffers
+    float* stage = reinterpret_cast<float*>(kvbuf);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) stage[head * kC + 32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
+      }
+    __syncthreads();
+    // 8 consecutive channels of one head per thread: normalise, inverse RoPE, bf16, 16-byte store
+    uint16_t* dst = a.out + (((int64_t)b * nq + qi) * a.n_h + (int64_t)hgrp * kHG) * kC;
+#pragma unroll 4
+    for (int it = 0; it < (kHG * kC) / (8 * kThreads); ++it) {
+      const int e = (it * kThreads + tid) * 8;
+      const int head = e >> 9, ch = e & (kC - 1);
+      const float4 v0 = *reinterpret_cast<const float4*>(stage + e);
+      const float4 v1 = *reinterpret_cast<const float4*>(stage + e + 4);
+      const float inv = den_s[head];
+      float x[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv,
+                    v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
+      if (a.rope_dims > 0 && ch >= kC - 64) {
+        const int f = (ch - (kC - 64)) >> 1;  // 4 pairs, frequencies f .. f + 3
+        const float4 c4 = *reinterpret_cast<const float4*>(rope_c + f);
+        const float4 s4 = *reinterpret_cast<const float4*>(rope_s + f);
+        const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = x[2 * j], x1 = x[2 * j + 1];
+          x[2 * j] = x0 * cj[j] + x1 * sj[j];
+          x[2 * j + 1] = x1 * cj[j] - x0 * sj[j];
         }
       }
-    return;
-  }
+      const u32x4 pk = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};
+      *reinterpret_cast<u32x4*>(dst + e) = pk;
+    }
+  };
 
-  // normalise, inverse RoPE, stage bf16 rows in LDS (reusing kv0) and store
-  uint16_t* stage = reinterpret_cast<uint16_t*>(kvbuf);  // [64 heads][512]
-  const int r0 = kC - a.rope_dims;
-  float cs8[8], sn8[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int d = ochan(wv, nt) + j;
-    if (a.rope_dims > 0 && d >= r0) {
-      rope_cs(-(double)t, a.rope.inv_freq[(d - r0) >> 1], cs8[nt], sn8[nt]);
-    } else {
-      cs8[nt] = 1.0f;
-      sn8[nt] = 0.0f;
+  {
+    f32x16 O[2][4];
+    float l_part;
+    if (run(std::integral_constant<int, kLazyPass>{}, O, l_part)) {
+      finish(O, l_part);
+      return;
     }
   }
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int head = 16 * mt + 4 * g + i;
-      float den = fin_l[head];
-      if (a.sink) den += __builtin_amdgcn_exp2f(a.sink[hgrp * kHG + head] * kLog2e - fin_m[head]);
-      const float inv = 1.0f / den;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        float x = O[mt][nt][i] * inv;
-        const float other = __shfl_xor(x, 1, 64);
-        x = (j & 1) ? other * sn8[nt] + x * cs8[nt] : x * cs8[nt] - other * sn8[nt];
-        stage[head * kC + ochan(wv, nt) + j] = f32_to_bf16(x);
-      }
-    }
-  __syncthreads();
-  uint16_t* dst = a.out + (((int64_t)b * nq + qi) * a.n_h + (int64_t)hgrp * kHG) * kC;
-#pragma unroll
-  for (int it = 0; it < (kHG * kC) / (8 * kThreads); ++it) {
-    const int e = (it * kThreads + tid) * 8;
-    *reinterpret_cast<uint4*>(dst + e) = *reinterpret_cast<const uint4*>(stage + e);
+  // a chunk maximum ran past the reference: exact maximum first, then P V again
+  wait_vmcnt<0>();  // a prefetch may still be landing
+  block_sync();     // every wave is done with both buffers
+  if (nchunks > 0) fill(kvbuf, 0);
+  {
+    f32x16 O[2][4];
+    float l_part;
+    run(std::integral_constant<int, kMaxPass>{}, O, l_part);
+  }
+  wait_vmcnt<0>();
+  block_sync();
+  if (nchunks > 0) fill(kvbuf, 0);
+  {
+    f32x16 O[2][4];
+    float l_part;
+    run(std::integral_constant<int, kFixedPass>{}, O, l_part);
+    finish(O, l_part);
   }
 }
 

@@ -102,6 +102,16 @@ __device__ __forceinline__ void rope_cs(double pos, double inv_freq, float& cs, 
   sincosf((float)r, &sn, &cs);
 }
 
+// Same rotation with the hardware sine/cosine (argument in revolutions, absolute
+// error near 1e-6 after the float64 reduction): for operands that are rounded to
+// bfloat16 right after the rotation.
+__device__ __forceinline__ void rope_cs_fast(double pos, double inv_freq, float& cs, float& sn) {
+  const double rev = pos * inv_freq * 0.15915494309189535;
+  const float r = (float)(rev - rint(rev));
+  sn = __builtin_amdgcn_sinf(r);
+  cs = __builtin_amdgcn_cosf(r);
+}
+
 // ------------------------------------------------------------- reductions --
 
 __device__ __forceinline__ float wave_sum(float v) {
