@@ -28,6 +28,14 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the MQA attention kernel, from two rocprofv3 PMC passes
+# (FETCH_SIZE, WRITE_SIZE) over this benchmark, each divided by the factor the same
+# counter reads on a plain device copy of known size (--copy-calibration).  Valid only
+# for the kernel source it was measured on: with any other source the figure is null.
+TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
+TRAFFIC = {"sha256": "dc2faa7ade9d5a3dff61359a7b6175856422394b5b676e6ff45be7ee0f35ed0d",
+           "fetch_bytes": 870934351, "write_bytes": 542233024}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -37,7 +45,33 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 4 device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def source_sha256(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes():
+    if TRAFFIC is None or TRAFFIC.get("sha256") != source_sha256(TRAFFIC_SOURCE):
+        return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
+
+def copy_calibration(mib):
+    import torch
+    nbytes = mib << 20
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": 4}))
 
 
 def log(msg):
@@ -51,6 +85,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -161,7 +199,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic_bytes(),
             "algorithmic_flops_per_launch": counts["attn_flops"],
             "avg_launch_ms": round(attn_ms, 4),
         },
