@@ -66,9 +66,11 @@ __device__ void wave_load_row(const void* src, int64_t off, int dt, int c, float
   }
 }
 
-// grid: x = query (prefill/HCA: j < T; decode: sequence b), y = head group,
-//       z = batch (prefill/HCA) or split (decode).
-__global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, float* part) {
+// One query position (prefill/HCA: row j of the chunk; decode: sequence b, candidate
+// split `split`) for heads h0 .. h0 + 7, by the whole workgroup.  Decode splits are
+// ceil(N / num_splits) candidates long unless split_len > 0 gives the length.
+__device__ void attend_item(const AttnArgs& a, float* part, int b, int j, int split, int h0,
+                            int64_t split_len, bool insert_new) {
   extern __shared__ float smem[];
   const int c = a.c, cp = c + 1;
   float* qs = smem;                          // [kHG][c]
@@ -77,11 +79,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
   float* st = zs + kHG * kCH;                // [kHG] alpha
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const bool decode = a.mode == kModeDecode;
-  const int b = decode ? blockIdx.x : blockIdx.z;
-  const int j = decode ? 0 : blockIdx.x;
-  const int split = decode ? blockIdx.z : 0;
   const int nsplit = decode ? a.num_splits : 1;
-  const int h0 = blockIdx.y * kHG;
   const int64_t t = decode ? a.t0 : a.t0 + j;
   const int64_t qrow = decode ? (int64_t)b * a.n_h : ((int64_t)b * a.T + j) * a.n_h;
 
@@ -97,10 +95,10 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
   const int64_t lo = t - a.w + 1 > 0 ? t - a.w + 1 : 0;
   const int64_t nl = t - lo + 1;
   const int64_t N = ncomp + nl;
-  const int64_t per = (N + nsplit - 1) / nsplit;
+  const int64_t per = split_len > 0 ? split_len : (N + nsplit - 1) / nsplit;
   const int64_t ub = min((int64_t)split * per, N), ue = min(ub + per, N);
 
-  if (decode && a.kv_new && blockIdx.y == 0 && split == 0) {
+  if (decode && a.kv_new && insert_new) {
     // step 1 of the decode order: the new token's row goes into slot t % w
     const int64_t dst = ((int64_t)b * a.w + t % a.w) * c;
     for (int d = tid; d < c; d += kThreads) {
@@ -249,6 +247,45 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
   }
 }
 
+// grid: x = query (prefill/HCA: j < T; decode: sequence b), y = head group,
+//       z = batch (prefill/HCA) or split (decode).
+__global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, float* part) {
+  const bool decode = a.mode == kModeDecode;
+  const int b = decode ? blockIdx.x : blockIdx.z;
+  const int j = decode ? 0 : blockIdx.x;
+  const int split = decode ? blockIdx.z : 0;
+  attend_item(a, part, b, j, split, blockIdx.y * kHG, 0, blockIdx.y == 0 && split == 0);
+}
+
+// Items listed by the matrix-core kernel for exact recomputation (a softmax reference
+// it could not use).  redo[0] = count, redo[1 + r] = item; items are numbered as in
+// that kernel: decode (sequence, 64-head group, split) with the split fastest,
+// prefill/HCA (position from the last, sequence, 64-head group) with the group fastest.
+// grid: x = list stride, y = 8-head group within the 64-head group.
+__global__ __launch_bounds__(kThreads) void attn_redo_kernel(AttnArgs a, float* part, const int* redo,
+                                                             int split_len) {
+  const int n = redo[0];
+  const int hgroups = a.n_h / 64;
+  for (int r = blockIdx.x; r < n; r += gridDim.x) {
+    const int64_t item = redo[1 + r];
+    int b, j = 0, split = 0, hgrp;
+    if (a.mode == kModeDecode) {
+      split = (int)(item % a.num_splits);
+      const int64_t q = item / a.num_splits;
+      hgrp = (int)(q % hgroups);
+      b = (int)(q / hgroups);
+    } else {
+      const int64_t bh = (int64_t)a.batch * hgroups;
+      const int64_t u = item / bh, q = item % bh;
+      b = (int)(q / hgroups);
+      hgrp = (int)(q % hgroups);
+      j = a.T - 1 - (int)u;
+    }
+    attend_item(a, part, b, j, split, hgrp * 64 + blockIdx.y * kHG, split_len, false);
+    __syncthreads();
+  }
+}
+
 // Merge of decode partial states: one block per (head, sequence).
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, const float* part) {
   const int h = blockIdx.x, b = blockIdx.y, c = a.c, ns = a.num_splits;
@@ -328,6 +365,13 @@ hipError_t launch_attention_generic(const AttnArgs& a, void* ws, hipStream_t s) 
   if (a.mode == kModeDecode && a.num_splits > 1)
     err = launch_attention_merge(a, reinterpret_cast<const float*>(ws), s);
   return err;
+}
+
+hipError_t launch_attention_redo(const AttnArgs& a, float* part, const int* redo, int split_len,
+                                 hipStream_t s) {
+  const size_t shmem = generic_smem(a.c);
+  hipLaunchKernelGGL(attn_redo_kernel, dim3(32, 64 / kHG), dim3(kThreads), shmem, s, a, part, redo, split_len);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s) {

@@ -37,7 +37,6 @@
 #include "device_common.h"
 #include "internal.h"
 
-#include <type_traits>
 
 namespace v4a {
 
@@ -107,6 +106,7 @@ struct MqaArgs {
   const float* q_gamma;   // [512] or null
   uint16_t* out;          // [batch][T or 1][n_h][512]
   float* part;            // decode partials [batch][splits][n_h][514]
+  int* redo;              // [1 + items]: count, then queries for the exact general kernel
   int64_t t0, E_cap, lrow_base, n_lrows;
   int T, n_h, k, w, m_prime, rope_dims, mode, splits, split_len;
   float eps, rope_base, qscale;
@@ -332,16 +332,12 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   }
   const int pbase = lane * 16;
 
-  // ---- candidate passes -------------------------------------------------------
-  // kLazyPass: reference maximum from the first chunk; returns false (abandoning
-  //   the pass) when a later chunk maximum exceeds it by more than kLazy.
-  // kMaxPass: scores only, exact maximum over the whole list (fallback).
-  // kFixedPass: P V with the exact maximum (fallback, cannot abandon).
-  constexpr int kLazyPass = 0, kMaxPass = 1, kFixedPass = 2;
+  // ---- candidate loop ---------------------------------------------------------
+  // Reference maximum from the first chunk; returns false (abandoning the query) when
+  // a later chunk maximum exceeds it by more than kLazy.
   float m_ref = -INFINITY;  // head 32 hh + l32 (log2 units)
 
-  auto run = [&](auto pass_tag, f32x16 (&O)[2][4], float& l_part) -> bool {
-    constexpr int PASS = decltype(pass_tag)::value;
+  auto run = [&](f32x16 (&O)[2][4], float& l_part) -> bool {
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
@@ -349,7 +345,6 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) O[ht][nt][i] = 0.0f;
     l_part = 0.0f;
-    float m_run = -INFINITY;
     for (int64_t c = 0; c < nchunks; ++c) {
       const int64_t r0 = c * kNC;
       const char* buf = kvbuf + (int)(c & 1) * kChunkBytes;
@@ -385,22 +380,16 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
       for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, S[i]);
       lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-      if (PASS == kMaxPass) {
-        m_run = fmaxf(m_run, lmax);
-        continue;
-      }
       bool restart = false;
-      if (PASS == kLazyPass) {
+      if (c == 0) {
+        // reference maximum: this chunk's maximum over both candidate blocks
         if (hl == 0) mx_s[wv][l32] = lmax;
-        if (c == 0) {
-          // reference maximum: this chunk's maximum over both candidate blocks
-          wait_lgkmcnt<0>();
-          block_sync();
-          m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
-          if (m_ref == -INFINITY) m_ref = 0.0f;
-        } else {
-          restart = lmax > m_ref + kLazy;
-        }
+        wait_lgkmcnt<0>();
+        block_sync();
+        m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
+        if (m_ref == -INFINITY) m_ref = 0.0f;
+      } else {
+        restart = lmax > m_ref + kLazy;
       }
       float pr[16];
       float ls = 0.0f;
@@ -417,13 +406,13 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
                           pk_bf16(p0[6], p0[7])};
         *reinterpret_cast<u32x4*>(pbuf + ((hh * 4 + 2 * cc + pp) * 64) * 16 + pbase) = pk;
       }
-      if (PASS == kLazyPass) {
+      {
         const bool any = __ballot(restart) != 0;
         if (lane == 0) flag_s[wv] = any ? 1 : 0;
       }
       wait_lgkmcnt<0>();
-      block_sync();  // P (and flags) of every wave visible
-      if (PASS == kLazyPass && (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3])) return false;
+      block_sync();  // P and flags of every wave visible
+      if (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3]) return false;
 
       // O[64 heads][channel tiles of wave wv] += P V over 4 steps of 16 candidates
       __builtin_amdgcn_sched_barrier(0);
@@ -454,14 +443,6 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         O[1][nt] = mfma32(pa[p & 1][1], vb[it % 3], O[1][nt]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    if (PASS == kMaxPass) {
-      // exact maximum over both candidate blocks of the head tile
-      if (hl == 0) mx_s[wv][l32] = m_run;
-      wait_lgkmcnt<0>();
-      block_sync();
-      m_ref = fmaxf(m_run, mx_s[wv ^ 1][l32]);
-      if (m_ref == -INFINITY) m_ref = 0.0f;
     }
     return true;
   };
@@ -549,28 +530,21 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   {
     f32x16 O[2][4];
     float l_part;
-    if (run(std::integral_constant<int, kLazyPass>{}, O, l_part)) {
+    if (run(O, l_part)) {
       finish(O, l_part);
       return;
     }
   }
-  // a chunk maximum ran past the reference: exact maximum first, then P V again
-  wait_vmcnt<0>();  // a prefetch may still be landing
-  block_sync();     // every wave is done with both buffers
-  if (nchunks > 0) fill(kvbuf, 0);
-  {
-    f32x16 O[2][4];
-    float l_part;
-    run(std::integral_constant<int, kMaxPass>{}, O, l_part);
-  }
-  wait_vmcnt<0>();
-  block_sync();
-  if (nchunks > 0) fill(kvbuf, 0);
-  {
-    f32x16 O[2][4];
-    float l_part;
-    run(std::integral_constant<int, kFixedPass>{}, O, l_part);
-    finish(O, l_part);
+  // a chunk maximum ran past the reference: list this query for the exact general
+  // kernel, which recomputes it after this one.  Items are numbered as that kernel
+  // reads them: decode (sequence, head group, split), split fastest; prefill (position
+  // from the last, sequence, head group), head group fastest.
+  if (tid == 0) {
+    const int hgroups = a.n_h / kHG;
+    const int64_t item = decode ? ((int64_t)b * hgroups + hgrp) * a.splits + split
+                                : ((int64_t)blockIdx.x * gridDim.z + b) * hgroups + hgrp;
+    const int slot = atomicAdd(a.redo, 1);
+    a.redo[1 + slot] = (int)item;
   }
 }
 
@@ -584,6 +558,7 @@ struct LocalPrepArgs {
   const uint16_t* kv_new;
   const float* gamma;
   uint16_t* ws;          // [batch][n_lrows][512]
+  int* redo;             // count of the recomputation list, cleared here
   int64_t lrow_base, loc_base, n_loc, n_lrows, t;
   int w, rope_dims, decode;
   float eps, rope_base;
@@ -591,6 +566,7 @@ struct LocalPrepArgs {
 };
 
 __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.redo[0] = 0;
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int b = blockIdx.y;
@@ -662,22 +638,37 @@ static int decode_split_len(const AttnArgs& a) {
   return (int)per;
 }
 
+// Work items of the matrix-core kernel (64 heads of one query, or of one decode split).
+static int64_t mfma_items(const AttnArgs& a) {
+  const int64_t per = a.mode == kModeDecode ? (a.num_splits > 1 ? a.num_splits : 1) : a.T;
+  return (int64_t)a.batch * (a.n_h / kHG) * per;
+}
+
+// workspace: [window rows bf16][decode partials f32][recomputation list int32]
 size_t attn_mfma_workspace(const AttnArgs& a) {
   size_t loc = ((size_t)a.batch * local_rows(a) * kC * 2 + 255) / 256 * 256;
   size_t part = 0;
   if (a.mode == kModeDecode && a.num_splits > 1)
-    part = (size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float);
-  return loc + part;
+    part = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
+  const size_t redo = (size_t)(1 + mfma_items(a)) * sizeof(int);
+  return loc + part + redo;
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s);
+hipError_t launch_attention_redo(const AttnArgs& a, float* part, const int* redo, int split_len,
+                                 hipStream_t s);
 
 hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   const int64_t nl_rows = local_rows(a);
   uint16_t* lws = reinterpret_cast<uint16_t*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                         ((size_t)a.batch * nl_rows * kC * 2 + 255) / 256 * 256);
+  const size_t loc_bytes = ((size_t)a.batch * nl_rows * kC * 2 + 255) / 256 * 256;
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + loc_bytes);
+  size_t part_bytes = 0;
+  if (a.mode == kModeDecode && a.num_splits > 1)
+    part_bytes = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
+  int* redo = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + loc_bytes + part_bytes);
   LocalPrepArgs lp{};
+  lp.redo = redo;
   lp.gamma = a.kv_gamma;
   lp.ws = lws;
   lp.n_lrows = nl_rows;
@@ -716,6 +707,7 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   m.q_gamma = a.q_gamma;
   m.out = reinterpret_cast<uint16_t*>(a.out);
   m.part = part;
+  m.redo = redo;
   m.t0 = a.t0;
   m.E_cap = a.E_cap;
   m.lrow_base = lp.lrow_base;
@@ -738,6 +730,8 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(mqa_mfma_kernel<kModeDecode>, dim3((unsigned)m.splits, hgroups, (unsigned)a.batch),
                        dim3(kThreads), 0, s, m);
     err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = launch_attention_redo(a, part, redo, m.split_len, s);
     if (err != hipSuccess || m.splits <= 1) return err;
     return launch_attention_merge(a, part, s);
   }
@@ -748,7 +742,9 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   else
     hipLaunchKernelGGL(mqa_mfma_kernel<kModeCSA>, dim3((unsigned)a.T, hgroups, (unsigned)a.batch),
                        dim3(kThreads), 0, s, m);
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_attention_redo(a, part, redo, 0, s);
 }
 
 }  // namespace v4a

@@ -319,6 +319,58 @@ def test_sparse_mqa_prefill_bf16(n, n_h, c, k, w, t0, sink, rd):
     assert_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16, what="prefill")
 
 
+def _aligned_late_rows(rng, kv, c, frac=0.5):
+    """Head 0 of every query gets direction u (zero on the rotated channels) and the later
+    compressed entries are u plus small noise, so their logits exceed every first-chunk
+    logit by far more than 2^6: the kernels must fall back to their exact path.
+    kv: decoded float64 rows; returns (u, new float64 rows)."""
+    u = np.zeros(c)
+    u[:c - 64] = rng.standard_normal(c - 64)
+    E = kv.shape[0]
+    kv = np.array(kv, dtype=np.float64, copy=True)
+    kv[int(E * frac):] = u[None, :] + 0.05 * rng.standard_normal((E - int(E * frac), c))
+    return u, kv
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_attention_reference_overflow_path(mode):
+    """Logit spreads beyond the kernels' fixed-reference range (query RMSNorm weight 4,
+    late candidates aligned with the query) go through the exact recomputation.  The
+    candidate rows keep unit weight so the outputs stay O(1) for the absolute gate."""
+    n, n_h, c, k, w, t0 = 300, 64, 512, 256, 64, 700
+    P = _small_prefill(4242, n, n_h, c, k, w, t0, sink=False, rd=64)
+    rng = np.random.default_rng(77)
+    u, kv = _aligned_late_rows(rng, f64(P["kv"], "bf16"), c)
+    P["kv"] = synth.formats.bf16_bits(kv)
+    q = f64(P["q"], "bf16")
+    q[:, 0, :] = u / math.sqrt(c)
+    P["q"] = synth.formats.bf16_bits(q)
+    g = np.full(c, 4.0, np.float32)
+    gk = np.ones(c, np.float32)
+    log(f"reference-overflow path {mode}")
+    if mode == "csa":
+        out = ops.sparse_mqa_prefill(up(P["q"]), up(P["kv"]), up(P["local"]), up(P["idx"]),
+                                     up(P["cnt"]), t0=t0, w=w, dt="bf16", loc_base=P["lb"],
+                                     q_gamma=up(g), kv_gamma=up(gk), rope_dims=64)
+    else:
+        mp = 4
+        out = ops.hca_attn(up(P["q"]), up(P["kv"]), up(P["local"]), t0=t0, m_prime=mp, w=w,
+                           dt="bf16", loc_base=P["lb"], q_gamma=up(g), kv_gamma=up(gk),
+                           rope_dims=64)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                     np.random.default_rng(3).integers(0, n, 24)]))
+    if mode == "csa":
+        ref = oracle.attend_csa(f64(P["q"], "bf16"), f64(P["kv"], "bf16"), f64(P["local"], "bf16"),
+                                P["idx"], P["cnt"], loc_base=P["lb"], t0=t0, w=w, q_gamma=g,
+                                kv_gamma=gk, q_norm=True, kv_norm=True, rope_dims=64, rows=rows)
+    else:
+        ref = oracle.attend_hca(f64(P["q"], "bf16"), f64(P["kv"], "bf16"), f64(P["local"], "bf16"),
+                                loc_base=P["lb"], t0=t0, m_prime=4, w=w, q_gamma=g, kv_gamma=gk,
+                                q_norm=True, kv_norm=True, rope_dims=64, rows=rows)
+    assert_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16, what=f"{mode} overflow")
+
+
 def test_csa_prefill_flash_8k_sampled(csa8k):
     """Full V4-Flash CSA prefill chain at n=8192 in the benchmark's launch configuration."""
     cfg, d = csa8k
@@ -435,8 +487,9 @@ def _run_decode(cfg, d, num_splits=0):
     qIs = up(d["qI_scale"]).unsqueeze(1)
     idx, cnt, sc = ops.indexer_topk(qI, KI, up(d["wI"]).unsqueeze(1), dt=idt, m=m, k=k, t0=t,
                                     qI_scale=qIs, KI_scale=KIs)
+    qg = up(d["q_gamma"]) if "q_gamma" in d else g
     out = ops.sparse_mqa_decode(up(d["q"]), kv, ring, up(d["kv_new"]), idx, cnt, t=t, w=w,
-                                dt="bf16", q_gamma=g, kv_gamma=g, rope_dims=cfg["rope_dims"],
+                                dt="bf16", q_gamma=qg, kv_gamma=g, rope_dims=cfg["rope_dims"],
                                 num_splits=num_splits)
     torch.cuda.synchronize()
     return dict(kv=kv, KI=KI, KIs=KIs, ring=ring, idx=idx[:, 0], cnt=cnt[:, 0], sc=sc[:, 0],
@@ -475,7 +528,8 @@ def _check_decode(cfg, d, r, check_seqs, sink=None):
         kvd = decode_stored(r["kv"][b][sel], "bf16")  # only the selected rows
         ref_o = oracle.attend_decode(f64(d["q"][b], "bf16"), kvd, ringd,
                                      np.arange(n, dtype=np.int32), n, t=t, w=w, sink=sink,
-                                     q_gamma=d["gamma"], kv_gamma=d["gamma"], q_norm=True,
+                                     q_gamma=d.get("q_gamma", d["gamma"]), kv_gamma=d["gamma"],
+                                     q_norm=True,
                                      kv_norm=True, rope_dims=cfg["rope_dims"])
         assert_close(decode_stored(r["out"][b], "bf16"), ref_o, atol=ATOL_BF16,
                      what=f"seq {b} output")
@@ -493,6 +547,27 @@ def test_decode_pro_1m_mxfp4():
     log("decode pro B=4 L=1048576 mxfp4 keys")
     r = _run_decode(cfg, d)
     _check_decode(cfg, d, r, [0, 3])
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_reference_overflow_path(splits):
+    """Decode splits whose later candidates exceed the fixed reference by far: exact path."""
+    cfg = synth.configs.workload("csa_decode_flash_128k", batch=2, L=4096)
+    cfg["id"] = 10
+    d = synth.configs.gen_csa_decode(cfg)
+    rng = np.random.default_rng(5)
+    E = d["kv_comp"].shape[1]
+    for b in range(2):
+        u, kvb = _aligned_late_rows(rng, f64(d["kv_comp"][b], "bf16"), cfg["c"])
+        kvb[E - 1] = 0.0  # still emitted by the step
+        d["kv_comp"][b] = synth.formats.bf16_bits(kvb)
+        qb = f64(d["q"][b], "bf16")
+        qb[0] = u / math.sqrt(cfg["c"])
+        d["q"][b] = synth.formats.bf16_bits(qb)
+    d["q_gamma"] = np.full(cfg["c"], 4.0, np.float32)
+    log(f"decode reference-overflow splits={splits}")
+    r = _run_decode(cfg, d, num_splits=splits)
+    _check_decode(cfg, d, r, [0, 1])
 
 
 @pytest.mark.parametrize("splits", [1, 3, 8])
