@@ -37,6 +37,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <algorithm>
+#include <type_traits>
 
 namespace v4a {
 
@@ -90,6 +92,30 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Values known to be equal in every lane, kept in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global -> LDS loads (16 or 4 bytes per lane; lane i lands at lds + size * i),
+// written out so that the compiler does not order every later LDS read behind them:
+// each use below is followed by an explicit vmcnt wait and a barrier before the data
+// is read.  gbase is wave-uniform (scalar registers), voff a per-lane byte offset.
+// No other instruction of these kernels reads M0.
+__device__ __forceinline__ void dma_b128(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(gbase) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m0), "v"(voff), "s"(gbase) : "memory");
+}
+
 // Two floats -> packed bf16 pair (round to nearest even, hardware conversion).
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   const bf16x2 r = {(__bf16)lo, (__bf16)hi};
@@ -106,9 +132,9 @@ struct MqaArgs {
   const float* q_gamma;   // [512] or null
   uint16_t* out;          // [batch][T or 1][n_h][512]
   float* part;            // decode partials [batch][splits][n_h][514]
-  int* redo;              // [1 + items]: count, then queries for the exact general kernel
+  int* redo;              // [1 + items]: count, then items for the exact general kernel
   int64_t t0, E_cap, lrow_base, n_lrows;
-  int T, n_h, k, w, m_prime, rope_dims, mode, splits, split_len;
+  int batch, T, n_h, k, w, m_prime, rope_dims, mode, splits, split_len;
   float eps, rope_base, qscale;
   RopeTab rope;
 };
@@ -136,9 +162,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // the A fragment of P V step p' of its 32-row block.
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kChunkBytes];  // double buffer
+  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kChunkBytes];  // chunk buffers / query rows
   __shared__ __attribute__((aligned(16))) char pbuf[2 * 4 * 64 * 16];     // P [head tile][step][lane]
-  __shared__ int rowid_s[MODE == kModeHCA ? 1 : kMaxCand];
+  __shared__ __attribute__((aligned(16))) int rawidx_s[MODE == kModeHCA ? 4 : kMaxCand];  // top-k row
   __shared__ float mx_s[4][32];   // chunk maximum per (wave, head of its tile)
   __shared__ float lsum_s[4][32]; // softmax sums per (wave, head of its tile)
   __shared__ int flag_s[4];
@@ -151,99 +177,120 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = wv >> 1, cc = wv & 1;
   const int hl = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.z;
-  const int hgrp = blockIdx.y;
   const bool decode = MODE == kModeDecode;
-  // prefill: the longest candidate lists (latest positions) are dispatched first
-  const int qi = decode ? 0 : (int)(a.T - 1 - (int)blockIdx.x);
-  const int split = decode ? blockIdx.x : 0;
-  const int64_t t = decode ? a.t0 : a.t0 + qi;
   const int nq = decode ? 1 : a.T;
+  const int hgroups = a.n_h / kHG;
+  const int64_t n_items = decode ? (int64_t)a.batch * hgroups * a.splits : (int64_t)a.batch * hgroups * a.T;
 
-  // ---- candidate list of this query --------------------------------------
-  int64_t ncomp;
-  if (MODE == kModeHCA) {
-    ncomp = (t + 1) / a.m_prime;
-  } else {
-    const int64_t qrow = (int64_t)b * nq + qi;
-    ncomp = min(max(a.cnt[qrow], 0), a.k);
-  }
-  const int64_t lo = t - a.w + 1 > 0 ? t - a.w + 1 : 0;
-  const int64_t N = ncomp + (t - lo + 1);
-  int64_t ub = 0, ue = N;
-  if (decode) {
-    ub = min((int64_t)split * a.split_len, N);
-    ue = min(ub + a.split_len, N);
-  }
-  const int64_t nrows = ue - ub;
-  const int pad_id = -1 - (int)(t - a.lrow_base);  // the query's own window row
-  // RoPE angles at t for the 32 frequencies (the inverse rotation of the output uses
-  // -sin); the frequency is picked with uniform indices so it comes from scalar loads
-  if (a.rope_dims > 0 && tid < kMaxRopeDims / 2) {
-    double f = 0.0;
-#pragma unroll
-    for (int i = 0; i < kMaxRopeDims / 2; ++i) f = tid == i ? a.rope.inv_freq[i] : f;
-    float cs, sn;
-    rope_cs_fast((double)t, f, cs, sn);
-    rope_c[tid] = cs;
-    rope_s[tid] = sn;
-  }
-  // candidate indices: all loads issued before anything waits on them
-  constexpr int kIdPer = MODE == kModeHCA ? 1 : kMaxCand / kThreads;
-  int idv[kIdPer];
-  if (MODE != kModeHCA) {
-    const int32_t* idx = a.idx + ((int64_t)b * nq + qi) * a.k;
-#pragma unroll
-    for (int it = 0; it < kIdPer; ++it) {
-      // unconditional loads at a clamped (valid) position, so none waits on a branch
-      const int64_t u = min(ub + it * kThreads + tid, (int64_t)a.k - 1);
-      idv[it] = idx[u];
+  // ---- work items -----------------------------------------------------------
+  // Persistent workgroups take items blockIdx.x, +gridDim.x, ...  Prefill items run
+  // from the latest position (longest candidate list) down; decode items are
+  // (sequence, head group, candidate split).
+  struct Item {
+    int b, hgrp, qi, split;
+    int64_t t, ncomp, lo, ub, nrows, nchunks;
+  };
+  auto describe = [&](int64_t j) {
+    Item it;
+    if (decode) {
+      it.split = (int)(j % a.splits);
+      const int64_t r = j / a.splits;
+      it.hgrp = (int)(r % hgroups);
+      it.b = (int)(r / hgroups);
+      it.qi = 0;
+      it.t = a.t0;
+    } else {
+      const int64_t bh = (int64_t)a.batch * hgroups;
+      const int64_t u = j / bh, r = j % bh;
+      it.b = (int)(r / hgroups);
+      it.hgrp = (int)(r % hgroups);
+      it.qi = a.T - 1 - (int)u;
+      it.split = 0;
+      it.t = a.t0 + it.qi;
     }
-  }
+    if (MODE == kModeHCA) {
+      it.ncomp = (it.t + 1) / a.m_prime;
+    } else {
+      it.ncomp = min(max(a.cnt[(int64_t)it.b * nq + it.qi], 0), a.k);
+    }
+    it.lo = it.t - a.w + 1 > 0 ? it.t - a.w + 1 : 0;
+    const int64_t N = it.ncomp + (it.t - it.lo + 1);
+    int64_t ub = 0, ue = N;
+    if (decode) {
+      ub = min((int64_t)it.split * a.split_len, N);
+      ue = min(ub + a.split_len, N);
+    }
+    it.ub = ub;
+    it.nrows = ue - ub;
+    it.nchunks = (it.nrows + kNC - 1) / kNC;
+    it.b = uni(it.b);
+    it.hgrp = uni(it.hgrp);
+    it.qi = uni(it.qi);
+    it.split = uni(it.split);
+    it.t = uni(it.t);
+    it.ncomp = uni(it.ncomp);
+    it.lo = uni(it.lo);
+    it.ub = uni(it.ub);
+    it.nrows = uni(it.nrows);
+    it.nchunks = uni(it.nchunks);
+    return it;
+  };
 
-  // ---- query rows: all 32 fragment loads of this lane in flight at once -------
-  // lane (hl, l32): head 32 hh + l32, k-step s covers channels 16 s + 8 hl .. +7
-  uint4 qraw[32];
-  {
-    const int64_t qrow = ((int64_t)b * nq + qi) * a.n_h + (int64_t)hgrp * kHG + 32 * hh + l32;
-    const uint16_t* qr = a.q + qrow * kC + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < 32; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qr + 16 * s);
-  }
-  if (a.q_gamma) {
-    const float2 g = *reinterpret_cast<const float2*>(a.q_gamma + 2 * tid);
-    *reinterpret_cast<float2*>(qg_s + 2 * tid) = g;
-  }
-  // row id of candidate u: entry index (>= 0) or -(1 + window workspace row)
-  if (MODE != kModeHCA) {
-#pragma unroll
-    for (int it = 0; it < kIdPer; ++it) {
-      const int r = it * kThreads + tid;
-      if (r < nrows) {
-        const int64_t u = ub + r;
-        rowid_s[r] = u < ncomp ? (int)min(max((int64_t)idv[it], (int64_t)0), a.E_cap - 1)  // no faults
-                               : -1 - (int)(lo + (u - ncomp) - a.lrow_base);
+  // Query rows (64 heads x 1 KiB) of an item into chunk buffer qbuf, 16 rows per wave,
+  // 16-byte chunks swizzled like candidate rows; and its top-k row into rawidx_s.
+  auto issue_item_loads = [&](int64_t j, int qbuf) {
+    Item it;
+    if (decode) {
+      const int64_t r = j / a.splits;
+      it.hgrp = uni((int)(r % hgroups));
+      it.b = uni((int)(r / hgroups));
+      it.qi = 0;
+    } else {
+      const int64_t bh = (int64_t)a.batch * hgroups;
+      const int64_t r = j % bh;
+      it.b = uni((int)(r / hgroups));
+      it.hgrp = uni((int)(r % hgroups));
+      it.qi = uni(a.T - 1 - (int)(j / bh));
+    }
+    if (MODE != kModeHCA) {
+      const int32_t* irow = a.idx + ((int64_t)it.b * nq + it.qi) * a.k;
+      for (int j0 = 64 * wv; j0 < a.k; j0 += kThreads) {
+        if (j0 + lane < a.k) dma_b32(irow + j0, (uint32_t)lane * 4u, rawidx_s + j0);
       }
     }
-  }
-  wait_lgkmcnt<0>();
-  block_sync();  // row ids and angles visible; the query loads stay in flight
-  const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)b * a.E_cap * kC);
-  const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)b * a.n_lrows * kC);
+    const char* qrows = reinterpret_cast<const char*>(
+        a.q + (((int64_t)it.b * nq + it.qi) * a.n_h + (int64_t)it.hgrp * kHG) * kC);
+    char* dst = kvbuf + qbuf * kChunkBytes;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 16 * wv + r;
+      const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;
+      dma_b128(qrows + (int64_t)h * kRowBytes, voff, dst + h * kRowBytes);
+    }
+  };
 
   // wave wv gathers rows [16 wv, 16 wv + 16) of the chunk starting at candidate r0;
   // lane i of a row load carries chunk i of the global row into LDS chunk i ^ swz.
-  auto fill = [&](char* dst, int64_t r0) {
+  auto fill = [&](const Item& it, char* dst, int64_t r0) {
+    const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)it.b * a.E_cap * kC);
+    const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)it.b * a.n_lrows * kC);
     // lane j < 16 forms the address of row 16 wv + j; each row load then takes it
     // from that lane into scalar registers (the lane offset stays a 32-bit vector
     // operand of the scalar-base form of the load)
-    int myid = pad_id;
+    int myid = -1 - (int)(it.t - a.lrow_base);  // past the list end: the query's own window row
     const int64_t rr = r0 + 16 * wv + (lane & 15);
-    if (MODE == kModeHCA) {
-      const int64_t u = ub + rr;
-      if (rr < nrows) myid = u < ncomp ? (int)u : -1 - (int)(lo + (u - ncomp) - a.lrow_base);
-    } else if (rr < nrows) {
-      myid = rowid_s[rr];
+    if (rr < it.nrows) {
+      const int64_t u = it.ub + rr;
+      if (u < it.ncomp) {
+        if (MODE == kModeHCA) {
+          myid = (int)u;
+        } else {
+          // out-of-range indices must not fault
+          myid = (int)min(max((int64_t)rawidx_s[u], (int64_t)0), a.E_cap - 1);
+        }
+      } else {
+        myid = -1 - (int)(it.lo + (u - it.ncomp) - a.lrow_base);
+      }
     }
     const uint64_t myaddr = myid >= 0 ? (uint64_t)kvc_b + (uint64_t)myid * kRowBytes
                                       : (uint64_t)kvl_b + (uint64_t)(-1 - myid) * kRowBytes;
@@ -254,66 +301,9 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ahi, r) << 32) |
                           (uint64_t)(uint32_t)__builtin_amdgcn_readlane(alo, r);
       const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;  // rows 16 wv + r share swz(r)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(ra) + voff,
-                                       (lds_void)(dst + (16 * wv + r) * kRowBytes), 16, 0, 0);
+      dma_b128(reinterpret_cast<const char*>(ra), voff, dst + (16 * wv + r) * kRowBytes);
     }
   };
-
-  const int64_t nchunks = (nrows + kNC - 1) / kNC;
-  if (nchunks > 0) fill(kvbuf, 0);
-
-  // ---- resident query heads: B fragments of S^T = K Q^T ------------------
-  // RMS-normalised, rotated at t on the last 64 channels (k-steps 28..31), scaled
-  bf16x8 qb[32];
-  {
-    float ss = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const uint32_t wds[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = __uint_as_float(wds[e] << 16), x1 = __uint_as_float(wds[e] & 0xFFFF0000u);
-        ss = fmaf(x0, x0, ss);
-        ss = fmaf(x1, x1, ss);
-      }
-    }
-    float inv = a.qscale;
-    if (a.q_gamma) {
-      ss += __shfl_xor(ss, 32, 64);
-      inv = a.qscale / sqrtf(ss / (float)kC + a.eps);
-    }
-#pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const uint32_t wds[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
-      float y[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[2 * e] = __uint_as_float(wds[e] << 16);
-        y[2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
-      }
-      if (a.q_gamma) {
-        const float4 g0 = *reinterpret_cast<const float4*>(qg_s + 16 * s + 8 * hl);
-        const float4 g1 = *reinterpret_cast<const float4*>(qg_s + 16 * s + 8 * hl + 4);
-        y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
-        y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
-      }
-      if (s >= 28 && a.rope_dims > 0) {
-        // pairs (16 s + 8 hl + 2 j, +1) use frequency 8 (s - 28) + 4 hl + j
-        const float4 c4 = *reinterpret_cast<const float4*>(rope_c + 8 * (s - 28) + 4 * hl);
-        const float4 s4 = *reinterpret_cast<const float4*>(rope_s + 8 * (s - 28) + 4 * hl);
-        const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float y0 = y[2 * j], y1 = y[2 * j + 1];
-          y[2 * j] = y0 * cj[j] - y1 * sj[j];
-          y[2 * j + 1] = y0 * sj[j] + y1 * cj[j];
-        }
-      }
-      const u32x4 pk = {pk_bf16(y[0] * inv, y[1] * inv), pk_bf16(y[2] * inv, y[3] * inv),
-                        pk_bf16(y[4] * inv, y[5] * inv), pk_bf16(y[6] * inv, y[7] * inv)};
-      qb[s] = __builtin_bit_cast(bf16x8, pk);
-    }
-  }
 
   // ---- per-lane LDS byte offsets (everything step-dependent is an immediate) --
   // score reads: row 32 cc + l32, chunk 2 s + hl = 8 (s >> 2) + (2 (s & 3) + hl), swizzled
@@ -332,219 +322,329 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   }
   const int pbase = lane * 16;
 
-  // ---- candidate loop ---------------------------------------------------------
-  // Reference maximum from the first chunk; returns false (abandoning the query) when
-  // a later chunk maximum exceeds it by more than kLazy.
-  float m_ref = -INFINITY;  // head 32 hh + l32 (log2 units)
-
-  auto run = [&](f32x16 (&O)[2][4], float& l_part) -> bool {
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[ht][nt][i] = 0.0f;
-    l_part = 0.0f;
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const int64_t r0 = c * kNC;
-      const char* buf = kvbuf + (int)(c & 1) * kChunkBytes;
-      char* nbuf = kvbuf + kChunkBytes - (int)(c & 1) * kChunkBytes;
-      wait_vmcnt<0>();
-      block_sync();  // chunk c landed for every wave; chunk c - 1 fully consumed
-      if (c + 1 < nchunks) fill(nbuf, r0 + kNC);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // scores: 32 k-steps, fragment reads two steps ahead
-      f32x16 S;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[i] = 0.0f;
-      bf16x8 ka[3];
-      ka[0] = lds_read_b128(buf, sb[0]);
-      ka[1] = lds_read_b128(buf, sb[1]);
-#pragma unroll
-      for (int s = 0; s < 32; ++s) {
-        if (s + 2 < 32) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 3] + 128 * ((s + 2) >> 2));
-        __builtin_amdgcn_sched_barrier(0);
-        S = mfma32(ka[s % 3], qb[s], S);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // candidates past the end of the list (last chunk only)
-      if (__builtin_expect(r0 + kNC > nrows, 0)) {
-        asm volatile("" ::: "memory");  // keep this a branch: only the last chunk is partial
-        const int lim = (int)(nrows - r0) - 32 * cc - 4 * hl;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + (i & 3) >= lim) S[i] = -INFINITY;
-      }
-      float lmax = S[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, S[i]);
-      lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-      bool restart = false;
-      if (c == 0) {
-        // reference maximum: this chunk's maximum over both candidate blocks
-        if (hl == 0) mx_s[wv][l32] = lmax;
-        wait_lgkmcnt<0>();
-        block_sync();
-        m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
-        if (m_ref == -INFINITY) m_ref = 0.0f;
-      } else {
-        restart = lmax > m_ref + kLazy;
-      }
-      float pr[16];
-      float ls = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(S[i] - m_ref);
-        ls += pr[i];
-      }
-      l_part += ls;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const float* p0 = pr + 8 * pp;
-        const u32x4 pk = {pk_bf16(p0[0], p0[1]), pk_bf16(p0[2], p0[3]), pk_bf16(p0[4], p0[5]),
-                          pk_bf16(p0[6], p0[7])};
-        *reinterpret_cast<u32x4*>(pbuf + ((hh * 4 + 2 * cc + pp) * 64) * 16 + pbase) = pk;
-      }
-      {
-        const bool any = __ballot(restart) != 0;
-        if (lane == 0) flag_s[wv] = any ? 1 : 0;
-      }
-      wait_lgkmcnt<0>();
-      block_sync();  // P and flags of every wave visible
-      if (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3]) return false;
-
-      // O[64 heads][channel tiles of wave wv] += P V over 4 steps of 16 candidates
-      __builtin_amdgcn_sched_barrier(0);
-      auto vread = [&](int it) -> bf16x8 {
-        // it = 4 p + nt
-        const int off = vbase + 16384 * (it >> 2) + 256 * (it & 3);
-        const u32x2 v1 = lds_read_tr(buf, off);
-        const u32x2 v2 = lds_read_tr(buf, off + 8 * kRowBytes);
-        const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
-        return __builtin_bit_cast(bf16x8, cat);
-      };
-      bf16x8 pa[2][2];
-      bf16x8 vb[3];
-      pa[0][0] = lds_read_b128(pbuf, pbase);
-      pa[0][1] = lds_read_b128(pbuf, pbase + 4 * 1024);
-      vb[0] = vread(0);
-      vb[1] = vread(1);
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int p = it >> 2, nt = it & 3;
-        if (nt == 0 && p + 1 < 4) {
-          pa[(p + 1) & 1][0] = lds_read_b128(pbuf, pbase + (p + 1) * 1024);
-          pa[(p + 1) & 1][1] = lds_read_b128(pbuf, pbase + 4 * 1024 + (p + 1) * 1024);
-        }
-        if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        O[0][nt] = mfma32(pa[p & 1][0], vb[it % 3], O[0][nt]);
-        O[1][nt] = mfma32(pa[p & 1][1], vb[it % 3], O[1][nt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  const int64_t item = blockIdx.x;
+  if (item >= n_items) return;
+  // every load of the prologue goes out at once: top-k row and query rows (direct to
+  // LDS), then the query RMSNorm weights and the RoPE frequencies
+  constexpr int par = 0;  // chunk c lives in buffer c & 1; the query rows land in buffer 1
+  issue_item_loads(item, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  float2 g = make_float2(1.0f, 1.0f);
+  if (a.q_gamma) g = *reinterpret_cast<const float2*>(a.q_gamma + 2 * tid);
+  const double f = tid < kMaxRopeDims / 2 ? a.rope.inv_freq[tid] : 0.0;
+  {
+    const Item cur = describe(item);
+    *reinterpret_cast<float2*>(qg_s + 2 * tid) = g;
+    wait_vmcnt<0>();
+    // RoPE angles at t for the 32 frequencies (the inverse rotation of the output uses
+    // -sin); without RoPE the table is the identity, so the rotations below need no branch
+    if (tid < kMaxRopeDims / 2) {
+      float cs = 1.0f, sn = 0.0f;
+      if (a.rope_dims > 0) rope_cs_fast((double)cur.t, f, cs, sn);
+      rope_c[tid] = cs;
+      rope_s[tid] = sn;
     }
-    return true;
-  };
+    wait_lgkmcnt<0>();
+    block_sync();  // query rows, top-k row, angles (and gamma) visible
+    if (cur.nchunks > 0) fill(cur, kvbuf + par * kChunkBytes, 0);
 
-  // ---- epilogue -------------------------------------------------------------
-  auto finish = [&](f32x16 (&O)[2][4], float l_part) {
+    // ---- resident query heads: B fragments of S^T = K Q^T ------------------
+    // lane (hl, l32): head 32 hh + l32, k-step s covers channels 16 s + 8 hl .. +7.
+    // The fragments hold q * gamma, rotated at t on the last 64 channels (k-steps
+    // 28..31); the per-head factor scale * log2 e / rms(q) is applied to the scores.
+    bf16x8 qb[32];
+    float qinv;
     {
-      const float l = l_part + __shfl_xor(l_part, 32, 64);
-      if (hl == 0) {
-        lsum_s[wv][l32] = l;
-        if (cc == 0) mref_s[32 * hh + l32] = m_ref;
-      }
-    }
-    __syncthreads();  // sums visible; every wave is done with the chunk buffers
-    const bool partial = decode && a.splits > 1;
-    if (tid < kHG) {
-      const int ht = tid >> 5, h = tid & 31;
-      const float l = lsum_s[2 * ht][h] + lsum_s[2 * ht + 1][h];
-      if (partial) {
-        den_s[tid] = l;
-      } else {
-        float den = l;
-        if (a.sink) den += __builtin_amdgcn_exp2f(a.sink[hgrp * kHG + tid] * kLog2e - mref_s[tid]);
-        den_s[tid] = 1.0f / den;
-      }
-    }
-    if (partial) {
-      // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
-      float* pg = a.part + (((int64_t)b * a.splits + split) * a.n_h + (int64_t)hgrp * kHG) * (kC + 2);
+      const char* qbufp = kvbuf + (par ^ 1) * kChunkBytes;
+      auto qread = [&](int s) {
+        const int qoff = (32 * hh + l32) * kRowBytes + (((2 * (s & 3) + hl) ^ swz(l32)) << 4) + 128 * (s >> 2);
+        return __builtin_bit_cast(u32x4, lds_read_b128(qbufp, qoff));
+      };
+      // one pass in groups of 4 k-steps: all reads of a group are issued before any use
+      float ss = 0.0f;
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht)
+      for (int s0 = 0; s0 < 32; s0 += 4) {
+        u32x4 v[4];
+        float4 g[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[u] = qread(s0 + u);
+          g[u][0] = *reinterpret_cast<const float4*>(qg_s + 16 * (s0 + u) + 8 * hl);
+          g[u][1] = *reinterpret_cast<const float4*>(qg_s + 16 * (s0 + u) + 8 * hl + 4);
+        }
+        float4 c4[4], s4[4];
+        if (s0 == 28) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            // pairs (16 s + 8 hl + 2 j, +1) use frequency 8 (s - 28) + 4 hl + j (identity
+            // angles when RoPE is off)
+            c4[u] = *reinterpret_cast<const float4*>(rope_c + 8 * u + 4 * hl);
+            s4[u] = *reinterpret_cast<const float4*>(rope_s + 8 * u + 4 * hl);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int s = s0 + u;
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(v[u][e] << 16);
+            x[2 * e + 1] = __uint_as_float(v[u][e] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+          float y[8] = {x[0] * g[u][0].x, x[1] * g[u][0].y, x[2] * g[u][0].z, x[3] * g[u][0].w,
+                        x[4] * g[u][1].x, x[5] * g[u][1].y, x[6] * g[u][1].z, x[7] * g[u][1].w};
+          if (s0 == 28) {
+            const float cj[4] = {c4[u].x, c4[u].y, c4[u].z, c4[u].w};
+            const float sj[4] = {s4[u].x, s4[u].y, s4[u].z, s4[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y0 = y[2 * j], y1 = y[2 * j + 1];
+              y[2 * j] = y0 * cj[j] - y1 * sj[j];
+              y[2 * j + 1] = y0 * sj[j] + y1 * cj[j];
+            }
+          }
+          const u32x4 pk = {pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]), pk_bf16(y[4], y[5]), pk_bf16(y[6], y[7])};
+          qb[s] = __builtin_bit_cast(bf16x8, pk);
+          asm volatile("" : "+v"(qb[s]));  // materialised here, not recomputed or deferred
+        }
+      }
+      qinv = a.qscale;
+      if (a.q_gamma) {
+        ss += __shfl_xor(ss, 32, 64);
+        qinv = a.qscale / sqrtf(ss / (float)kC + a.eps);
+      }
+    }
+
+    const int sb_idx = (int)((cur.nchunks - 1 + par) & 1);  // the last chunk's buffer
+
+    // ---- candidate loop ---------------------------------------------------------
+    // Reference maximum from the first chunk; returns false (abandoning the item) when
+    // a later chunk maximum exceeds it by more than kLazy.
+    float m_ref = -INFINITY;  // head 32 hh + l32 (log2 units)
+    const int64_t nchunks = cur.nchunks;
+
+    auto run = [&](f32x16 (&O)[2][4], float& l_part) -> bool {
+      {
+        // zero the accumulators with the matrix unit, so that every value reaching the
+        // loop-carried accumulators is defined by an MFMA (keeps them in AGPRs)
+        const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        f32x16 z16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z16[i] = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) O[ht][nt] = mfma32(z8, z8, z16);
+      }
+      l_part = 0.0f;
+      for (int64_t c = 0; c < nchunks; ++c) {
+        const int64_t r0 = c * kNC;
+        const int bi = (int)((c + par) & 1);
+        const char* buf = kvbuf + bi * kChunkBytes;
+        char* nbuf = kvbuf + (bi ^ 1) * kChunkBytes;
+        wait_vmcnt<0>();
+        block_sync();  // chunk c landed for every wave; chunk c - 1 fully consumed
+        if (c + 1 < nchunks) fill(cur, nbuf, r0 + kNC);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // scores: 32 k-steps, fragment reads two steps ahead
+        f32x16 S;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[i] = 0.0f;
+        bf16x8 ka[3];
+        ka[0] = lds_read_b128(buf, sb[0]);
+        ka[1] = lds_read_b128(buf, sb[1]);
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+          if (s + 2 < 32) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 3] + 128 * ((s + 2) >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+          S = mfma32(ka[s % 3], qb[s], S);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // candidates past the end of the list (last chunk only)
+        if (__builtin_expect(r0 + kNC > cur.nrows, 0)) {
+          asm volatile("" ::: "memory");  // keep this a branch: only the last chunk is partial
+          const int lim = (int)(cur.nrows - r0) - 32 * cc - 4 * hl;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= lim) S[i] = -INFINITY;
+        }
+        float lmax = S[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, S[i]);
+        lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64)) * qinv;  // qinv > 0: order kept
+        bool restart = false;
+        if (c == 0) {
+          // reference maximum: this chunk's maximum over both candidate blocks
+          if (hl == 0) mx_s[wv][l32] = lmax;
+          wait_lgkmcnt<0>();
+          block_sync();
+          m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
+          if (m_ref == -INFINITY) m_ref = 0.0f;
+        } else {
+          restart = lmax > m_ref + kLazy;
+        }
+        float pr[16];
+        float ls = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
-          float* prow = pg + (int64_t)head * (kC + 2);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) prow[32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
+          pr[i] = __builtin_amdgcn_exp2f(fmaf(S[i], qinv, -m_ref));
+          ls += pr[i];
         }
-      if (tid < kHG) {
-        float* prow = pg + (int64_t)tid * (kC + 2);
-        prow[kC] = mref_s[tid];
-        prow[kC + 1] = den_s[tid];
-      }
-      return;
-    }
-    // stage O as float32 [64 heads][512] in the chunk buffers
-    float* stage = reinterpret_cast<float*>(kvbuf);
+        l_part += ls;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) stage[head * kC + 32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
-      }
-    __syncthreads();
-    // 8 consecutive channels of one head per thread: normalise, inverse RoPE, bf16, 16-byte store
-    uint16_t* dst = a.out + (((int64_t)b * nq + qi) * a.n_h + (int64_t)hgrp * kHG) * kC;
-#pragma unroll 4
-    for (int it = 0; it < (kHG * kC) / (8 * kThreads); ++it) {
-      const int e = (it * kThreads + tid) * 8;
-      const int head = e >> 9, ch = e & (kC - 1);
-      const float4 v0 = *reinterpret_cast<const float4*>(stage + e);
-      const float4 v1 = *reinterpret_cast<const float4*>(stage + e + 4);
-      const float inv = den_s[head];
-      float x[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv,
-                    v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
-      if (a.rope_dims > 0 && ch >= kC - 64) {
-        const int f = (ch - (kC - 64)) >> 1;  // 4 pairs, frequencies f .. f + 3
-        const float4 c4 = *reinterpret_cast<const float4*>(rope_c + f);
-        const float4 s4 = *reinterpret_cast<const float4*>(rope_s + f);
-        const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x0 = x[2 * j], x1 = x[2 * j + 1];
-          x[2 * j] = x0 * cj[j] + x1 * sj[j];
-          x[2 * j + 1] = x1 * cj[j] - x0 * sj[j];
+        for (int pp = 0; pp < 2; ++pp) {
+          const float* p0 = pr + 8 * pp;
+          const u32x4 pk = {pk_bf16(p0[0], p0[1]), pk_bf16(p0[2], p0[3]), pk_bf16(p0[4], p0[5]),
+                            pk_bf16(p0[6], p0[7])};
+          *reinterpret_cast<u32x4*>(pbuf + ((hh * 4 + 2 * cc + pp) * 64) * 16 + pbase) = pk;
         }
-      }
-      const u32x4 pk = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};
-      *reinterpret_cast<u32x4*>(dst + e) = pk;
-    }
-  };
+        {
+          const bool any = __ballot(restart) != 0;
+          if (lane == 0) flag_s[wv] = any ? 1 : 0;
+        }
+        wait_lgkmcnt<0>();
+        block_sync();  // P and flags of every wave visible
+        if (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3]) return false;
 
-  {
-    f32x16 O[2][4];
-    float l_part;
-    if (run(O, l_part)) {
-      finish(O, l_part);
-      return;
+        // O[64 heads][channel tiles of wave wv] += P V over 4 steps of 16 candidates
+        __builtin_amdgcn_sched_barrier(0);
+        auto vread = [&](int it) -> bf16x8 {
+          // it = 4 p + nt
+          const int off = vbase + 16384 * (it >> 2) + 256 * (it & 3);
+          const u32x2 v1 = lds_read_tr(buf, off);
+          const u32x2 v2 = lds_read_tr(buf, off + 8 * kRowBytes);
+          const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
+          return __builtin_bit_cast(bf16x8, cat);
+        };
+        bf16x8 pa[2][2];
+        bf16x8 vb[3];
+        pa[0][0] = lds_read_b128(pbuf, pbase);
+        pa[0][1] = lds_read_b128(pbuf, pbase + 4 * 1024);
+        vb[0] = vread(0);
+        vb[1] = vread(1);
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int p = it >> 2, nt = it & 3;
+          if (nt == 0 && p + 1 < 4) {
+            pa[(p + 1) & 1][0] = lds_read_b128(pbuf, pbase + (p + 1) * 1024);
+            pa[(p + 1) & 1][1] = lds_read_b128(pbuf, pbase + 4 * 1024 + (p + 1) * 1024);
+          }
+          if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          O[0][nt] = mfma32(pa[p & 1][0], vb[it % 3], O[0][nt]);
+          O[1][nt] = mfma32(pa[p & 1][1], vb[it % 3], O[1][nt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return true;
+    };
+
+    // ---- epilogue -------------------------------------------------------------
+    // staging in the last chunk's buffer (free once every wave passed the sums barrier)
+    auto finish = [&](f32x16 (&O)[2][4], float l_part) {
+      {
+        const float l = l_part + __shfl_xor(l_part, 32, 64);
+        if (hl == 0) {
+          lsum_s[wv][l32] = l;
+          if (cc == 0) mref_s[32 * hh + l32] = m_ref;
+        }
+      }
+      wait_lgkmcnt<0>();
+      block_sync();  // sums visible; every wave is done with the chunk buffers
+      const bool partial = decode && a.splits > 1;
+      if (tid < kHG) {
+        const int ht = tid >> 5, h = tid & 31;
+        const float l = lsum_s[2 * ht][h] + lsum_s[2 * ht + 1][h];
+        if (partial) {
+          den_s[tid] = l;
+        } else {
+          float den = l;
+          if (a.sink) den += __builtin_amdgcn_exp2f(a.sink[cur.hgrp * kHG + tid] * kLog2e - mref_s[tid]);
+          den_s[tid] = 1.0f / den;
+        }
+      }
+      if (partial) {
+        // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
+        float* pg = a.part + (((int64_t)cur.b * a.splits + cur.split) * a.n_h + (int64_t)cur.hgrp * kHG) * (kC + 2);
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
+            float* prow = pg + (int64_t)head * (kC + 2);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) prow[32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
+          }
+        if (tid < kHG) {
+          float* prow = pg + (int64_t)tid * (kC + 2);
+          prow[kC] = mref_s[tid];
+          prow[kC + 1] = den_s[tid];
+        }
+        return;
+      }
+      // two halves of 32 heads: stage O as float32 [32 heads][512] in the last chunk's
+      // buffer, then normalise, inverse RoPE, bf16 and 16-byte stores
+      float* stage = reinterpret_cast<float*>(kvbuf + sb_idx * kChunkBytes);
+      uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        if (ht == 1) {
+          wait_lgkmcnt<0>();
+          block_sync();  // every wave is done reading the first half
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int hrow = 8 * (i >> 2) + 4 * hl + (i & 3);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) stage[hrow * kC + 32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
+        }
+        wait_lgkmcnt<0>();
+        block_sync();
+#pragma unroll
+        for (int it = 0; it < (32 * kC) / (8 * kThreads); ++it) {
+          const int e = (it * kThreads + tid) * 8;
+          const int hrow = e >> 9, ch = e & (kC - 1);
+          const float4 v0 = *reinterpret_cast<const float4*>(stage + e);
+          const float4 v1 = *reinterpret_cast<const float4*>(stage + e + 4);
+          const float inv = den_s[32 * ht + hrow];
+          float x[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv,
+                        v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
+          if (ch >= kC - 64) {
+            const int f = (ch - (kC - 64)) >> 1;  // 4 pairs, frequencies f .. f + 3
+            const float4 c4 = *reinterpret_cast<const float4*>(rope_c + f);
+            const float4 s4 = *reinterpret_cast<const float4*>(rope_s + f);
+            const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x0 = x[2 * j], x1 = x[2 * j + 1];
+              x[2 * j] = x0 * cj[j] + x1 * sj[j];
+              x[2 * j + 1] = x1 * cj[j] - x0 * sj[j];
+            }
+          }
+          const u32x4 pk = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]),
+                            pk_bf16(x[6], x[7])};
+          *reinterpret_cast<u32x4*>(dst + (int64_t)32 * ht * kC + e) = pk;
+        }
+      }
+    };
+
+    {
+      f32x16 O[2][4];
+      float l_part;
+      if (run(O, l_part)) {
+        finish(O, l_part);
+      } else {
+        // a chunk maximum ran past the reference: list the item for the exact general
+        // kernel, which recomputes it after this one, and move on
+        if (tid == 0) {
+          const int slot = atomicAdd(a.redo, 1);
+          a.redo[1 + slot] = (int)item;
+        }
+      }
     }
-  }
-  // a chunk maximum ran past the reference: list this query for the exact general
-  // kernel, which recomputes it after this one.  Items are numbered as that kernel
-  // reads them: decode (sequence, head group, split), split fastest; prefill (position
-  // from the last, sequence, head group), head group fastest.
-  if (tid == 0) {
-    const int hgroups = a.n_h / kHG;
-    const int64_t item = decode ? ((int64_t)b * hgroups + hgrp) * a.splits + split
-                                : ((int64_t)blockIdx.x * gridDim.z + b) * hgroups + hgrp;
-    const int slot = atomicAdd(a.redo, 1);
-    a.redo[1 + slot] = (int)item;
   }
 }
 
@@ -723,12 +823,14 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   m.rope_base = a.rope_base;
   m.qscale = a.scale * kLog2e;
   m.rope = a.rope;
-  const unsigned hgroups = (unsigned)(a.n_h / kHG);
+  m.batch = a.batch;
+  // one workgroup per item (64 heads of one query, or of one decode split)
+  const int64_t hgroups = a.n_h / kHG;
   if (a.mode == kModeDecode) {
     m.splits = a.num_splits > 1 ? a.num_splits : 1;
     m.split_len = m.splits > 1 ? decode_split_len(a) : (a.k + a.w);
-    hipLaunchKernelGGL(mqa_mfma_kernel<kModeDecode>, dim3((unsigned)m.splits, hgroups, (unsigned)a.batch),
-                       dim3(kThreads), 0, s, m);
+    const int64_t items = (int64_t)a.batch * hgroups * m.splits;
+    hipLaunchKernelGGL(mqa_mfma_kernel<kModeDecode>, dim3((unsigned)items), dim3(kThreads), 0, s, m);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     err = launch_attention_redo(a, part, redo, m.split_len, s);
@@ -736,12 +838,11 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
     return launch_attention_merge(a, part, s);
   }
   m.splits = 1;
+  const unsigned grid = (unsigned)((int64_t)a.batch * hgroups * a.T);
   if (a.mode == kModeHCA)
-    hipLaunchKernelGGL(mqa_mfma_kernel<kModeHCA>, dim3((unsigned)a.T, hgroups, (unsigned)a.batch),
-                       dim3(kThreads), 0, s, m);
+    hipLaunchKernelGGL(mqa_mfma_kernel<kModeHCA>, dim3(grid), dim3(kThreads), 0, s, m);
   else
-    hipLaunchKernelGGL(mqa_mfma_kernel<kModeCSA>, dim3((unsigned)a.T, hgroups, (unsigned)a.batch),
-                       dim3(kThreads), 0, s, m);
+    hipLaunchKernelGGL(mqa_mfma_kernel<kModeCSA>, dim3(grid), dim3(kThreads), 0, s, m);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_attention_redo(a, part, redo, 0, s);
