@@ -417,7 +417,6 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       }
     }
 
-    const int sb_idx = (int)((cur.nchunks - 1 + par) & 1);  // the last chunk's buffer
 
     // ---- candidate loop ---------------------------------------------------------
     // Reference maximum from the first chunk; returns false (abandoning the item) when
@@ -543,7 +542,6 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     };
 
     // ---- epilogue -------------------------------------------------------------
-    // staging in the last chunk's buffer (free once every wave passed the sums barrier)
     auto finish = [&](f32x16 (&O)[2][4], float l_part) {
       {
         const float l = l_part + __shfl_xor(l_part, 32, 64);
@@ -585,49 +583,44 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         }
         return;
       }
-      // two halves of 32 heads: stage O as float32 [32 heads][512] in the last chunk's
-      // buffer, then normalise, inverse RoPE, bf16 and 16-byte stores
-      float* stage = reinterpret_cast<float*>(kvbuf + sb_idx * kChunkBytes);
-      uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
+      // stage O as float32 [64 heads][512] in both chunk buffers (every wave passed the
+      // sums barrier, so neither buffer is read any more), then normalise, inverse RoPE
+      // (identity angles when RoPE is off), bf16 and 16-byte stores, 8 channels a thread
+      float* stage = reinterpret_cast<float*>(kvbuf);
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        if (ht == 1) {
-          wait_lgkmcnt<0>();
-          block_sync();  // every wave is done reading the first half
-        }
+      for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int hrow = 8 * (i >> 2) + 4 * hl + (i & 3);
+          const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) stage[hrow * kC + 32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
+          for (int nt = 0; nt < 4; ++nt) stage[head * kC + 32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
         }
-        wait_lgkmcnt<0>();
-        block_sync();
+      wait_lgkmcnt<0>();
+      block_sync();
+      uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
+#pragma unroll 4
+      for (int it = 0; it < (kHG * kC) / (8 * kThreads); ++it) {
+        const int e = (it * kThreads + tid) * 8;
+        const int head = e >> 9, ch = e & (kC - 1);
+        const float4 v0 = *reinterpret_cast<const float4*>(stage + e);
+        const float4 v1 = *reinterpret_cast<const float4*>(stage + e + 4);
+        const float inv = den_s[head];
+        float x[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv,
+                      v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
+        if (ch >= kC - 64) {
+          const int f = (ch - (kC - 64)) >> 1;  // 4 pairs, frequencies f .. f + 3
+          const float4 c4 = *reinterpret_cast<const float4*>(rope_c + f);
+          const float4 s4 = *reinterpret_cast<const float4*>(rope_s + f);
+          const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-        for (int it = 0; it < (32 * kC) / (8 * kThreads); ++it) {
-          const int e = (it * kThreads + tid) * 8;
-          const int hrow = e >> 9, ch = e & (kC - 1);
-          const float4 v0 = *reinterpret_cast<const float4*>(stage + e);
-          const float4 v1 = *reinterpret_cast<const float4*>(stage + e + 4);
-          const float inv = den_s[32 * ht + hrow];
-          float x[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv,
-                        v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
-          if (ch >= kC - 64) {
-            const int f = (ch - (kC - 64)) >> 1;  // 4 pairs, frequencies f .. f + 3
-            const float4 c4 = *reinterpret_cast<const float4*>(rope_c + f);
-            const float4 s4 = *reinterpret_cast<const float4*>(rope_s + f);
-            const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float x0 = x[2 * j], x1 = x[2 * j + 1];
-              x[2 * j] = x0 * cj[j] + x1 * sj[j];
-              x[2 * j + 1] = x1 * cj[j] - x0 * sj[j];
-            }
+          for (int j = 0; j < 4; ++j) {
+            const float x0 = x[2 * j], x1 = x[2 * j + 1];
+            x[2 * j] = x0 * cj[j] + x1 * sj[j];
+            x[2 * j + 1] = x1 * cj[j] - x0 * sj[j];
           }
-          const u32x4 pk = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]),
-                            pk_bf16(x[6], x[7])};
-          *reinterpret_cast<u32x4*>(dst + (int64_t)32 * ht * kC + e) = pk;
         }
+        const u32x4 pk = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};
+        *reinterpret_cast<u32x4*>(dst + e) = pk;
       }
     };
 
