@@ -508,7 +508,9 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         block_sync();  // P and flags of every wave visible
         if (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3]) return false;
 
-        // O[64 heads][channel tiles of wave wv] += P V over 4 steps of 16 candidates
+        // O^T[channel tiles of wave wv][64 heads] += V^T P^T over 4 steps of 16 candidates:
+        // the V fragments are the A operand, the P fragments the B operand, so a lane ends
+        // with 4 consecutive channels of one head (stored without staging)
         __builtin_amdgcn_sched_barrier(0);
         auto vread = [&](int it) -> bf16x8 {
           // it = 4 p + nt
@@ -533,8 +535,8 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           }
           if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
           __builtin_amdgcn_sched_barrier(0);
-          O[0][nt] = mfma32(pa[p & 1][0], vb[it % 3], O[0][nt]);
-          O[1][nt] = mfma32(pa[p & 1][1], vb[it % 3], O[1][nt]);
+          O[0][nt] = mfma32(vb[it % 3], pa[p & 1][0], O[0][nt]);
+          O[1][nt] = mfma32(vb[it % 3], pa[p & 1][1], O[1][nt]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -564,18 +566,26 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           den_s[tid] = 1.0f / den;
         }
       }
+      wait_lgkmcnt<0>();
+      block_sync();  // per-head denominators visible
+      // lane (hl, l32) holds, for head tile ht and channel tile T = wv + 4 nt, head
+      // 32 ht + l32 at channels 32 T + 8 j + 4 hl + (0..3) in O[ht][nt][4 j .. 4 j + 3]
       if (partial) {
         // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
         float* pg = a.part + (((int64_t)cur.b * a.splits + cur.split) * a.n_h + (int64_t)cur.hgrp * kHG) * (kC + 2);
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
+        for (int ht = 0; ht < 2; ++ht) {
+          float* prow = pg + (int64_t)(32 * ht + l32) * (kC + 2);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
-            float* prow = pg + (int64_t)head * (kC + 2);
+          for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) prow[32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
-          }
+            for (int j = 0; j < 4; ++j) {
+              // rows are c + 2 floats long, so only 8-byte alignment is guaranteed
+              float* d = prow + 32 * (wv + 4 * nt) + 8 * j + 4 * hl;
+              *reinterpret_cast<float2*>(d) = make_float2(O[ht][nt][4 * j], O[ht][nt][4 * j + 1]);
+              *reinterpret_cast<float2*>(d + 2) = make_float2(O[ht][nt][4 * j + 2], O[ht][nt][4 * j + 3]);
+            }
+        }
         if (tid < kHG) {
           float* prow = pg + (int64_t)tid * (kC + 2);
           prow[kC] = mref_s[tid];
@@ -583,44 +593,45 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         }
         return;
       }
-      // stage O as float32 [64 heads][512] in both chunk buffers (every wave passed the
-      // sums barrier, so neither buffer is read any more), then normalise, inverse RoPE
-      // (identity angles when RoPE is off), bf16 and 16-byte stores, 8 channels a thread
-      float* stage = reinterpret_cast<float*>(kvbuf);
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int head = 32 * ht + 8 * (i >> 2) + 4 * hl + (i & 3);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) stage[head * kC + 32 * (wv + 4 * nt) + l32] = O[ht][nt][i];
-        }
-      wait_lgkmcnt<0>();
-      block_sync();
+      // normalise, inverse RoPE on the last 64 channels (waves 2 and 3, channel tile 3), bf16,
+      // then the two half-waves swap 4-channel groups so each lane stores 8 consecutive
+      // channels (16 bytes) of its head
       uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
-#pragma unroll 4
-      for (int it = 0; it < (kHG * kC) / (8 * kThreads); ++it) {
-        const int e = (it * kThreads + tid) * 8;
-        const int head = e >> 9, ch = e & (kC - 1);
-        const float4 v0 = *reinterpret_cast<const float4*>(stage + e);
-        const float4 v1 = *reinterpret_cast<const float4*>(stage + e + 4);
-        const float inv = den_s[head];
-        float x[8] = {v0.x * inv, v0.y * inv, v0.z * inv, v0.w * inv,
-                      v1.x * inv, v1.y * inv, v1.z * inv, v1.w * inv};
-        if (ch >= kC - 64) {
-          const int f = (ch - (kC - 64)) >> 1;  // 4 pairs, frequencies f .. f + 3
-          const float4 c4 = *reinterpret_cast<const float4*>(rope_c + f);
-          const float4 s4 = *reinterpret_cast<const float4*>(rope_s + f);
-          const float cj[4] = {c4.x, c4.y, c4.z, c4.w}, sj[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const float inv = den_s[32 * ht + l32];
+        uint16_t* drow = dst + (int64_t)(32 * ht + l32) * kC;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          uint32_t pk[4][2];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float x0 = x[2 * j], x1 = x[2 * j + 1];
-            x[2 * j] = x0 * cj[j] + x1 * sj[j];
-            x[2 * j + 1] = x1 * cj[j] - x0 * sj[j];
+            float x[4] = {O[ht][nt][4 * j] * inv, O[ht][nt][4 * j + 1] * inv, O[ht][nt][4 * j + 2] * inv,
+                          O[ht][nt][4 * j + 3] * inv};
+            if (nt == 3 && wv >= 2) {
+              // pairs (ch, ch + 1), ch = 32 T + 8 j + 4 hl + 2 e, use frequency (ch - (c - 64)) / 2
+              const int f = 16 * (wv - 2) + 4 * j + 2 * hl;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const float cs = rope_c[f + e], sn = rope_s[f + e];
+                const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                x[2 * e] = x0 * cs + x1 * sn;
+                x[2 * e + 1] = x1 * cs - x0 * sn;
+              }
+            }
+            pk[j][0] = pk_bf16(x[0], x[1]);
+            pk[j][1] = pk_bf16(x[2], x[3]);
+          }
+#pragma unroll
+          for (int jp = 0; jp < 2; ++jp) {
+            // lower half keeps group 2 jp and takes the upper half's; the upper half keeps
+            // group 2 jp + 1 and takes the lower half's: channels 16 jp + 8 hl .. + 7
+            const auto w0 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][0], pk[2 * jp + 1][0], false, false);
+            const auto w1 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][1], pk[2 * jp + 1][1], false, false);
+            const u32x4 v = {w0[0], w1[0], w0[1], w1[1]};
+            *reinterpret_cast<u32x4*>(drow + 32 * (wv + 4 * nt) + 16 * jp + 8 * hl) = v;
           }
         }
-        const u32x4 pk = {pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7])};
-        *reinterpret_cast<u32x4*>(dst + e) = pk;
       }
     };
 
