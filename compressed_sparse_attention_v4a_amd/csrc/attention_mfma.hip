@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   __shared__ float mref_s[kHG];
   __shared__ __attribute__((aligned(16))) float rope_c[kMaxRopeDims / 2], rope_s[kMaxRopeDims / 2];
   __shared__ __attribute__((aligned(16))) float qg_s[kC];  // query RMSNorm weights
+  __shared__ float qinv_s[kHG];  // scale * log2 e / rms(q) per head
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -348,43 +349,29 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     block_sync();  // query rows, top-k row, angles (and gamma) visible
     if (cur.nchunks > 0) fill(cur, kvbuf + par * kChunkBytes, 0);
 
-    // ---- resident query heads: B fragments of S^T = K Q^T ------------------
-    // lane (hl, l32): head 32 hh + l32, k-step s covers channels 16 s + 8 hl .. +7.
-    // The fragments hold q * gamma, rotated at t on the last 64 channels (k-steps
-    // 28..31); the per-head factor scale * log2 e / rms(q) is applied to the scores.
-    bf16x8 qb[32];
-    float qinv;
+    // ---- query rows: q * gamma, rotated at t on the last 64 channels, bf16, in place ----
+    // Wave wv prepares heads 16 wv + l16 (l16 = lane & 15); lane quarter g4 = lane >> 4
+    // takes the 16-byte chunks g4 + 4 u.  The per-head factor scale * log2 e / rms(q) is
+    // applied to the float32 scores instead.
+    char* qbufp = kvbuf + (par ^ 1) * kChunkBytes;
     {
-      const char* qbufp = kvbuf + (par ^ 1) * kChunkBytes;
-      auto qread = [&](int s) {
-        const int qoff = (32 * hh + l32) * kRowBytes + (((2 * (s & 3) + hl) ^ swz(l32)) << 4) + 128 * (s >> 2);
-        return __builtin_bit_cast(u32x4, lds_read_b128(qbufp, qoff));
-      };
-      // one pass in groups of 4 k-steps: all reads of a group are issued before any use
+      const int l16 = lane & 15, g4 = lane >> 4;
+      const int hq = 16 * wv + l16;
       float ss = 0.0f;
 #pragma unroll
-      for (int s0 = 0; s0 < 32; s0 += 4) {
+      for (int u0 = 0; u0 < 16; u0 += 4) {
         u32x4 v[4];
-        float4 g[4][2];
+        float4 gm[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          v[u] = qread(s0 + u);
-          g[u][0] = *reinterpret_cast<const float4*>(qg_s + 16 * (s0 + u) + 8 * hl);
-          g[u][1] = *reinterpret_cast<const float4*>(qg_s + 16 * (s0 + u) + 8 * hl + 4);
-        }
-        float4 c4[4], s4[4];
-        if (s0 == 28) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            // pairs (16 s + 8 hl + 2 j, +1) use frequency 8 (s - 28) + 4 hl + j (identity
-            // angles when RoPE is off)
-            c4[u] = *reinterpret_cast<const float4*>(rope_c + 8 * u + 4 * hl);
-            s4[u] = *reinterpret_cast<const float4*>(rope_s + 8 * u + 4 * hl);
-          }
+          const int j = g4 + 4 * (u0 + u);
+          v[u] = __builtin_bit_cast(u32x4, lds_read_b128(qbufp, hq * kRowBytes + ((j ^ swz(l16)) << 4)));
+          gm[u][0] = *reinterpret_cast<const float4*>(qg_s + 8 * j);
+          gm[u][1] = *reinterpret_cast<const float4*>(qg_s + 8 * j + 4);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int s = s0 + u;
+          const int j = g4 + 4 * (u0 + u);
           float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -393,30 +380,43 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-          float y[8] = {x[0] * g[u][0].x, x[1] * g[u][0].y, x[2] * g[u][0].z, x[3] * g[u][0].w,
-                        x[4] * g[u][1].x, x[5] * g[u][1].y, x[6] * g[u][1].z, x[7] * g[u][1].w};
-          if (s0 == 28) {
-            const float cj[4] = {c4[u].x, c4[u].y, c4[u].z, c4[u].w};
-            const float sj[4] = {s4[u].x, s4[u].y, s4[u].z, s4[u].w};
+          float y[8] = {x[0] * gm[u][0].x, x[1] * gm[u][0].y, x[2] * gm[u][0].z, x[3] * gm[u][0].w,
+                        x[4] * gm[u][1].x, x[5] * gm[u][1].y, x[6] * gm[u][1].z, x[7] * gm[u][1].w};
+          if (u0 + u >= 14) {
+            // chunks 56 .. 63: pairs (8 j + 2 e, +1) use frequency 4 (j - 56) + e (identity
+            // angles when RoPE is off)
+            const float4 c4 = *reinterpret_cast<const float4*>(rope_c + 4 * (j - 56));
+            const float4 s4 = *reinterpret_cast<const float4*>(rope_s + 4 * (j - 56));
+            const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+            const float sj[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float y0 = y[2 * j], y1 = y[2 * j + 1];
-              y[2 * j] = y0 * cj[j] - y1 * sj[j];
-              y[2 * j + 1] = y0 * sj[j] + y1 * cj[j];
+            for (int e = 0; e < 4; ++e) {
+              const float y0 = y[2 * e], y1 = y[2 * e + 1];
+              y[2 * e] = y0 * cj[e] - y1 * sj[e];
+              y[2 * e + 1] = y0 * sj[e] + y1 * cj[e];
             }
           }
           const u32x4 pk = {pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]), pk_bf16(y[4], y[5]), pk_bf16(y[6], y[7])};
-          qb[s] = __builtin_bit_cast(bf16x8, pk);
-          asm volatile("" : "+v"(qb[s]));  // materialised here, not recomputed or deferred
+          *reinterpret_cast<u32x4*>(qbufp + hq * kRowBytes + ((j ^ swz(l16)) << 4)) = pk;
         }
       }
-      qinv = a.qscale;
-      if (a.q_gamma) {
-        ss += __shfl_xor(ss, 32, 64);
-        qinv = a.qscale / sqrtf(ss / (float)kC + a.eps);
-      }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (g4 == 0) qinv_s[hq] = a.q_gamma ? a.qscale / sqrtf(ss / (float)kC + a.eps) : a.qscale;
     }
+    wait_lgkmcnt<0>();
+    block_sync();  // prepared query rows and factors visible
 
+    // ---- resident query heads: B fragments of S^T = K Q^T ------------------
+    // lane (hl, l32): head 32 hh + l32, k-step s covers channels 16 s + 8 hl .. +7
+    bf16x8 qb[32];
+#pragma unroll
+    for (int s = 0; s < 32; ++s)
+      qb[s] = lds_read_b128(qbufp, (32 * hh + l32) * kRowBytes + (((2 * (s & 3) + hl) ^ swz(l32)) << 4) + 128 * (s >> 2));
+    const float qinv = qinv_s[32 * hh + l32];
+    // the next chunk's gather overwrites the query rows: every fragment read has returned
+    // before the first loop barrier
+    wait_lgkmcnt<0>();
 
     // ---- candidate loop ---------------------------------------------------------
     // Reference maximum from the first chunk; returns false (abandoning the item) when

@@ -30,6 +30,30 @@ def assert_close(got, ref, *, atol=0.0, rtol=0.0, what=""):
                              f"{i}: got {got[i]!r} ref {ref[i]!r} err {err[i]:.3g} bound {bound[i]:.3g}")
 
 
+def assert_attn_close(got, ref, *, atol, rel_rms, what=""):
+    """Attention outputs: every element within `atol` (the element-wise gate), and every
+    output row (one query, one head: the last axis) within `rel_rms` of the row's RMS in RMS
+    error, plus atol / 16 for rows that are nearly zero.
+
+    The second bound is what catches structural mistakes: attention outputs of unit-RMS rows
+    averaged over hundreds of candidates are only ~0.05 in size, so a row that loses or
+    double-counts a tenth of its softmax mass can stay within an absolute 2e-2.  The bf16
+    path rounds the normalised query, the probabilities and the output to 8 significant
+    bits (2^-9 relative each), which puts its RMS error near 0.5 % of the row's RMS."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert_close(got, ref, atol=atol, what=what)
+    n = ref.shape[-1]
+    e = np.sqrt(np.mean((got - ref) ** 2, axis=-1))
+    r = np.sqrt(np.mean(ref ** 2, axis=-1))
+    bound = rel_rms * r + atol / 16.0
+    bad = ~(e <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, e / np.maximum(r, 1e-30), -np.inf)), e.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {e.size} rows (of {n}) beyond RMS bound; "
+                             f"worst at {i}: rms err {e[i]:.3g}, row rms {r[i]:.3g}")
+
+
 def assert_bf16_close(got, ref, ulps=1.0, atol=4e-6, what=""):
     """|got - ref| <= ulps * ulp_bf16(ref) + atol.  The float32 result rounded to bf16 may land
     on either neighbour of the exact value (1 ulp); atol covers float32 accumulation over up to

@@ -14,14 +14,15 @@ import torch
 
 import oracle
 import synth
-from _helpers import (assert_bf16_close, assert_close, check_topk, decode_stored, e2m1_step,
-                      fp8_step, log)
+from _helpers import (assert_attn_close, assert_bf16_close, assert_close, check_topk, decode_stored,
+                      e2m1_step, fp8_step, log)
 from compressed_sparse_attention_v4a_amd import ops
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 ATOL_BF16 = 2e-2
+REL_RMS_BF16 = 0.03  # per output row, see assert_attn_close
 ATOL_F32 = 1e-4
 
 
@@ -316,7 +317,8 @@ def test_sparse_mqa_prefill_bf16(n, n_h, c, k, w, t0, sink, rd):
                             P["idx"], P["cnt"], loc_base=P["lb"], t0=t0, w=w, sink=P["sink"],
                             q_gamma=P["g"], kv_gamma=P["g"], q_norm=True, kv_norm=True,
                             rope_dims=rd, rows=rows)
-    assert_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16, what="prefill")
+    assert_attn_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16,
+                      rel_rms=REL_RMS_BF16, what="prefill")
 
 
 def _aligned_late_rows(rng, kv, c, frac=0.5):
@@ -368,7 +370,8 @@ def test_attention_reference_overflow_path(mode):
         ref = oracle.attend_hca(f64(P["q"], "bf16"), f64(P["kv"], "bf16"), f64(P["local"], "bf16"),
                                 loc_base=P["lb"], t0=t0, m_prime=4, w=w, q_gamma=g, kv_gamma=gk,
                                 q_norm=True, kv_norm=True, rope_dims=64, rows=rows)
-    assert_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16, what=f"{mode} overflow")
+    assert_attn_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16,
+                      rel_rms=REL_RMS_BF16, what=f"{mode} overflow")
 
 
 def test_csa_prefill_flash_8k_sampled(csa8k):
@@ -396,7 +399,8 @@ def test_csa_prefill_flash_8k_sampled(csa8k):
         ref = oracle.attend_csa(qd[i:i + 1], kvd, ld, idx_h[r:r + 1], cnt_h[r:r + 1], loc_base=0,
                                 t0=int(r), w=128, q_gamma=d["gamma"], kv_gamma=d["gamma"],
                                 q_norm=True, kv_norm=True, rope_dims=64)
-        assert_close(got[r:r + 1], ref, atol=ATOL_BF16, what=f"flash row {r}")
+        assert_attn_close(got[r:r + 1], ref, atol=ATOL_BF16, rel_rms=REL_RMS_BF16,
+                          what=f"flash row {r}")
 
 
 # ---------------------------------------------------------------- HCA attention --- #
@@ -424,7 +428,8 @@ def test_hca_attn_bf16(n, n_h, c, mp, w, t0, sink):
     ref = oracle.attend_hca(f64(q, "bf16"), f64(kv, "bf16"), f64(local, "bf16"), loc_base=lb,
                             t0=t0, m_prime=mp, w=w, sink=sk, q_gamma=g, kv_gamma=g, q_norm=True,
                             kv_norm=True, rope_dims=64, rows=rows)
-    assert_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16, what="hca")
+    assert_attn_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16,
+                      rel_rms=REL_RMS_BF16, what="hca")
 
 
 def test_hca_prefill_flash_64k_sampled():
@@ -457,7 +462,8 @@ def test_hca_prefill_flash_64k_sampled():
         ref = oracle.attend_hca(f64(qrows[r], "bf16"), kvd, ld[lb:r + 1], loc_base=lb, t0=r,
                                 m_prime=128, w=128, q_gamma=d["gamma"], kv_gamma=d["gamma"],
                                 q_norm=True, kv_norm=True, rope_dims=64)
-        assert_close(decode_stored(out[0, r:r + 1], "bf16"), ref, atol=ATOL_BF16, what=f"row {r}")
+        assert_attn_close(decode_stored(out[0, r:r + 1], "bf16"), ref, atol=ATOL_BF16,
+                          rel_rms=REL_RMS_BF16, what=f"row {r}")
 
 
 # ------------------------------------------------------------------ decode step --- #
@@ -531,8 +537,8 @@ def _check_decode(cfg, d, r, check_seqs, sink=None):
                                      q_gamma=d.get("q_gamma", d["gamma"]), kv_gamma=d["gamma"],
                                      q_norm=True,
                                      kv_norm=True, rope_dims=cfg["rope_dims"])
-        assert_close(decode_stored(r["out"][b], "bf16"), ref_o, atol=ATOL_BF16,
-                     what=f"seq {b} output")
+        assert_attn_close(decode_stored(r["out"][b], "bf16"), ref_o, atol=ATOL_BF16,
+                          rel_rms=REL_RMS_BF16, what=f"seq {b} output")
 
 
 def test_decode_flash_128k_fp8():
