@@ -313,13 +313,17 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4);
   // transposing V reads, 16-lane group G = lane >> 4, J = lane & 15 = 4 i + q:
-  //   row 16 p + 8 e + 4 (G >> 1) + i, channels 32 T + 16 (G & 1) + 4 q .. +3, T = wv + 4 nt
-  int vbase;
+  //   row 16 p + 8 e + 4 (G >> 1) + i, channels 32 T + 16 (G & 1) + 4 q .. +3, T = 4 wv + nt
+  //   (wave wv owns the 128 contiguous channels 128 wv ..); chunk 16 wv + 4 nt + x lies at
+  //   byte 256 wv + 128 (nt >> 1) + 16 ((4 (nt & 1) + x) ^ swz(row)) of its row
+  int vbase[2];
   {
     const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
     const int x = 2 * (G & 1) + (q >> 1);
     const int y = (i << 1) | (G >> 1);  // swz of the row
-    vbase = (4 * (G >> 1) + i) * kRowBytes + 128 * (wv >> 1) + (((4 * (wv & 1) + x) ^ y) << 4) + 8 * (q & 1);
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd)
+      vbase[odd] = (4 * (G >> 1) + i) * kRowBytes + 256 * wv + (((4 * odd + x) ^ y) << 4) + 8 * (q & 1);
   }
   const int pbase = lane * 16;
 
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         auto vread = [&](int it) -> bf16x8 {
           // it = 4 p + nt
-          const int off = vbase + 16384 * (it >> 2) + 256 * (it & 3);
+          const int off = vbase[it & 1] + 16384 * (it >> 2) + 128 * ((it & 3) >> 1);
           const u32x2 v1 = lds_read_tr(buf, off);
           const u32x2 v2 = lds_read_tr(buf, off + 8 * kRowBytes);
           const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
@@ -568,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       }
       wait_lgkmcnt<0>();
       block_sync();  // per-head denominators visible
-      // lane (hl, l32) holds, for head tile ht and channel tile T = wv + 4 nt, head
+      // lane (hl, l32) holds, for head tile ht and channel tile T = 4 wv + nt, head
       // 32 ht + l32 at channels 32 T + 8 j + 4 hl + (0..3) in O[ht][nt][4 j .. 4 j + 3]
       if (partial) {
         // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               // rows are c + 2 floats long, so only 8-byte alignment is guaranteed
-              float* d = prow + 32 * (wv + 4 * nt) + 8 * j + 4 * hl;
+              float* d = prow + 128 * wv + 32 * nt + 8 * j + 4 * hl;
               *reinterpret_cast<float2*>(d) = make_float2(O[ht][nt][4 * j], O[ht][nt][4 * j + 1]);
               *reinterpret_cast<float2*>(d + 2) = make_float2(O[ht][nt][4 * j + 2], O[ht][nt][4 * j + 3]);
             }
@@ -593,14 +597,16 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         }
         return;
       }
-      // normalise, inverse RoPE on the last 64 channels (waves 2 and 3, channel tile 3), bf16,
-      // then the two half-waves swap 4-channel groups so each lane stores 8 consecutive
-      // channels (16 bytes) of its head
-      uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
+      // normalise, inverse RoPE on the last 64 channels (wave 3, channel tiles 2 and 3), bf16;
+      // the two half-waves swap 4-channel groups so each lane holds 8 consecutive channels,
+      // and each wave transposes its 64 heads x 128 channels through its own 16 KiB of the
+      // chunk buffers (row = head, 16-byte chunk 4 nt + 2 jp + hl at position chunk ^ (head
+      // & 7)), so that every store instruction writes 4 whole 256-byte head segments
+      char* tb = kvbuf + wv * 16384;
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         const float inv = den_s[32 * ht + l32];
-        uint16_t* drow = dst + (int64_t)(32 * ht + l32) * kC;
+        const int h = 32 * ht + l32;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           uint32_t pk[4][2];
@@ -608,9 +614,9 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           for (int j = 0; j < 4; ++j) {
             float x[4] = {O[ht][nt][4 * j] * inv, O[ht][nt][4 * j + 1] * inv, O[ht][nt][4 * j + 2] * inv,
                           O[ht][nt][4 * j + 3] * inv};
-            if (nt == 3 && wv >= 2) {
+            if (nt >= 2 && wv == 3) {
               // pairs (ch, ch + 1), ch = 32 T + 8 j + 4 hl + 2 e, use frequency (ch - (c - 64)) / 2
-              const int f = 16 * (wv - 2) + 4 * j + 2 * hl;
+              const int f = 16 * (nt - 2) + 4 * j + 2 * hl;
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
                 const float cs = rope_c[f + e], sn = rope_s[f + e];
@@ -629,9 +635,20 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
             const auto w0 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][0], pk[2 * jp + 1][0], false, false);
             const auto w1 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][1], pk[2 * jp + 1][1], false, false);
             const u32x4 v = {w0[0], w1[0], w0[1], w1[1]};
-            *reinterpret_cast<u32x4*>(drow + 32 * (wv + 4 * nt) + 16 * jp + 8 * hl) = v;
+            const int cidx = 4 * nt + 2 * jp + hl;
+            *reinterpret_cast<u32x4*>(tb + h * 256 + ((cidx ^ (h & 7)) << 4)) = v;
           }
         }
+      }
+      asm volatile("" ::: "memory");  // LDS operations of a wave complete in order
+      uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // lanes 16 k .. 16 k + 15: head 4 i + k, chunk cidx = lane & 15 = channels
+        // 128 wv + 8 cidx .. + 7
+        const int h = 4 * i + (lane >> 4), cidx = lane & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tb + h * 256 + ((cidx ^ (h & 7)) << 4));
+        *reinterpret_cast<u32x4*>(dst + (int64_t)h * kC + 128 * wv + 8 * cidx) = v;
       }
     };
 
