@@ -228,6 +228,148 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   }
 }
 
+// Entries pooling at most 8 positions (CSA, m <= 4 with overlap): one group of G = c / VEC
+// lanes per entry holds every pooled position in registers, so the softmax needs no merge
+// across lanes and the RMSNorm / quantisation maxima are shuffle reductions within the
+// group.  Each wave covers 64 / G entries; no LDS, no barriers.
+template <typename Tin, int G>
+__global__ __launch_bounds__(64) void compress_rows_kernel(CompressArgs a) {
+  constexpr int VEC = Vec<Tin>::N;
+  constexpr int kMaxPos = 8;
+  const int c = a.c, m = a.m;
+  const int lane = threadIdx.x;
+  const int g = lane % G, ch0 = g * VEC;
+  const int64_t slot = (int64_t)blockIdx.x * (64 / G) + lane / G;
+  const bool valid = slot < a.n_entries;
+  const int64_t i = a.i_begin + (valid ? slot : 0);
+  const int b = blockIdx.y;
+  const int width = a.overlap ? 2 * c : c;
+  const int npos = (a.overlap && i > 0) ? 2 * m : m;
+  const Tin* Cb = reinterpret_cast<const Tin*>(a.C) + (int64_t)b * a.n_buf * width;
+  const Tin* Zb = reinterpret_cast<const Tin*>(a.Z) + (int64_t)b * a.n_buf * width;
+
+  // every load first: logits and values of the pooled positions (u < m: stream a of
+  // block i, else stream b of block i - 1), and the positional bias rows
+  float lg[kMaxPos][VEC], cv[kMaxPos][VEC];
+#pragma unroll
+  for (int u = 0; u < kMaxPos; ++u) {
+    if (valid && u < npos) {
+      const bool sa = u < m;
+      const int64_t pos = sa ? (int64_t)m * i + u : (int64_t)m * (i - 1) + (u - m);
+      const int64_t off = (pos - a.tok_base) * width + (sa ? 0 : c) + ch0;
+      Vec<Tin>::load(Zb, off, lg[u]);
+      Vec<Tin>::load(Cb, off, cv[u]);
+      const float* brow = a.B + (int64_t)u * c + ch0;  // B^a rows 0..m-1, B^b rows m..2m-1
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) lg[u][v] = (lg[u][v] + brow[v]) * kLog2e;
+    } else {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) { lg[u][v] = -INFINITY; cv[u][v] = 0.0f; }
+    }
+  }
+  float x[VEC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float mx = lg[0][v];
+#pragma unroll
+    for (int u = 1; u < kMaxPos; ++u) mx = fmaxf(mx, lg[u][v]);
+    if (mx == -INFINITY) mx = 0.0f;  // lanes of an entry past the end
+    float sm = 0.0f, ac = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMaxPos; ++u) {
+      const float e = __builtin_amdgcn_exp2f(lg[u][v] - mx);
+      sm += e;
+      ac = fmaf(e, cv[u][v], ac);
+    }
+    x[v] = valid ? ac / sm : 0.0f;
+    ss = fmaf(x[v], x[v], ss);
+  }
+  if (a.gamma) {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = 1.0f / sqrtf(ss / (float)c + a.eps);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) x[v] = x[v] * inv * a.gamma[ch0 + v];
+  }
+  if (a.rope_dims > 0 && ch0 + VEC > c - a.rope_dims) {
+    const int r0 = c - a.rope_dims;
+    const double pos = (double)((int64_t)m * i);
+#pragma unroll
+    for (int v = 0; v < VEC; v += 2) {
+      const int ch = ch0 + v;
+      if (ch >= r0) {
+        float cs, sn;
+        // float32 entries keep the accurate sine; rounded entries take the hardware one
+        if (a.out_dt == kF32) rope_cs(pos, a.rope.inv_freq[(ch - r0) >> 1], cs, sn);
+        else rope_cs_fast(pos, a.rope.inv_freq[(ch - r0) >> 1], cs, sn);
+        const float x0 = x[v], x1 = x[v + 1];
+        x[v] = x0 * cs - x1 * sn;
+        x[v + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+
+  const int64_t orow = (int64_t)b * a.E_cap + i;
+  if (a.out_dt == kF32) {
+    if (valid) {
+      float* o = reinterpret_cast<float*>(a.out) + orow * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 4) *reinterpret_cast<float4*>(o + v) = make_float4(x[v], x[v + 1], x[v + 2], x[v + 3]);
+    }
+  } else if (a.out_dt == kBF16) {
+    if (valid) {
+      uint32_t w[VEC / 2];
+#pragma unroll
+      for (int v = 0; v < VEC; v += 2) w[v / 2] = (uint32_t)f32_to_bf16(x[v]) | ((uint32_t)f32_to_bf16(x[v + 1]) << 16);
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + orow * c + ch0;
+      if (VEC == 8) *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2 % (VEC / 2)], w[3 % (VEC / 2)]);
+      else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1 % (VEC / 2)]);
+    }
+  } else if (a.out_dt == kFP8) {
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) am = fmaxf(am, fabsf(x[v]));
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    float scale = am / 448.0f;
+    if (!(scale > 0.0f)) scale = 1.0f;
+    if (valid) {
+      uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const float y = x[v] / scale;
+        o[v] = (uint8_t)(f32_to_e4m3_abs(fabsf(y)) | (y < 0.0f ? 0x80u : 0u));
+      }
+      if (g == 0) reinterpret_cast<float*>(a.out_scale)[orow] = scale;
+    }
+  } else {  // MXFP4: blocks of 32 channels = 32 / VEC consecutive lanes of the group
+    constexpr int lpb = 32 / VEC;
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) am = fmaxf(am, fabsf(x[v]));
+#pragma unroll
+    for (int o = 1; o < lpb; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if (valid) {
+      int sexp = 0;
+      if (am > 0.0f) sexp = (int)((__float_as_uint(am) >> 23) & 255u) - 127 - 2;
+      if (sexp < -127) sexp = -127;
+      if (sexp > 127) sexp = 127;
+      const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);  // 2^-sexp (|sexp| <= 127)
+      uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow * (c / 2) + ch0 / 2;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 2) {
+        const float y0 = x[v] * inv, y1 = x[v + 1] * inv;
+        const uint32_t n0 = f32_to_e2m1_abs(fabsf(y0)) | (y0 < 0.0f ? 8u : 0u);
+        const uint32_t n1 = f32_to_e2m1_abs(fabsf(y1)) | (y1 < 0.0f ? 8u : 0u);
+        o[v / 2] = (uint8_t)(n0 | (n1 << 4));
+      }
+      if ((g % lpb) == 0)
+        reinterpret_cast<uint8_t*>(a.out_scale)[orow * (c / 32) + ch0 / 32] = (uint8_t)(sexp + 127);
+    }
+  }
+}
+
 __global__ void visibility_kernel(int64_t t0, int T, int m, int k, int w, int32_t* E, int32_t* cnt,
                                   int32_t* lo, int32_t* len) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
@@ -243,8 +385,27 @@ __global__ void visibility_kernel(int64_t t0, int T, int m, int k, int w, int32_
 
 }  // namespace
 
+template <typename Tin>
+static bool launch_rows(const CompressArgs& a, hipStream_t s) {
+  const int VEC = Vec<Tin>::N;
+  const int npos = a.overlap ? 2 * a.m : a.m;
+  if (npos > 8 || a.c % VEC != 0) return false;
+  const int G = a.c / VEC;
+  const unsigned waves = (unsigned)((a.n_entries + (64 / G) - 1) / (64 / G));
+  const dim3 grid(waves, (unsigned)a.batch);
+  switch (G) {
+    case 16: hipLaunchKernelGGL((compress_rows_kernel<Tin, 16>), grid, dim3(64), 0, s, a); return true;
+    case 32: hipLaunchKernelGGL((compress_rows_kernel<Tin, 32>), grid, dim3(64), 0, s, a); return true;
+    case 64: hipLaunchKernelGGL((compress_rows_kernel<Tin, 64>), grid, dim3(64), 0, s, a); return true;
+    default: return false;
+  }
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.n_entries <= 0 || a.batch <= 0) return hipSuccess;
+  // short pooling windows (CSA): the register-resident kernel; otherwise (HCA, m' = 128)
+  // the position-split kernel with its merge through LDS
+  if (a.in_dt == kF32 ? launch_rows<float>(a, s) : launch_rows<uint16_t>(a, s)) return hipGetLastError();
   const int VEC = a.in_dt == kF32 ? 4 : 8;
   const int G = a.c / VEC;
   const int P = kThreads / G;
