@@ -40,6 +40,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// 16x16 score tiles with heads as rows: lane (g, jj) holds heads 16 mt + 4 g + i of entry
+// jj.  Returns sum_h w_h ReLU(S_h) over all 64 heads in every lane of column jj: four
+// independent partial sums, then the four 16-lane rows are combined with the gfx950
+// row-swap instructions (no LDS round trip).  ReLU is an integer maximum of the float bits
+// with 0 (one instruction; negative values, -0 included, have negative bit patterns).
+__device__ __forceinline__ float relu_weighted_sum(const f32x4 (&S)[4], const float (&w)[4][4]) {
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fmaf(w[mt][i], __int_as_float(max(__float_as_int(S[mt][i]), 0)), p[i]);
+  float acc = (p[0] + p[1]) + (p[2] + p[3]);
+  const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+  acc = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);  // rows r and r ^ 2
+  const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+  return __uint_as_float(x16[0]) + __uint_as_float(x16[1]);  // rows r and r ^ 1
+}
+
 // Exact top-k of one query over its scores sc[0..E) by one wave; writes the
 // selected indices in ascending order, -1 padding, the count and the scores.
 __device__ void wave_topk(const float* sc, int E, int k, uint32_t* hist, int* sh, int32_t* oidx,
@@ -142,7 +160,10 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
   const int64_t Eq = qvalid ? (a.t0 + j + 1) / a.m : 0;
   const char* kb = reinterpret_cast<const char*>(a.KI) + (int64_t)b * a.E_cap * kRowB;
 
-  // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them
+  // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them.  The loads
+  // are written out (M0 = LDS destination, per-lane 64-bit source address) so that the
+  // compiler does not wait for them before every later LDS read; the loop waits for them
+  // explicitly before the barrier that publishes the tile.
   auto fill = [&](char* buf, int64_t s0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -151,8 +172,10 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
       int64_t se = s0 + e;
       if (se >= Ewg) se = Ewg - 1;         // padding rows: any visible entry (masked later)
       const int ch = (lane & 15) ^ (e & 7);
-      __builtin_amdgcn_global_load_lds(kb + se * kRowB + ch * 16, (lds_void)(buf + ins * 1024), 16, 0,
-                                       0);
+      const char* src = kb + se * kRowB + ch * 16;
+      const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void)(buf + ins * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(m0), "v"(src) : "memory");
     }
   };
   const int nchunks = (int)((Ewg + kNE - 1) / kNE);
@@ -186,26 +209,32 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
     __builtin_amdgcn_s_barrier();
     if (c + 1 < nchunks) fill(kbuf + (kNE * kRowB - cur), (int64_t)(c + 1) * kNE);
     __builtin_amdgcn_sched_barrier(0);
+    // K fragments of entry tile et + 1 are read while tile et is multiplied; the four head
+    // tiles are independent accumulation chains, interleaved k-step by k-step
+    auto kread = [&](int et, int ks) {
+      return *reinterpret_cast<const bf16x8*>(buf + ((ks & 1) ? bb1 : bb0) + et * 16 * kRowB + 128 * (ks >> 1));
+    };
+    bf16x8 kv[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kv[0][ks] = kread(0, ks);
 #pragma unroll
     for (int et = 0; et < 4; ++et) {
+      if (et + 1 < 4) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kv[(et + 1) & 1][ks] = kread(et + 1, ks);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 S[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) S[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(buf + ((ks & 1) ? bb1 : bb0) + et * 16 * kRowB +
-                                                          128 * (ks >> 1));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv, S[mt], 0, 0, 0);
+          S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv[et & 1][ks], S[mt], 0, 0, 0);
       }
-      float acc = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(wgt[mt][i], fmaxf(S[mt][i], 0.0f), acc);
-      acc += __shfl_xor(acc, 16, 64);
-      acc += __shfl_xor(acc, 32, 64);
+      __builtin_amdgcn_sched_barrier(0);
+      const float acc = relu_weighted_sum(S, wgt);
       const int64_t s = (int64_t)c * kNE + 16 * et + jj;
       if (g == 0 && s < Eq) scw[s] = acc;
     }
@@ -342,13 +371,7 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerArgs a, float*
         }
       }
     }
-    float acc = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(wq[mt][i], fmaxf(S[mt][i], 0.0f), acc);
-    acc += __shfl_xor(acc, 16, 64);
-    acc += __shfl_xor(acc, 32, 64);
+    const float acc = relu_weighted_sum(S, wq);
     if (g == 0 && sval) srow[s] = acc * ks;
   }
 }
