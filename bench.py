@@ -33,8 +33,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "c4ccd1d435594925d9dd9b54213d316d817eaa3a171660f2b36cb27ba1ef8bbc",
-           "fetch_bytes": 859157461, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "36233cb6076ed39974942adfd7fce72bf080cee1ae425be4fdcbc97c70ddec79",
+           "fetch_bytes": 859598890, "write_bytes": 536870912}
 
 
 def parse():
