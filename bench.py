@@ -9,7 +9,10 @@ resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s for the whole step, the roofline position of the
 dominant kernel (the sparse attention, measured with HIP events on its stream),
-and the float64 CPU oracle timed on a bounded sample of the same workload.
+the float64 CPU oracle timed on a bounded sample of the same workload, and the two
+decode workloads (V4-Flash at 128K context, batch 32, fp8 index keys; V4-Pro at 1M
+context, batch 4, MXFP4 index keys) as microseconds per decode call against the HBM
+roofline of the bytes the call must move.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -43,6 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -206,9 +210,124 @@ def main():
         "stages_ms": stages_ms,
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_decode:
+        del T, kv, KI, idx, cnt, out, ws_i, ws_a, q4, qI4, wI3, loc3
+        torch.cuda.empty_cache()
+        line["decode"] = {name: decode_timing(name, stream) for name in
+                          ("csa_decode_flash_128k", "csa_decode_pro_1m")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def _quant_rows(x, dt):
+    """Quantised index keys on the device: fp8 E4M3 codes with a float32 scale per row
+    (amax / 448), or MXFP4 (E2M1 pairs, low nibble first, and an E8M0 exponent per 32
+    values: 2^(floor(log2 amax) - 2), values rounded to the nearest code, saturating at 6)."""
+    import torch
+    if dt == "fp8":
+        sc = (x.abs().amax(dim=-1) / 448.0).clamp_min(1e-30)
+        codes = (x / sc.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+        return codes, sc.float()
+    blk = x.reshape(*x.shape[:-1], x.shape[-1] // 32, 32)
+    amax = blk.abs().amax(dim=-1).clamp_min(1e-30)
+    e = torch.floor(torch.log2(amax)) - 2
+    v = blk / torch.exp2(e).unsqueeze(-1)
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=x.device)
+    mag = (v.abs().unsqueeze(-1) - grid).abs().argmin(dim=-1)  # nearest magnitude code
+    code = (mag | ((v < 0) & (mag > 0)).to(torch.int64) * 8).to(torch.uint8)
+    code = code.reshape(*x.shape)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
+def decode_timing(name, stream, rounds=20, warmup=3):
+    """One decode call = tail compression (main and index entry E - 1), index scan and
+    top-k over the E entries, ring insert and sparse attention, for every sequence of the
+    batch at t = L - 1.  Inputs come from seeded device generators with the workload's
+    shapes and distributions (the parity tests run the same path on host-generated ones).
+    Reported: median over rounds with the 256 MB last-level cache flushed before each call
+    (cold, the headline) and back to back (warm)."""
+    import torch
+    from compressed_sparse_attention_v4a_amd import binding as B, costmodel, ops
+    import synth
+    cfg = synth.configs.workload(name)
+    bsz, L, c, n_h, n_hI, cI, m, k, w = (cfg[x] for x in ("batch", "L", "c", "n_h", "n_hI", "cI",
+                                                          "m", "k", "w"))
+    idt = cfg["idt"]
+    dt_code = B.FP8_E4M3 if idt == "fp8" else B.MXFP4
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x5EED0000 + 256 * cfg["id"])
+    t = L - 1
+    E = L // m
+    sc = 1.0 / math.sqrt(c)
+    rn = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=dev) * std)
+    kv = rn(bsz, E, c).to(torch.bfloat16)
+    KI, KIs = _quant_rows(rn(bsz, E, cI), idt)
+    qI, qIs = _quant_rows(rn(bsz, 1, n_hI, cI), idt)
+    wI = torch.rand(bsz, 1, n_hI, generator=gen, device=dev)
+    ring = rn(bsz, w, c, std=sc).to(torch.bfloat16)
+    kv_new = rn(bsz, c, std=sc).to(torch.bfloat16)
+    C = rn(bsz, 2 * m, 2 * c, std=sc).to(torch.bfloat16)
+    Z = rn(bsz, 2 * m, 2 * c).to(torch.bfloat16)
+    CI = rn(bsz, 2 * m, 2 * cI).to(torch.bfloat16)
+    ZI = rn(bsz, 2 * m, 2 * cI).to(torch.bfloat16)
+    Bm = rn(2 * m, c, std=math.sqrt(0.1))
+    BI = rn(2 * m, cI, std=math.sqrt(0.1))
+    q = rn(bsz, n_h, c, std=sc).to(torch.bfloat16)
+    g = torch.ones(c, device=dev)
+    gI = torch.ones(cI, device=dev)
+    idx = torch.empty(bsz, 1, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(bsz, 1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws_i_bytes = B.v4a_indexer_topk_workspace(bsz, 1, t, n_hI, cI, m, k, dt_code)
+    ws_i = ops.workspace(ws_i_bytes, dev)
+    ws_a_bytes = B.v4a_sparse_mqa_decode_workspace(bsz, n_h, c, k, w, 0, B.BF16)
+    ws_a = ops.workspace(ws_a_bytes, dev)
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    base = m * (E - 2)
+
+    def call():
+        B.v4a_compress(C, Z, B.BF16, Bm, bsz, 2 * m, base, t, 1, c, m, 1, g, 1e-6, 64, 10000.0,
+                       kv, None, B.BF16, E, stream)
+        B.v4a_compress(CI, ZI, B.BF16, BI, bsz, 2 * m, base, t, 1, cI, m, 1, gI, 1e-6, 0, 10000.0,
+                       KI, KIs, dt_code, E, stream)
+        B.v4a_indexer_topk(qI, qIs, KI, KIs, dt_code, wI, bsz, 1, t, n_hI, cI, m, k, E, idx, cnt,
+                           None, ws_i, ws_i_bytes, stream)
+        B.v4a_sparse_mqa_decode(q, kv, ring, kv_new, t, idx.reshape(bsz, k), cnt.reshape(bsz), None,
+                                g, g, 1e-6, 64, 10000.0, 0.0, bsz, n_h, c, k, w, E, 0, out, B.BF16,
+                                ws_a, ws_a_bytes, stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(2 * rounds)]
+    for r in range(rounds):
+        flush.zero_()
+        ev[r][0].record(stream)
+        call()
+        ev[r][1].record(stream)
+    for r in range(rounds, 2 * rounds):
+        ev[r][0].record(stream)
+        call()
+        ev[r][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    cold = sorted(ms[:rounds])[rounds // 2]
+    warm = sorted(ms[rounds:])[rounds // 2]
+    counts = costmodel.csa_decode_counts(bsz, L, m, k, w, n_h, c, n_hI, cI, idt)
+    gbs = counts["total_bytes"] / (cold * 1e-3) / 1e9
+    res = {"batch": bsz, "L": L, "n_h": n_h, "k": k, "index_keys": idt,
+           "us_per_call": round(cold * 1e3, 2), "us_per_call_warm": round(warm * 1e3, 2),
+           "tokens_per_s": round(bsz / (cold * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "algorithmic_bytes": counts["total_bytes"]}}
+    del kv, KI, KIs, flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(d, cfg, target_s):

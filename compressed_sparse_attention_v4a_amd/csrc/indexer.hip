@@ -177,6 +177,115 @@ __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_t
   if (threadIdx.x == 0) a.topk_cnt[q] = n;
 }
 
+// Register forms of the two stages (keys loaded once, contiguous per thread; see topk.h).
+// Stage A over tiles of 4096 entries with 256 threads.
+constexpr int kRegTile = 4096;
+
+__global__ __launch_bounds__(256) void topk_tile_reg_kernel(IndexerArgs a, const float* scores,
+                                                            int64_t ld, int n_tiles, int kc,
+                                                            uint32_t* cand_key, int32_t* cand_idx) {
+  constexpr int PER = kRegTile / 256;
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[16];
+  const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t s0 = (int64_t)tl * kRegTile;
+  const int N = (int)max((int64_t)0, min((int64_t)kRegTile, E - s0));
+  const int64_t q = (int64_t)b * a.T + j;
+  const float* srow = scores + q * ld + s0;
+  const int base = threadIdx.x * PER;
+  uint32_t key[PER];
+  if (N == kRegTile) {
+#pragma unroll
+    for (int v = 0; v < PER; v += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(srow + base + v);
+      key[v] = score_key(f.x); key[v + 1] = score_key(f.y);
+      key[v + 2] = score_key(f.z); key[v + 3] = score_key(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < PER; ++v) key[v] = base + v < N ? score_key(srow[base + v]) : 0u;
+  }
+  const bool final_out = n_tiles == 1;
+  const int want = final_out ? a.k : kc;
+  const int n = min(N, want);
+  int32_t* oidx = a.topk_idx + q * a.k;
+  float* osc = a.topk_score ? a.topk_score + q * a.k : nullptr;
+  uint32_t* ck = cand_key + (q * n_tiles + tl) * kc;
+  int32_t* ci = cand_idx + (q * n_tiles + tl) * kc;
+  auto emit = [&](int pos, int i, uint32_t kk) {
+    if (final_out) {
+      oidx[pos] = (int32_t)(s0 + i);
+      if (osc) osc[pos] = key_score(kk);
+    } else {
+      ck[pos] = kk;
+      ci[pos] = (int32_t)(s0 + i);
+    }
+  };
+  // N <= want: every element, in order (the selection "all keys > 0 or == 0" with need_eq
+  // equal to the number of zero keys among the first N is the same as taking all)
+  Selection sel{0u, kRegTile};
+  if (N > want) sel = reg_radix_select(key, N, want, hist, sh);
+  reg_select_emit(key, N, sel, sh, emit);
+  for (int p = n + threadIdx.x; p < want; p += blockDim.x) {
+    if (final_out) {
+      oidx[p] = -1;
+      if (osc) osc[p] = 0.0f;
+    } else {
+      ck[p] = 0u;  // below every real score's key
+      ci[p] = -1;
+    }
+  }
+  if (final_out && threadIdx.x == 0) a.topk_cnt[q] = n;
+}
+
+// Stage B over N = n_tiles * kc <= 1024 * PER candidates with 1024 threads.
+template <int PER>
+__global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int n_tiles, int kc,
+                                                              const uint32_t* cand_key,
+                                                              const int32_t* cand_idx) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[40];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t q = (int64_t)b * a.T + j;
+  const int k = a.k;
+  const int n = (int)min((int64_t)k, E);
+  const int N = n_tiles * kc;
+  const uint32_t* ck = cand_key + q * N;
+  const int32_t* ci = cand_idx + q * N;
+  int32_t* oidx = a.topk_idx + q * k;
+  float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
+  const int base = threadIdx.x * PER;
+  uint32_t key[PER];
+  if (base + PER <= N && (N & 3) == 0) {
+#pragma unroll
+    for (int v = 0; v < PER; v += 4) {
+      const uint4 u = *reinterpret_cast<const uint4*>(ck + base + v);
+      key[v] = u.x; key[v + 1] = u.y; key[v + 2] = u.z; key[v + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < PER; ++v) key[v] = base + v < N ? ck[base + v] : 0u;
+  }
+  if (n > 0) {
+    // exactly n real candidates are wanted; padding keys (0) rank below all of them
+    const Selection sel = reg_radix_select(key, N, n, hist, sh);
+    auto emit = [&](int pos, int i, uint32_t kk) {
+      oidx[pos] = ci[i];
+      if (osc) osc[pos] = key_score(kk);
+    };
+    reg_select_emit(key, N, sel, sh, emit);
+  }
+  for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
+    oidx[p] = -1;
+    if (osc) osc[p] = 0.0f;
+  }
+  if (threadIdx.x == 0) a.topk_cnt[q] = n;
+}
+
 }  // namespace
 
 // MFMA paths (indexer_mfma.hip)
@@ -236,12 +345,25 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
     }
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(topk_tile_kernel, dim3((unsigned)a.T, (unsigned)p.n_tiles, (unsigned)a.batch),
-                     dim3(256), 0, s, a, scores, p.ld, p.tile, p.n_tiles, p.kc, ck, ci);
+  const dim3 tgrid((unsigned)a.T, (unsigned)p.n_tiles, (unsigned)a.batch);
+  if (p.tile == kRegTile)
+    hipLaunchKernelGGL(topk_tile_reg_kernel, tgrid, dim3(256), 0, s, a, scores, p.ld, p.n_tiles, p.kc,
+                       ck, ci);
+  else
+    hipLaunchKernelGGL(topk_tile_kernel, tgrid, dim3(256), 0, s, a, scores, p.ld, p.tile, p.n_tiles,
+                       p.kc, ck, ci);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.n_tiles > 1) {
-    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.T, (unsigned)a.batch), dim3(1024), 0, s,
-                       a, p.n_tiles, p.kc, ck, ci);
+    const int64_t N = (int64_t)p.n_tiles * p.kc;
+    const dim3 mgrid((unsigned)a.T, (unsigned)a.batch);
+    if (N <= 4 * 1024)
+      hipLaunchKernelGGL(topk_merge_reg_kernel<4>, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
+    else if (N <= 16 * 1024)
+      hipLaunchKernelGGL(topk_merge_reg_kernel<16>, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
+    else if (N <= 64 * 1024)
+      hipLaunchKernelGGL(topk_merge_reg_kernel<64>, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
+    else
+      hipLaunchKernelGGL(topk_merge_kernel, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
     err = hipGetLastError();
   }
   return err;
