@@ -234,11 +234,14 @@ int v4a_sparse_mqa_prefill(const void* q, const void* kv_comp, const void* kv_lo
                     "v4a_sparse_mqa_prefill");
 }
 
-static int decode_splits(int batch, int num_splits, int k, int w) {
+static int decode_splits(int batch, int n_h, int num_splits, int k, int w) {
   if (num_splits > 0) return num_splits;
-  // enough workgroups to cover the chip: about 2 per CU over batch * head-groups
+  // about one workgroup per CU over batch x head groups x splits, but every split at least
+  // two 64-candidate chunks long: the partial states (c + 2 floats per head and split)
+  // are written and merged again, so splitting short lists costs more than it gains
+  const int groups = batch * ((n_h + 63) / 64);
   int s = 1;
-  while (batch * s < 128 && s * 64 < k + w) s *= 2;
+  while (groups * 2 * s <= 256 && 2 * s * 128 <= k + w) s *= 2;
   return s;
 }
 
@@ -247,7 +250,7 @@ size_t v4a_sparse_mqa_decode_workspace(int batch, int n_h, int c, int k, int w, 
   v4a::AttnArgs a = attn_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                               nullptr, nullptr, nullptr, 0, 0, 0, 0, batch, 0, 1, n_h, c, k, w, 0,
                               0, 0, 0, nullptr, dt, v4a::kModeDecode,
-                              decode_splits(batch, num_splits, k, w));
+                              decode_splits(batch, n_h, num_splits, k, w));
   return v4a::attn_workspace(a, g_policy.load());
 }
 
@@ -262,7 +265,7 @@ int v4a_sparse_mqa_decode(const void* q, const void* kv_comp, void* kv_ring, con
   REQUIRE(kv_ring && topk_idx && topk_cnt, V4A_EINVAL, "null kv_ring, topk_idx or topk_cnt");
   REQUIRE(t >= 0 && k >= 1 && E_cap >= 1, V4A_EINVAL, "t must be >= 0, k and E_cap >= 1");
   REQUIRE(num_splits >= 0 && num_splits <= 64, V4A_EINVAL, "num_splits must be in [0, 64]");
-  const int ns = decode_splits(batch, num_splits, k, w);
+  const int ns = decode_splits(batch, n_h, num_splits, k, w);
   v4a::AttnArgs a = attn_args(q, kv_comp, kv_ring, kv_ring, kv_new, topk_idx, topk_cnt, sink,
                               q_gamma, kv_gamma, eps, rope_dims, rope_base, scale, batch, t, 1, n_h,
                               c, k, w, 0, E_cap, 0, 0, out, dt, v4a::kModeDecode, ns);

@@ -178,15 +178,14 @@ __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_t
 }
 
 // Register forms of the two stages (keys loaded once, contiguous per thread; see topk.h).
-// Stage A over tiles of 4096 entries with 256 threads.
-constexpr int kRegTile = 4096;
-
-__global__ __launch_bounds__(256) void topk_tile_reg_kernel(IndexerArgs a, const float* scores,
+// Stage A over tiles of 16 * THREADS entries (4096 or 16384).
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void topk_tile_reg_kernel(IndexerArgs a, const float* scores,
                                                             int64_t ld, int n_tiles, int kc,
                                                             uint32_t* cand_key, int32_t* cand_idx) {
-  constexpr int PER = kRegTile / 256;
+  constexpr int PER = 16, kRegTile = PER * THREADS;
   __shared__ uint32_t hist[256];
-  __shared__ int sh[16];
+  __shared__ int sh[40];
   const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
   const int64_t t = a.t0 + j;
   const int64_t E = (t + 1) / a.m;
@@ -301,7 +300,10 @@ IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, 
   const int64_t Emax = (t0 + T) / m;
   p.ld = (Emax + 63) / 64 * 64;
   if (p.ld < 64) p.ld = 64;
+  // register-resident tile stage: 4096-entry tiles (256 threads) while the merge stays at
+  // most 8192 candidates per query, otherwise 16384-entry tiles (1024 threads)
   p.tile = 4096;
+  if ((Emax + 4095) / 4096 * (int64_t)(k < 4096 ? k : 4096) > 8192) p.tile = 16384;
   if (k > p.tile) p.tile = (k + 4095) / 4096 * 4096;
   p.n_tiles = (int)((Emax + p.tile - 1) / p.tile);
   if (p.n_tiles < 1) p.n_tiles = 1;
@@ -346,9 +348,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
     if (err != hipSuccess) return err;
   }
   const dim3 tgrid((unsigned)a.T, (unsigned)p.n_tiles, (unsigned)a.batch);
-  if (p.tile == kRegTile)
-    hipLaunchKernelGGL(topk_tile_reg_kernel, tgrid, dim3(256), 0, s, a, scores, p.ld, p.n_tiles, p.kc,
-                       ck, ci);
+  if (p.tile == 4096)
+    hipLaunchKernelGGL(topk_tile_reg_kernel<256>, tgrid, dim3(256), 0, s, a, scores, p.ld, p.n_tiles,
+                       p.kc, ck, ci);
+  else if (p.tile == 16384)
+    hipLaunchKernelGGL(topk_tile_reg_kernel<1024>, tgrid, dim3(1024), 0, s, a, scores, p.ld, p.n_tiles,
+                       p.kc, ck, ci);
   else
     hipLaunchKernelGGL(topk_tile_kernel, tgrid, dim3(256), 0, s, a, scores, p.ld, p.tile, p.n_tiles,
                        p.kc, ck, ci);
@@ -358,6 +363,8 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
     const dim3 mgrid((unsigned)a.T, (unsigned)a.batch);
     if (N <= 4 * 1024)
       hipLaunchKernelGGL(topk_merge_reg_kernel<4>, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
+    else if (N <= 8 * 1024)
+      hipLaunchKernelGGL(topk_merge_reg_kernel<8>, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
     else if (N <= 16 * 1024)
       hipLaunchKernelGGL(topk_merge_reg_kernel<16>, mgrid, dim3(1024), 0, s, a, p.n_tiles, p.kc, ck, ci);
     else if (N <= 64 * 1024)
