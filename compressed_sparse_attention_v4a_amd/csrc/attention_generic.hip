@@ -286,47 +286,82 @@ __global__ __launch_bounds__(kThreads) void attn_redo_kernel(AttnArgs a, float* 
   }
 }
 
-// Merge of decode partial states: one block per (head, sequence).
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, const float* part) {
-  const int h = blockIdx.x, b = blockIdx.y, c = a.c, ns = a.num_splits;
-  const float* p0 = part + ((int64_t)b * ns * a.n_h + h) * (c + 2);
+// Merge of decode partial states (online-softmax combination over the splits, then the
+// sink, normalisation and inverse RoPE at t).  One wave per (head, sequence), four heads
+// per block; lane l holds channels 8 l + 512 i .. + 7.  Every split's state is loaded in
+// one pass with a running maximum (no separate max / sum / value passes), so the whole
+// merge costs one memory round trip per group of splits.
+constexpr int kMergeHeads = 4;
+__global__ __launch_bounds__(64 * kMergeHeads) void attn_merge_kernel(AttnArgs a, const float* part) {
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kMergeHeads + (threadIdx.x >> 6), b = blockIdx.y;
+  if (h >= a.n_h) return;
+  const int c = a.c, ns = a.num_splits;
   const int64_t sstride = (int64_t)a.n_h * (c + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p0[s * sstride + c]);
-  float L = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = p0[s * sstride + c];
-    if (ms != -INFINITY) L += p0[s * sstride + c + 1] * __builtin_amdgcn_exp2f(ms - M);
-  }
-  if (a.sink) L += __builtin_amdgcn_exp2f(a.sink[h] * kLog2e - M);
-  const float inv = 1.0f / L;
+  const float* p0 = part + ((int64_t)b * ns * a.n_h + h) * (c + 2);
   const int r0 = c - a.rope_dims;
-  const int64_t t = a.t0;
-  for (int d = 2 * threadIdx.x; d < c; d += 2 * blockDim.x) {
-    float x0 = 0.0f, x1 = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = p0[s * sstride + c];
-      if (ms == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(ms - M);
-      x0 = fmaf(p0[s * sstride + d], f, x0);
-      x1 = fmaf(p0[s * sstride + d + 1], f, x1);
+  for (int d0 = 8 * lane; d0 < c; d0 += 512) {
+    float M = -INFINITY, L = 0.0f, acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+      const float* ps = p0 + sp * sstride;
+      // rows are c + 2 floats long (c even): 8-byte alignment only; channel pairs past c
+      // (c not a multiple of 8) are not read
+      float2 xp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xp[e] = d0 + 2 * e < c ? *reinterpret_cast<const float2*>(ps + d0 + 2 * e) : make_float2(0.0f, 0.0f);
+      const float2 ml = *reinterpret_cast<const float2*>(ps + c);  // (reference max, sum)
+      if (ml.x == -INFINITY) continue;  // a split without candidates
+      const float Mn = fmaxf(M, ml.x);
+      const float fo = __builtin_amdgcn_exp2f(M - Mn), fs = __builtin_amdgcn_exp2f(ml.x - Mn);
+      const float xs[8] = {xp[0].x, xp[0].y, xp[1].x, xp[1].y, xp[2].x, xp[2].y, xp[3].x, xp[3].y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(xs[e], fs, acc[e] * fo);
+      L = fmaf(ml.y, fs, L * fo);
+      M = Mn;
     }
-    x0 *= inv;
-    x1 *= inv;
-    if (a.rope_dims > 0 && d >= r0) {
-      float cs, sn;
-      rope_cs(-(double)t, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
-      const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-      x0 = y0;
-      x1 = y1;
+    if (a.sink) L += __builtin_amdgcn_exp2f(a.sink[h] * kLog2e - M);
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int d = d0 + e;
+      float x0 = acc[e] * inv, x1 = acc[e + 1] * inv;
+      if (a.rope_dims > 0 && d >= r0 && d < c) {
+        float cs, sn;
+        rope_cs(-(double)a.t0, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
+        const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+        x0 = y0;
+        x1 = y1;
+      }
+      acc[e] = x0;
+      acc[e + 1] = x1;
     }
-    const int64_t o = ((int64_t)b * a.n_h + h) * c + d;
-    if (a.dt == kF32) {
-      reinterpret_cast<float*>(a.out)[o] = x0;
-      reinterpret_cast<float*>(a.out)[o + 1] = x1;
+    const int64_t o = ((int64_t)b * a.n_h + h) * c + d0;
+    if ((c & 7) == 0) {
+      if (a.dt == kF32) {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)f32_to_bf16(acc[2 * e]) | ((uint32_t)f32_to_bf16(acc[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + o) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     } else {
-      reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(x0);
-      reinterpret_cast<uint16_t*>(a.out)[o + 1] = f32_to_bf16(x1);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        if (d0 + e >= c) break;
+        if (a.dt == kF32) {
+          reinterpret_cast<float*>(a.out)[o + e] = acc[e];
+          reinterpret_cast<float*>(a.out)[o + e + 1] = acc[e + 1];
+        } else {
+          reinterpret_cast<uint16_t*>(a.out)[o + e] = f32_to_bf16(acc[e]);
+          reinterpret_cast<uint16_t*>(a.out)[o + e + 1] = f32_to_bf16(acc[e + 1]);
+        }
+      }
     }
   }
 }
@@ -370,13 +405,15 @@ hipError_t launch_attention_generic(const AttnArgs& a, void* ws, hipStream_t s) 
 hipError_t launch_attention_redo(const AttnArgs& a, float* part, const int* redo, int split_len,
                                  hipStream_t s) {
   const size_t shmem = generic_smem(a.c);
-  hipLaunchKernelGGL(attn_redo_kernel, dim3(32, 64 / kHG), dim3(kThreads), shmem, s, a, part, redo, split_len);
+  // listed items are rare (never for normalised queries and rows): a few workgroups walk
+  // the list, so the launch costs little when it is empty
+  hipLaunchKernelGGL(attn_redo_kernel, dim3(2, 64 / kHG), dim3(kThreads), shmem, s, a, part, redo, split_len);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s) {
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.n_h, (unsigned)a.batch), dim3(256), 0, s,
-                     a, part);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((a.n_h + kMergeHeads - 1) / kMergeHeads), (unsigned)a.batch),
+                     dim3(64 * kMergeHeads), 0, s, a, part);
   return hipGetLastError();
 }
 

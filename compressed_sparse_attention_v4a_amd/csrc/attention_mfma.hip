@@ -21,8 +21,9 @@
 //   * Softmax with a fixed reference maximum per head (the first chunk's
 //     maximum): probabilities are exp2(s - m_ref) < 2^64, so O is never rescaled;
 //     if a later chunk maximum exceeds the reference by more than that, the
-//     workgroup restarts its candidate loop with the larger reference (exact in
-//     every case, and never triggered for normalised queries and rows).  The
+//     workgroup abandons the item and lists it for the exact general kernel, which
+//     recomputes it in float32 afterwards (never triggered for normalised queries
+//     and rows).  The
 //     score accumulator layout of the 32x32 tile is already the A-operand layout
 //     of P V (candidate k-slots permuted identically on both sides), so each
 //     wave packs its P to bf16 and stores it to LDS as ready-made fragments.
@@ -61,8 +62,8 @@ constexpr int kThreads = 256;
 constexpr int kMaxCand = 2048; // candidate-list capacity of one workgroup (k + w)
 // Probabilities are exp2(s - m_ref) with m_ref fixed after the first chunk.  They
 // stay below 2^kLazy; O (|v| < 2^6, at most 2^11 candidates) stays below 2^81, far
-// from float32 overflow.  A chunk maximum that grows further restarts the candidate
-// loop with the larger reference, so O is never rescaled.
+// from float32 overflow.  A chunk maximum that grows further sends the item to the
+// exact general kernel, so O is never rescaled.
 constexpr float kLazy = 64.0f;
 
 // XOR applied to the low three bits of the 16-byte chunk index of row r.  Eight
@@ -702,6 +703,12 @@ __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
     src = a.src + ((int64_t)b * a.n_loc + (pos - a.loc_base)) * kC;
   }
   const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * lane);
+  // RMSNorm weights are loaded with the row, not after the reduction
+  float4 g0 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), g1 = g0;
+  if (a.gamma) {
+    g0 = *reinterpret_cast<const float4*>(a.gamma + 8 * lane);
+    g1 = *reinterpret_cast<const float4*>(a.gamma + 8 * lane + 4);
+  }
   if (a.decode && pos == a.t && a.kv_new)
     *reinterpret_cast<uint4*>(a.ring + ((int64_t)b * a.w + a.t % a.w) * kC + 8 * lane) = v;
   const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
@@ -716,8 +723,9 @@ __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
   for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
   if (a.gamma) {
     const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)kC + a.eps);
+    const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * a.gamma[8 * lane + e];
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * gw[e];
   }
   const int r0 = kC - a.rope_dims;
   uint32_t o[4];

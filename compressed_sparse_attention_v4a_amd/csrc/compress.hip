@@ -267,6 +267,10 @@ __global__ __launch_bounds__(64) void compress_rows_kernel(CompressArgs a) {
       for (int v = 0; v < VEC; ++v) { lg[u][v] = -INFINITY; cv[u][v] = 0.0f; }
     }
   }
+  // RMSNorm weights go out with the other loads, not after the reduction
+  float gw[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) gw[v] = a.gamma ? a.gamma[ch0 + v] : 1.0f;
   float x[VEC];
   float ss = 0.0f;
 #pragma unroll
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(64) void compress_rows_kernel(CompressArgs a) {
     for (int o = G / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
     const float inv = 1.0f / sqrtf(ss / (float)c + a.eps);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) x[v] = x[v] * inv * a.gamma[ch0 + v];
+    for (int v = 0; v < VEC; ++v) x[v] = x[v] * inv * gw[v];
   }
   if (a.rope_dims > 0 && ch0 + VEC > c - a.rope_dims) {
     const int r0 = c - a.rope_dims;

@@ -264,9 +264,10 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 constexpr int kScanEntries = 1024;  // per workgroup (4 waves x 16 tiles x 16 entries)
+constexpr int kScanTiles = kScanEntries / 4 / 16;  // 16-entry tiles per wave
 
 template <int DT>
-__global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerArgs a, float* scores, int64_t ld) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerArgs a, float* scores, int64_t ld) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, jj = lane & 15;
@@ -326,53 +327,94 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(IndexerArgs a, float*
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.KI);
   float* srow = scores + q * ld;
   const int64_t kbase = (int64_t)b * a.E_cap;
-#pragma unroll 2
-  for (int tile = 0; tile < kScanEntries / 4 / 16; ++tile) {
-    const int64_t s0 = e0 + 16 * tile;
-    if (s0 >= E) break;
-    int64_t s = s0 + jj;
-    const bool sval = s < E;
-    if (!sval) s = E - 1;
-    const int64_t row = kbase + s;
-    f32x4 S[4];
+  // The wave's 16 tiles go in batches: every key load of a batch is issued before its
+  // first MFMA, so a wave waits for four (MXFP4: two) memory round trips instead of one per tile (the
+  // compiler, left alone, serialises load -> MFMA per tile).  Four FP8 (eight MXFP4) tiles
+  // are 32 key VGPRs, which keeps the kernel within 128 VGPRs, i.e. four waves per SIMD:
+  // the whole decode grid is resident at once.  Entries past E read the last valid row (a cache
+  // hit) and are not stored.
+  constexpr int kB = DT == kBF16 ? 1 : DT == kFP8 ? 4 : 8;  // tiles per batch
+  constexpr int kW = DT == kBF16 ? 4 : DT == kFP8 ? 2 : 1;  // 16-byte key loads per lane and tile
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) S[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float ks = 1.0f;
-    if (DT == kFP8) {
-      const uint4* p = reinterpret_cast<const uint4*>(kb + row * kCI + 32 * g);
-      const uint4 x0 = p[0], x1 = p[1];
-      const i32x8 kv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      ks = reinterpret_cast<const float*>(a.KI_scale)[row];
+  for (int b0 = 0; b0 < kScanTiles; b0 += kB) {
+    float res[kB];
+    uint4 kx[kB][kW];
+    float ksf[kB];
+    int ksc[kB];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        S[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, S[mt], 0, 0, 0, 127, 0, 127);
-    } else if (DT == kMXFP4) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(kb + row * (kCI / 2) + 16 * g);
-      const i32x8 kv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-      const int ksc = reinterpret_cast<const uint8_t*>(a.KI_scale)[row * (kCI / 32) + g];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        S[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, S[mt], 4, 4, 0, qs[mt], 0, ksc);
-    } else {
-      const uint16_t* kr = reinterpret_cast<const uint16_t*>(kb) + row * kCI + 32 * g;
-      const uint4 x0 = reinterpret_cast<const uint4*>(kr)[0], x1 = reinterpret_cast<const uint4*>(kr)[1];
-      const uint4 x2 = reinterpret_cast<const uint4*>(kr + 16)[0], x3 = reinterpret_cast<const uint4*>(kr + 16)[1];
-      const uint4 kx[4] = {x0, x1, x2, x3};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const uint4 kk = kx[st];
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, kk);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const i32x8 src = st < 2 ? qa[mt] : qa_hi[mt];
-          const uint4 qq = (st & 1) ? uint4{(unsigned)src[4], (unsigned)src[5], (unsigned)src[6], (unsigned)src[7]}
-                                    : uint4{(unsigned)src[0], (unsigned)src[1], (unsigned)src[2], (unsigned)src[3]};
-          S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qq), kv, S[mt], 0, 0, 0);
-        }
+    for (int t = 0; t < kB; ++t) {
+      int64_t s = e0 + 16 * (b0 + t) + jj;
+      if (s >= E) s = E - 1;
+      const int64_t row = kbase + s;
+      if (DT == kFP8) {
+        const uint4* p = reinterpret_cast<const uint4*>(kb + row * kCI + 32 * g);
+        kx[t][0] = p[0];
+        kx[t][1] = p[1];
+        ksf[t] = reinterpret_cast<const float*>(a.KI_scale)[row];
+      } else if (DT == kMXFP4) {
+        kx[t][0] = *reinterpret_cast<const uint4*>(kb + row * (kCI / 2) + 16 * g);
+        ksc[t] = reinterpret_cast<const uint8_t*>(a.KI_scale)[row * (kCI / 32) + g];
+      } else {
+        const uint16_t* kr = reinterpret_cast<const uint16_t*>(kb) + row * kCI + 32 * g;
+        kx[t][0] = reinterpret_cast<const uint4*>(kr)[0];
+        kx[t][1] = reinterpret_cast<const uint4*>(kr)[1];
+        kx[t][2] = reinterpret_cast<const uint4*>(kr + 16)[0];
+        kx[t][3] = reinterpret_cast<const uint4*>(kr + 16)[1];
       }
     }
-    const float acc = relu_weighted_sum(S, wq);
-    if (g == 0 && sval) srow[s] = acc * ks;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kB; ++t) {
+      f32x4 S[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) S[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      float ks = 1.0f;
+      if (DT == kFP8) {
+        const uint4 x0 = kx[t][0], x1 = kx[t][1];
+        const i32x8 kv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        ks = ksf[t];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          S[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, S[mt], 0, 0, 0, 127, 0, 127);
+      } else if (DT == kMXFP4) {
+        const uint4 x0 = kx[t][0];
+        const i32x8 kv = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          S[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kv, S[mt], 4, 4, 0, qs[mt], 0, ksc[t]);
+      } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8 kv = __builtin_bit_cast(bf16x8, kx[t][st]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const i32x8 src = st < 2 ? qa[mt] : qa_hi[mt];
+            const uint4 qq = (st & 1) ? uint4{(unsigned)src[4], (unsigned)src[5], (unsigned)src[6], (unsigned)src[7]}
+                                      : uint4{(unsigned)src[0], (unsigned)src[1], (unsigned)src[2], (unsigned)src[3]};
+            S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qq), kv, S[mt], 0, 0, 0);
+          }
+        }
+      }
+      // every lane of column jj holds the full weighted sum after the row reductions
+      res[t] = relu_weighted_sum(S, wq) * ks;
+    }
+    if (kB % 4 == 0) {
+      // lane group g stores tiles b0 + g, b0 + g + 4, ...: one instruction writes 64
+      // consecutive scores
+#pragma unroll
+      for (int u = 0; u < kB / 4; ++u) {
+        const float v = g == 0 ? res[4 * u] : g == 1 ? res[4 * u + 1] : g == 2 ? res[4 * u + 2] : res[4 * u + 3];
+        const int64_t s = e0 + 16 * (b0 + 4 * u + g) + jj;
+        if (s < E) srow[s] = v;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kB; ++t) {
+        const int64_t s = e0 + 16 * (b0 + t) + jj;
+        if (g == 0 && s < E) srow[s] = res[t];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
