@@ -232,6 +232,9 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
 // lanes per entry holds every pooled position in registers, so the softmax needs no merge
 // across lanes and the RMSNorm / quantisation maxima are shuffle reductions within the
 // group.  Each wave covers 64 / G entries; no LDS, no barriers.
+// RMSNorm weights of a call without RMSNorm (read, never applied; VEC <= 8)
+__device__ __attribute__((aligned(16))) const float kOnes[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+
 template <typename Tin, int G>
 __global__ __launch_bounds__(64) void compress_rows_kernel(CompressArgs a) {
   constexpr int VEC = Vec<Tin>::N;
@@ -248,29 +251,46 @@ __global__ __launch_bounds__(64) void compress_rows_kernel(CompressArgs a) {
   const Tin* Cb = reinterpret_cast<const Tin*>(a.C) + (int64_t)b * a.n_buf * width;
   const Tin* Zb = reinterpret_cast<const Tin*>(a.Z) + (int64_t)b * a.n_buf * width;
 
-  // every load first: logits and values of the pooled positions (u < m: stream a of
-  // block i, else stream b of block i - 1), and the positional bias rows
+  // RMSNorm weights go out with the other loads, not after the reduction
+  float gw[VEC];
+  {
+    const float* gp = a.gamma ? a.gamma + ch0 : kOnes;
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(gp + v);
+      gw[v] = g4.x; gw[v + 1] = g4.y; gw[v + 2] = g4.z; gw[v + 3] = g4.w;
+    }
+  }
+  // every load first, with no branch between them (a branch per position would make
+  // each position's loads wait for the previous ones): logits and values of the pooled
+  // positions (u < m: stream a of block i, else stream b of block i - 1) and the
+  // positional bias rows.  Positions past npos read a pooled row of the same entry
+  // (always inside the buffer) and get logit -inf.
   float lg[kMaxPos][VEC], cv[kMaxPos][VEC];
 #pragma unroll
   for (int u = 0; u < kMaxPos; ++u) {
-    if (valid && u < npos) {
-      const bool sa = u < m;
-      const int64_t pos = sa ? (int64_t)m * i + u : (int64_t)m * (i - 1) + (u - m);
-      const int64_t off = (pos - a.tok_base) * width + (sa ? 0 : c) + ch0;
-      Vec<Tin>::load(Zb, off, lg[u]);
-      Vec<Tin>::load(Cb, off, cv[u]);
-      const float* brow = a.B + (int64_t)u * c + ch0;  // B^a rows 0..m-1, B^b rows m..2m-1
+    const bool use = valid && u < npos;
+    const int uu = u < npos ? u : 0;
+    const bool sa = uu < m;
+    const int64_t pos = sa ? (int64_t)m * i + uu : (int64_t)m * (i - 1) + (uu - m);
+    const int64_t off = (pos - a.tok_base) * width + (sa ? 0 : c) + ch0;
+    Vec<Tin>::load(Zb, off, lg[u]);
+    Vec<Tin>::load(Cb, off, cv[u]);
+    const float* brow = a.B + (int64_t)uu * c + ch0;  // B^a rows 0..m-1, B^b rows m..2m-1
+    float bv[VEC];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) lg[u][v] = (lg[u][v] + brow[v]) * kLog2e;
-    } else {
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 b4 = *reinterpret_cast<const float4*>(brow + v);
+      bv[v] = b4.x; bv[v + 1] = b4.y; bv[v + 2] = b4.z; bv[v + 3] = b4.w;
+    }
+    // arithmetic masking (the loaded values are finite), so no load sits under a branch
+    const float lmask = use ? 0.0f : -INFINITY, cmask = use ? 1.0f : 0.0f;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) { lg[u][v] = -INFINITY; cv[u][v] = 0.0f; }
+    for (int v = 0; v < VEC; ++v) {
+      lg[u][v] = fmaf(lg[u][v] + bv[v], kLog2e, lmask);
+      cv[u][v] *= cmask;
     }
   }
-  // RMSNorm weights go out with the other loads, not after the reduction
-  float gw[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) gw[v] = a.gamma ? a.gamma[ch0 + v] : 1.0f;
   float x[VEC];
   float ss = 0.0f;
 #pragma unroll
