@@ -244,8 +244,9 @@ def _quant_rows(x, dt):
 def decode_timing(name, stream, rounds=20, warmup=3):
     """One decode call = tail compression (main and index entry E - 1), index scan and
     top-k over the E entries, ring insert and sparse attention, for every sequence of the
-    batch at t = L - 1.  Inputs come from seeded device generators with the workload's
-    shapes and distributions (the parity tests run the same path on host-generated ones).
+    batch at t = L - 1, through v4a_csa_decode_step (the four separate calls are timed as
+    well).  Inputs come from seeded device generators with the workload's shapes and
+    distributions (the parity tests run the same path on host-generated ones).
     Reported: median over rounds with the 256 MB last-level cache flushed before each call
     (cold, the headline) and back to back (warm)."""
     import torch
@@ -288,7 +289,7 @@ def decode_timing(name, stream, rounds=20, warmup=3):
     flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
     base = m * (E - 2)
 
-    def call():
+    def separate():
         B.v4a_compress(C, Z, B.BF16, Bm, bsz, 2 * m, base, t, 1, c, m, 1, g, 1e-6, 64, 10000.0,
                        kv, None, B.BF16, E, stream)
         B.v4a_compress(CI, ZI, B.BF16, BI, bsz, 2 * m, base, t, 1, cI, m, 1, gI, 1e-6, 0, 10000.0,
@@ -299,33 +300,53 @@ def decode_timing(name, stream, rounds=20, warmup=3):
                                 g, g, 1e-6, 64, 10000.0, 0.0, bsz, n_h, c, k, w, E, 0, out, B.BF16,
                                 ws_a, ws_a_bytes, stream)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(2 * rounds)]
-    for r in range(rounds):
-        flush.zero_()
-        ev[r][0].record(stream)
-        call()
-        ev[r][1].record(stream)
-    for r in range(rounds, 2 * rounds):
-        ev[r][0].record(stream)
-        call()
-        ev[r][1].record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ev]
-    cold = sorted(ms[:rounds])[rounds // 2]
-    warm = sorted(ms[rounds:])[rounds // 2]
+    # the same step as one call (tail compressions and window prep in one launch)
+    step = B.decode_step(
+        t=t, E_cap=E, n_buf=2 * m, tok_base=base, batch=bsz, n_h=n_h, c=c, n_hI=n_hI, cI=cI, m=m,
+        k=k, w=w, num_splits=0, rope_dims=64, rope_dims_I=0, rope_base=10000.0, eps=1e-6,
+        scale=0.0, tail_dt=B.BF16, index_dt=dt_code, attn_dt=B.BF16, C=C, Z=Z, B=Bm, gamma=g,
+        CI=CI, ZI=ZI, BI=BI, gammaI=gI, kv_comp=kv, KI=KI, KI_scale=KIs, qI=qI, qI_scale=qIs,
+        wI=wI, q=q, sink=None, q_gamma=g, kv_gamma=g, kv_ring=ring, kv_new=kv_new, topk_idx=idx,
+        topk_cnt=cnt, topk_score=None, out=out)
+    ws_s_bytes = B.v4a_csa_decode_step_workspace(step)
+    ws_s = ops.workspace(ws_s_bytes, dev)
+
+    def fused():
+        B.v4a_csa_decode_step(step, ws_s, ws_s_bytes, stream)
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(2 * rounds)]
+        for r in range(rounds):
+            flush.zero_()
+            ev[r][0].record(stream)
+            call()
+            ev[r][1].record(stream)
+        for r in range(rounds, 2 * rounds):
+            ev[r][0].record(stream)
+            call()
+            ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        return sorted(ms[:rounds])[rounds // 2], sorted(ms[rounds:])[rounds // 2]
+
+    cold_sep, warm_sep = timed(separate)
+    cold, warm = timed(fused)
     counts = costmodel.csa_decode_counts(bsz, L, m, k, w, n_h, c, n_hI, cI, idt)
     gbs = counts["total_bytes"] / (cold * 1e-3) / 1e9
     res = {"batch": bsz, "L": L, "n_h": n_h, "k": k, "index_keys": idt,
+           "entry": "v4a_csa_decode_step",
            "us_per_call": round(cold * 1e3, 2), "us_per_call_warm": round(warm * 1e3, 2),
+           "us_per_call_separate_calls": round(cold_sep * 1e3, 2),
+           "us_per_call_separate_calls_warm": round(warm_sep * 1e3, 2),
            "tokens_per_s": round(bsz / (cold * 1e-3), 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": counts["total_bytes"]}}
-    del kv, KI, KIs, flush
+    del kv, KI, KIs, flush, ws_s
     torch.cuda.empty_cache()
     return res
 

@@ -58,8 +58,60 @@ def lib() -> ct.CDLL:
         L.v4a_hca_attn_workspace.argtypes = [i32, i64, i32, i64, i64, i32, i32, i32, i32, i32]
         L.v4a_hca_attn.argtypes = [vp, vp, vp, i64, i64, vp, vp, vp, f32, i32, f32, f32, i32, i64,
                                    i32, i32, i32, i32, i32, i64, vp, i32, vp, sz, vp]
+        L.v4a_decode_step_layout.restype = i32
+        L.v4a_decode_step_layout.argtypes = [vp, i32, vp]
+        L.v4a_csa_decode_step_workspace.restype = sz
+        L.v4a_csa_decode_step_workspace.argtypes = [vp]
+        L.v4a_csa_decode_step.argtypes = [vp, vp, sz, vp]
+        _check_step_layout(L)
         _lib = L
     return _lib
+
+
+class DecodeStep(ct.Structure):
+    """Mirror of v4a_decode_step (field order and types as declared in include/v4a.h;
+    checked against the library's own offsets when the library loads)."""
+    _fields_ = (
+        [(n, ct.c_int64) for n in ("t", "E_cap", "n_buf", "tok_base")]
+        + [(n, ct.c_int) for n in ("batch", "n_h", "c", "n_hI", "cI", "m", "k", "w", "num_splits",
+                                   "rope_dims", "rope_dims_I")]
+        + [(n, ct.c_float) for n in ("rope_base", "eps", "scale")]
+        + [(n, ct.c_int) for n in ("tail_dt", "index_dt", "attn_dt")]
+        + [(n, ct.c_void_p) for n in ("C", "Z", "B", "gamma", "CI", "ZI", "BI", "gammaI", "kv_comp",
+                                      "KI", "KI_scale", "qI", "qI_scale", "wI", "q", "sink",
+                                      "q_gamma", "kv_gamma", "kv_ring", "kv_new", "topk_idx",
+                                      "topk_cnt", "topk_score", "out")])
+
+
+def _check_step_layout(L):
+    n = len(DecodeStep._fields_)
+    off = (ct.c_size_t * n)()
+    size = ct.c_size_t()
+    nf = L.v4a_decode_step_layout(ct.cast(off, ct.c_void_p), n, ct.cast(ct.byref(size), ct.c_void_p))
+    mine = [getattr(DecodeStep, f).offset for f, _ in DecodeStep._fields_]
+    if nf != n or list(off) != mine or size.value != ct.sizeof(DecodeStep):
+        raise RuntimeError("v4a_decode_step layout of the library does not match the binding")
+
+
+def decode_step(**fields) -> DecodeStep:
+    """A DecodeStep from keyword arguments: tensors (or None) for the pointer fields,
+    numbers for the rest (unset fields are 0 / NULL)."""
+    d = DecodeStep()
+    ptrs = {f for f, t in DecodeStep._fields_ if t is ct.c_void_p}
+    for key, val in fields.items():
+        if key not in {f for f, _ in DecodeStep._fields_}:
+            raise TypeError(f"unknown decode-step field {key!r}")
+        setattr(d, key, (None if val is None else val.data_ptr()) if key in ptrs else val)
+    return d
+
+
+def v4a_csa_decode_step_workspace(step: DecodeStep) -> int:
+    return lib().v4a_csa_decode_step_workspace(ct.c_void_p(ct.addressof(step)))
+
+
+def v4a_csa_decode_step(step: DecodeStep, ws, ws_bytes, stream=None):
+    _check("v4a_csa_decode_step", lib().v4a_csa_decode_step(
+        ct.c_void_p(ct.addressof(step)), _p(ws), ws_bytes, _s(stream)))
 
 
 def _p(t):

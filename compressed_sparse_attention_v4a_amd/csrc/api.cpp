@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstddef>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -90,10 +91,14 @@ int v4a_visibility(int64_t t0, int T, int m, int k, int w, int32_t* E, int32_t* 
                     "v4a_visibility");
 }
 
-int v4a_compress(const void* C, const void* Z, v4a_dtype in_dt, const float* B, int batch,
-                 int64_t n_buf, int64_t tok_base, int64_t t0, int T, int c, int m, int overlap,
-                 const float* gamma, float eps, int rope_dims, float rope_base, void* out,
-                 void* out_scale, v4a_dtype out_dt, int64_t E_cap, void* stream) {
+}  // extern "C"
+
+// Validation and internal arguments of v4a_compress (shared with the decode step).
+static int compress_prepare(const void* C, const void* Z, v4a_dtype in_dt, const float* B,
+                            int batch, int64_t n_buf, int64_t tok_base, int64_t t0, int T, int c,
+                            int m, int overlap, const float* gamma, float eps, int rope_dims,
+                            float rope_base, void* out, void* out_scale, v4a_dtype out_dt,
+                            int64_t E_cap, v4a::CompressArgs& a) {
   REQUIRE(C && Z && B && out, V4A_EINVAL, "null C, Z, B or out");
   REQUIRE(batch >= 1, V4A_EINVAL, "batch must be >= 1");
   REQUIRE(c >= 2 && c % 2 == 0, V4A_EINVAL, "c must be even and >= 2 (got %d)", c);
@@ -131,12 +136,25 @@ int v4a_compress(const void* C, const void* Z, v4a_dtype in_dt, const float* B, 
             "buffer ends at position %lld but entry %lld needs position %lld",
             (long long)(tok_base + n_buf), (long long)(i_end - 1), (long long)(m * i_end - 1));
   }
-  v4a::CompressArgs a{};
+  a = v4a::CompressArgs{};
   a.C = C; a.Z = Z; a.B = B; a.gamma = gamma; a.out = out; a.out_scale = out_scale;
   a.n_buf = n_buf; a.tok_base = tok_base; a.i_begin = i_begin; a.E_cap = E_cap;
   a.n_entries = (int)(i_end - i_begin); a.batch = batch; a.c = c; a.m = m; a.overlap = overlap;
   a.rope_dims = rope_dims; a.in_dt = in_dt; a.out_dt = out_dt; a.eps = eps; a.rope_base = rope_base;
   v4a::rope_table(a.rope, rope_dims, rope_base);
+  return V4A_OK;
+}
+
+extern "C" {
+
+int v4a_compress(const void* C, const void* Z, v4a_dtype in_dt, const float* B, int batch,
+                 int64_t n_buf, int64_t tok_base, int64_t t0, int T, int c, int m, int overlap,
+                 const float* gamma, float eps, int rope_dims, float rope_base, void* out,
+                 void* out_scale, v4a_dtype out_dt, int64_t E_cap, void* stream) {
+  v4a::CompressArgs a;
+  const int rc = compress_prepare(C, Z, in_dt, B, batch, n_buf, tok_base, t0, T, c, m, overlap,
+                                  gamma, eps, rope_dims, rope_base, out, out_scale, out_dt, E_cap, a);
+  if (rc != V4A_OK) return rc;
   return hip_status(v4a::launch_compress(a, (hipStream_t)stream), "v4a_compress");
 }
 
@@ -306,6 +324,99 @@ int v4a_hca_attn(const void* q, const void* kv_comp, const void* kv_local, int64
   REQUIRE(need == 0 || (ws && aligned(ws, 256)), V4A_EINVAL, "workspace must be 256-byte aligned");
   return hip_status(v4a::launch_attention(a, ws, g_policy.load(), (hipStream_t)stream),
                     "v4a_hca_attn");
+}
+
+// ---- decode step: the whole CSA decode of one token per sequence in one call ----
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static v4a::IndexerPlan step_plan(const v4a_decode_step* d) {
+  return v4a::indexer_plan(d->batch, 1, d->t, d->n_hI, d->cI, d->m, d->k, d->index_dt,
+                           g_policy.load());
+}
+
+static v4a::AttnArgs step_attn(const v4a_decode_step* d) {
+  return attn_args(d->q, d->kv_comp, d->kv_ring, d->kv_ring, d->kv_new, d->topk_idx, d->topk_cnt,
+                   d->sink, d->q_gamma, d->kv_gamma, d->eps, d->rope_dims, d->rope_base, d->scale,
+                   d->batch, d->t, 1, d->n_h, d->c, d->k, d->w, 0, d->E_cap, 0, 0, d->out,
+                   d->attn_dt, v4a::kModeDecode,
+                   decode_splits(d->batch, d->n_h, d->num_splits, d->k, d->w));
+}
+
+int v4a_decode_step_layout(size_t* off, int n, size_t* size) {
+#define V4A_OFF(f) offsetof(v4a_decode_step, f)
+  const size_t o[] = {
+      V4A_OFF(t), V4A_OFF(E_cap), V4A_OFF(n_buf), V4A_OFF(tok_base), V4A_OFF(batch), V4A_OFF(n_h),
+      V4A_OFF(c), V4A_OFF(n_hI), V4A_OFF(cI), V4A_OFF(m), V4A_OFF(k), V4A_OFF(w),
+      V4A_OFF(num_splits), V4A_OFF(rope_dims), V4A_OFF(rope_dims_I), V4A_OFF(rope_base),
+      V4A_OFF(eps), V4A_OFF(scale), V4A_OFF(tail_dt), V4A_OFF(index_dt), V4A_OFF(attn_dt),
+      V4A_OFF(C), V4A_OFF(Z), V4A_OFF(B), V4A_OFF(gamma), V4A_OFF(CI), V4A_OFF(ZI), V4A_OFF(BI),
+      V4A_OFF(gammaI), V4A_OFF(kv_comp), V4A_OFF(KI), V4A_OFF(KI_scale), V4A_OFF(qI),
+      V4A_OFF(qI_scale), V4A_OFF(wI), V4A_OFF(q), V4A_OFF(sink), V4A_OFF(q_gamma),
+      V4A_OFF(kv_gamma), V4A_OFF(kv_ring), V4A_OFF(kv_new), V4A_OFF(topk_idx), V4A_OFF(topk_cnt),
+      V4A_OFF(topk_score), V4A_OFF(out)};
+#undef V4A_OFF
+  const int nf = (int)(sizeof(o) / sizeof(o[0]));
+  for (int i = 0; i < nf && i < n && off; ++i) off[i] = o[i];
+  if (size) *size = sizeof(v4a_decode_step);
+  return nf;
+}
+
+size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d) {
+  if (!d || d->batch < 1 || d->m < 1 || d->k < 1 || d->t < 0 || d->n_h < 1 || d->c < 2 ||
+      d->num_splits < 0 || d->num_splits > 64)
+    return 0;
+  return align256(step_plan(d).total) + v4a::attn_workspace(step_attn(d), g_policy.load());
+}
+
+int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(d, V4A_EINVAL, "null step description");
+  REQUIRE(d->t >= 0 && d->t < INT32_MAX, V4A_EINVAL, "t out of range");
+  REQUIRE(d->num_splits >= 0 && d->num_splits <= 64, V4A_EINVAL, "num_splits must be in [0, 64]");
+  REQUIRE(d->attn_dt == V4A_F32 || d->attn_dt == V4A_BF16, V4A_ENOTSUP,
+          "attention dtype must be F32 or BF16");
+  // the three stages' own checks, exactly as the separate calls make them
+  v4a::CompressArgs cm, ci;
+  int rc = compress_prepare(d->C, d->Z, d->tail_dt, d->B, d->batch, d->n_buf, d->tok_base, d->t, 1,
+                            d->c, d->m, 1, d->gamma, d->eps, d->rope_dims, d->rope_base,
+                            d->kv_comp, nullptr, d->attn_dt, d->E_cap, cm);
+  if (rc != V4A_OK) return rc;
+  rc = compress_prepare(d->CI, d->ZI, d->tail_dt, d->BI, d->batch, d->n_buf, d->tok_base, d->t, 1,
+                        d->cI, d->m, 1, d->gammaI, d->eps, d->rope_dims_I, d->rope_base, d->KI,
+                        d->KI_scale, d->index_dt, d->E_cap, ci);
+  if (rc != V4A_OK) return rc;
+  rc = indexer_check(d->qI, d->qI_scale, d->KI, d->KI_scale, d->index_dt, d->wI, d->batch, 1, d->t,
+                     d->n_hI, d->cI, d->m, d->k, d->E_cap, d->topk_idx, d->topk_cnt);
+  if (rc != V4A_OK) return rc;
+  rc = check_attn_common(d->q, d->kv_comp, d->out, d->n_h, d->c, d->rope_dims, d->w, d->attn_dt,
+                         d->batch, d->eps);
+  if (rc != V4A_OK) return rc;
+  REQUIRE(d->kv_ring, V4A_EINVAL, "null kv_ring");
+  const v4a::IndexerPlan p = step_plan(d);
+  v4a::AttnArgs aa = step_attn(d);
+  const int policy = g_policy.load();
+  const size_t ws_i = align256(p.total), need = ws_i + v4a::attn_workspace(aa, policy);
+  REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
+  REQUIRE(ws && aligned(ws, 256), V4A_EINVAL, "workspace must be 256-byte aligned");
+  v4a::IndexerArgs ia{};
+  ia.qI = d->qI; ia.qI_scale = d->qI_scale; ia.KI = d->KI; ia.KI_scale = d->KI_scale; ia.wI = d->wI;
+  ia.topk_idx = d->topk_idx; ia.topk_cnt = d->topk_cnt; ia.topk_score = d->topk_score;
+  ia.t0 = d->t; ia.E_cap = d->E_cap; ia.batch = d->batch; ia.T = 1; ia.n_hI = d->n_hI;
+  ia.cI = d->cI; ia.m = d->m; ia.k = d->k; ia.dt = d->index_dt;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws_a = reinterpret_cast<char*>(ws) + ws_i;
+  hipError_t e;
+  if (v4a::decode_front_supported(cm, ci, aa, policy)) {
+    // tail compressions, window prep and ring insert in one launch
+    e = v4a::launch_decode_front(cm, ci, aa, ws_a, s);
+    aa.prep_done = 1;
+  } else {
+    e = v4a::launch_compress(cm, s);
+    if (e == hipSuccess) e = v4a::launch_compress(ci, s);
+  }
+  if (e == hipSuccess) e = v4a::launch_indexer_topk(ia, p, ws, s);
+  if (e == hipSuccess) e = v4a::launch_attention(aa, ws_a, policy, s);
+  return hip_status(e, "v4a_csa_decode_step");
 }
 
 }  // extern "C"

@@ -35,8 +35,10 @@
 //     states (unnormalised O, reference max, sum) for the merge kernel.
 // Local window rows are normalised and rotated once by a pre-pass into a bf16
 // workspace, so every candidate is a plain row gather.
+#include "compress_rows.h"
 #include "device_common.h"
 #include "internal.h"
+#include "window_prep.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -674,76 +676,28 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 //   prefill/HCA: ws row r <- local position lrow_base + r
 //   decode:      ws row r <- position lo + r read from the ring (token t from kv_new),
 //                and kv_new is written into ring slot t % w
-struct LocalPrepArgs {
-  const uint16_t* src;   // prefill: kv_local [batch][n_loc][512]; decode: ring [batch][w][512]
-  uint16_t* ring;        // decode: ring to insert kv_new into (may alias src)
-  const uint16_t* kv_new;
-  const float* gamma;
-  uint16_t* ws;          // [batch][n_lrows][512]
-  int* redo;             // count of the recomputation list, cleared here
-  int64_t lrow_base, loc_base, n_loc, n_lrows, t;
-  int w, rope_dims, decode;
-  float eps, rope_base;
-  RopeTab rope;
-};
-
 __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.redo[0] = 0;
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  window_prep_block(a, blockIdx.x, blockIdx.y, threadIdx.x);
+}
+
+// Decode front: the independent first steps of a decode step in one launch, so that
+// they overlap instead of paying a launch and a memory round trip each.  Row b of the
+// grid: block v < n_comp runs compressor group v of the main instance in wave 0 and of
+// the index instance in wave 1 (first, as they have the longest dependency chain);
+// blocks n_comp .. prepare the window rows and insert the new token into the ring.
+// GM, GI: lanes per entry (c / 8) of the main and index instance (bf16 tails).
+template <int GM, int GI>
+__global__ __launch_bounds__(256) void decode_front_kernel(CompressArgs cm, CompressArgs ci,
+                                                           LocalPrepArgs lp, int n_comp) {
   const int b = blockIdx.y;
-  if (r >= a.n_lrows) return;
-  const int64_t pos = a.lrow_base + r;
-  const uint16_t* src;
-  if (a.decode) {
-    if (pos > a.t) return;
-    src = (pos == a.t && a.kv_new) ? a.kv_new + (int64_t)b * kC
-                                   : a.src + ((int64_t)b * a.w + pos % a.w) * kC;
-  } else {
-    src = a.src + ((int64_t)b * a.n_loc + (pos - a.loc_base)) * kC;
+  if ((int)blockIdx.x >= n_comp) {
+    window_prep_block(lp, (int)blockIdx.x - n_comp, b, threadIdx.x);
+    return;
   }
-  const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * lane);
-  // RMSNorm weights are loaded with the row, not after the reduction
-  float4 g0 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), g1 = g0;
-  if (a.gamma) {
-    g0 = *reinterpret_cast<const float4*>(a.gamma + 8 * lane);
-    g1 = *reinterpret_cast<const float4*>(a.gamma + 8 * lane + 4);
-  }
-  if (a.decode && pos == a.t && a.kv_new)
-    *reinterpret_cast<uint4*>(a.ring + ((int64_t)b * a.w + a.t % a.w) * kC + 8 * lane) = v;
-  const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-  float x[8];
-  float ss = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(wds[e] << 16);
-    x[2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-  if (a.gamma) {
-    const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)kC + a.eps);
-    const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * gw[e];
-  }
-  const int r0 = kC - a.rope_dims;
-  uint32_t o[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const int d = 8 * lane + e;
-    float y0 = x[e], y1 = x[e + 1];
-    if (a.rope_dims > 0 && d >= r0) {
-      float cs, sn;
-      rope_cs((double)pos, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
-      const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
-      y0 = z0;
-      y1 = z1;
-    }
-    o[e / 2] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
-  }
-  *reinterpret_cast<uint4*>(a.ws + ((int64_t)b * a.n_lrows + r) * kC + 8 * lane) =
-      make_uint4(o[0], o[1], o[2], o[3]);
+  const int64_t vb = blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv == 0 && vb * (64 / GM) < cm.n_entries) compress_rows_body<uint16_t, GM>(cm, vb, b, lane);
+  if (wv == 1 && vb * (64 / GI) < ci.n_entries) compress_rows_body<uint16_t, GI>(ci, vb, b, lane);
 }
 
 }  // namespace
@@ -787,20 +741,31 @@ hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStrea
 hipError_t launch_attention_redo(const AttnArgs& a, float* part, const int* redo, int split_len,
                                  hipStream_t s);
 
-hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
+// workspace pieces: [window rows bf16][decode partials f32][recomputation list int32]
+struct MfmaWs {
+  uint16_t* lws;
+  float* part;
+  int* redo;
+};
+static MfmaWs mfma_ws(const AttnArgs& a, void* ws) {
   const int64_t nl_rows = local_rows(a);
-  uint16_t* lws = reinterpret_cast<uint16_t*>(ws);
+  MfmaWs w;
+  w.lws = reinterpret_cast<uint16_t*>(ws);
   const size_t loc_bytes = ((size_t)a.batch * nl_rows * kC * 2 + 255) / 256 * 256;
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + loc_bytes);
+  w.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + loc_bytes);
   size_t part_bytes = 0;
   if (a.mode == kModeDecode && a.num_splits > 1)
     part_bytes = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
-  int* redo = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + loc_bytes + part_bytes);
+  w.redo = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + loc_bytes + part_bytes);
+  return w;
+}
+
+static LocalPrepArgs prep_args(const AttnArgs& a, const MfmaWs& w) {
   LocalPrepArgs lp{};
-  lp.redo = redo;
+  lp.redo = w.redo;
   lp.gamma = a.kv_gamma;
-  lp.ws = lws;
-  lp.n_lrows = nl_rows;
+  lp.ws = w.lws;
+  lp.n_lrows = local_rows(a);
   lp.rope_dims = a.rope_dims;
   lp.eps = a.eps;
   lp.rope_base = a.rope_base;
@@ -821,10 +786,60 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
     lp.t = a.t0 + a.T - 1;
     lp.decode = 0;
   }
-  hipLaunchKernelGGL(local_prep_kernel, dim3((unsigned)((nl_rows + 3) / 4), (unsigned)a.batch),
-                     dim3(256), 0, s, lp);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return lp;
+}
+
+static bool tail_rows_ok(const CompressArgs& a) {
+  if (a.n_entries <= 0) return true;
+  const int npos = a.overlap ? 2 * a.m : a.m;
+  return a.in_dt == kBF16 && npos <= 8 && (a.c == 128 || a.c == 256 || a.c == 512);
+}
+
+bool decode_front_supported(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
+                            int policy) {
+  return a.mode == kModeDecode && policy == 0 && attn_mfma_supported(a) && tail_rows_ok(cm) &&
+         tail_rows_ok(ci) && cm.batch == a.batch && ci.batch == a.batch;
+}
+
+hipError_t launch_decode_front(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
+                               void* attn_ws, hipStream_t s) {
+  const LocalPrepArgs lp = prep_args(a, mfma_ws(a, attn_ws));
+  const int n_prep = (int)((lp.n_lrows + 3) / 4);
+  auto groups = [](const CompressArgs& x) -> int64_t {
+    return x.n_entries > 0 ? ((int64_t)x.n_entries + 64 / (x.c / 8) - 1) / (64 / (x.c / 8)) : 0;
+  };
+  const int64_t gm = groups(cm), gi = groups(ci);
+  const int n_comp = (int)(gm > gi ? gm : gi);
+  const int64_t nb = n_prep + n_comp;
+  const dim3 grid((unsigned)nb, (unsigned)a.batch);
+  // instance widths c / 8 (16, 32 or 64 lanes per entry; checked by tail_rows_ok)
+  const int GM = cm.n_entries > 0 ? cm.c / 8 : 64, GI = ci.n_entries > 0 ? ci.c / 8 : 16;
+#define V4A_FRONT(gm, gi)                                                                     \
+  if (GM == gm && GI == gi) {                                                                  \
+    hipLaunchKernelGGL((decode_front_kernel<gm, gi>), grid, dim3(256), 0, s, cm, ci, lp, n_comp); \
+    return hipGetLastError();                                                                  \
+  }
+  V4A_FRONT(64, 16) V4A_FRONT(64, 32) V4A_FRONT(64, 64)
+  V4A_FRONT(32, 16) V4A_FRONT(32, 32) V4A_FRONT(32, 64)
+  V4A_FRONT(16, 16) V4A_FRONT(16, 32) V4A_FRONT(16, 64)
+#undef V4A_FRONT
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
+  const int64_t nl_rows = local_rows(a);
+  const MfmaWs wsp = mfma_ws(a, ws);
+  uint16_t* lws = wsp.lws;
+  float* part = wsp.part;
+  int* redo = wsp.redo;
+  const LocalPrepArgs lp = prep_args(a, wsp);
+  hipError_t err = hipSuccess;
+  if (!a.prep_done) {
+    hipLaunchKernelGGL(local_prep_kernel, dim3((unsigned)((nl_rows + 3) / 4), (unsigned)a.batch),
+                       dim3(256), 0, s, lp);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
 
   MqaArgs m{};
   m.q = reinterpret_cast<const uint16_t*>(a.q);

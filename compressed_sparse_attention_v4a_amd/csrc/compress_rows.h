@@ -1,0 +1,205 @@
+// Register-resident compressor body for entries pooling at most 8 positions (CSA tails
+// and prefill, m <= 4 with overlap), shared by the compressor kernel and the fused decode
+// front kernel.  What it computes: "CSA And HCA: Definition, State, And Cost Model",
+// sections 2.1 (overlapping softmax pooling) and 5.2 (RMSNorm and partial RoPE of an
+// emitted entry).
+#pragma once
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace v4a {
+namespace {
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  using raw = float4;
+  __device__ static void load(const void* base, int64_t off, float* dst) {
+    float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  }
+};
+template <>
+struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const void* base, int64_t off, float* dst) {
+    uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dst[2 * i] = __uint_as_float(w[i] << 16);
+      dst[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+// Entries pooling at most 8 positions (CSA, m <= 4 with overlap): one group of G = c / VEC
+// lanes per entry holds every pooled position in registers, so the softmax needs no merge
+// across lanes and the RMSNorm / quantisation maxima are shuffle reductions within the
+// group.  Each wave covers 64 / G entries; no LDS, no barriers.
+// RMSNorm weights of a call without RMSNorm (read, never applied; VEC <= 8)
+__device__ __attribute__((aligned(16))) const float kOnes[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+
+// One wave: entries 64 / G * vblock .. of sequence b; lane = lane of the wave.
+template <typename Tin, int G>
+__device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_t vblock, int b, int lane) {
+  constexpr int VEC = Vec<Tin>::N;
+  constexpr int kMaxPos = 8;
+  const int c = a.c, m = a.m;
+  const int g = lane % G, ch0 = g * VEC;
+  const int64_t slot = vblock * (64 / G) + lane / G;
+  const bool valid = slot < a.n_entries;
+  const int64_t i = a.i_begin + (valid ? slot : 0);
+  const int width = a.overlap ? 2 * c : c;
+  const int npos = (a.overlap && i > 0) ? 2 * m : m;
+  const Tin* Cb = reinterpret_cast<const Tin*>(a.C) + (int64_t)b * a.n_buf * width;
+  const Tin* Zb = reinterpret_cast<const Tin*>(a.Z) + (int64_t)b * a.n_buf * width;
+
+  // RMSNorm weights go out with the other loads, not after the reduction
+  float gw[VEC];
+  {
+    const float* gp = a.gamma ? a.gamma + ch0 : kOnes;
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(gp + v);
+      gw[v] = g4.x; gw[v + 1] = g4.y; gw[v + 2] = g4.z; gw[v + 3] = g4.w;
+    }
+  }
+  // every load first, with no branch between them (a branch per position would make
+  // each position's loads wait for the previous ones): logits and values of the pooled
+  // positions (u < m: stream a of block i, else stream b of block i - 1) and the
+  // positional bias rows.  Positions past npos read a pooled row of the same entry
+  // (always inside the buffer) and get logit -inf.
+  float lg[kMaxPos][VEC], cv[kMaxPos][VEC];
+#pragma unroll
+  for (int u = 0; u < kMaxPos; ++u) {
+    const bool use = valid && u < npos;
+    const int uu = u < npos ? u : 0;
+    const bool sa = uu < m;
+    const int64_t pos = sa ? (int64_t)m * i + uu : (int64_t)m * (i - 1) + (uu - m);
+    const int64_t off = (pos - a.tok_base) * width + (sa ? 0 : c) + ch0;
+    Vec<Tin>::load(Zb, off, lg[u]);
+    Vec<Tin>::load(Cb, off, cv[u]);
+    const float* brow = a.B + (int64_t)uu * c + ch0;  // B^a rows 0..m-1, B^b rows m..2m-1
+    float bv[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; v += 4) {
+      const float4 b4 = *reinterpret_cast<const float4*>(brow + v);
+      bv[v] = b4.x; bv[v + 1] = b4.y; bv[v + 2] = b4.z; bv[v + 3] = b4.w;
+    }
+    // arithmetic masking (the loaded values are finite), so no load sits under a branch
+    const float lmask = use ? 0.0f : -INFINITY, cmask = use ? 1.0f : 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      lg[u][v] = fmaf(lg[u][v] + bv[v], kLog2e, lmask);
+      cv[u][v] *= cmask;
+    }
+  }
+  float x[VEC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float mx = lg[0][v];
+#pragma unroll
+    for (int u = 1; u < kMaxPos; ++u) mx = fmaxf(mx, lg[u][v]);
+    if (mx == -INFINITY) mx = 0.0f;  // lanes of an entry past the end
+    float sm = 0.0f, ac = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMaxPos; ++u) {
+      const float e = __builtin_amdgcn_exp2f(lg[u][v] - mx);
+      sm += e;
+      ac = fmaf(e, cv[u][v], ac);
+    }
+    x[v] = valid ? ac / sm : 0.0f;
+    ss = fmaf(x[v], x[v], ss);
+  }
+  if (a.gamma) {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = 1.0f / sqrtf(ss / (float)c + a.eps);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) x[v] = x[v] * inv * gw[v];
+  }
+  if (a.rope_dims > 0 && ch0 + VEC > c - a.rope_dims) {
+    const int r0 = c - a.rope_dims;
+    const double pos = (double)((int64_t)m * i);
+#pragma unroll
+    for (int v = 0; v < VEC; v += 2) {
+      const int ch = ch0 + v;
+      if (ch >= r0) {
+        float cs, sn;
+        // float32 entries keep the accurate sine; rounded entries take the hardware one
+        if (a.out_dt == kF32) rope_cs(pos, a.rope.inv_freq[(ch - r0) >> 1], cs, sn);
+        else rope_cs_fast(pos, a.rope.inv_freq[(ch - r0) >> 1], cs, sn);
+        const float x0 = x[v], x1 = x[v + 1];
+        x[v] = x0 * cs - x1 * sn;
+        x[v + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+
+  const int64_t orow = (int64_t)b * a.E_cap + i;
+  if (a.out_dt == kF32) {
+    if (valid) {
+      float* o = reinterpret_cast<float*>(a.out) + orow * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 4) *reinterpret_cast<float4*>(o + v) = make_float4(x[v], x[v + 1], x[v + 2], x[v + 3]);
+    }
+  } else if (a.out_dt == kBF16) {
+    if (valid) {
+      uint32_t w[VEC / 2];
+#pragma unroll
+      for (int v = 0; v < VEC; v += 2) w[v / 2] = (uint32_t)f32_to_bf16(x[v]) | ((uint32_t)f32_to_bf16(x[v + 1]) << 16);
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + orow * c + ch0;
+      if (VEC == 8) *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2 % (VEC / 2)], w[3 % (VEC / 2)]);
+      else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1 % (VEC / 2)]);
+    }
+  } else if (a.out_dt == kFP8) {
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) am = fmaxf(am, fabsf(x[v]));
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    float scale = am / 448.0f;
+    if (!(scale > 0.0f)) scale = 1.0f;
+    if (valid) {
+      uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow * c + ch0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const float y = x[v] / scale;
+        o[v] = (uint8_t)(f32_to_e4m3_abs(fabsf(y)) | (y < 0.0f ? 0x80u : 0u));
+      }
+      if (g == 0) reinterpret_cast<float*>(a.out_scale)[orow] = scale;
+    }
+  } else {  // MXFP4: blocks of 32 channels = 32 / VEC consecutive lanes of the group
+    constexpr int lpb = 32 / VEC;
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) am = fmaxf(am, fabsf(x[v]));
+#pragma unroll
+    for (int o = 1; o < lpb; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if (valid) {
+      int sexp = 0;
+      if (am > 0.0f) sexp = (int)((__float_as_uint(am) >> 23) & 255u) - 127 - 2;
+      if (sexp < -127) sexp = -127;
+      if (sexp > 127) sexp = 127;
+      const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);  // 2^-sexp (|sexp| <= 127)
+      uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow * (c / 2) + ch0 / 2;
+#pragma unroll
+      for (int v = 0; v < VEC; v += 2) {
+        const float y0 = x[v] * inv, y1 = x[v + 1] * inv;
+        const uint32_t n0 = f32_to_e2m1_abs(fabsf(y0)) | (y0 < 0.0f ? 8u : 0u);
+        const uint32_t n1 = f32_to_e2m1_abs(fabsf(y1)) | (y1 < 0.0f ? 8u : 0u);
+        o[v / 2] = (uint8_t)(n0 | (n1 << 4));
+      }
+      if ((g % lpb) == 0)
+        reinterpret_cast<uint8_t*>(a.out_scale)[orow * (c / 32) + ch0 / 32] = (uint8_t)(sexp + 127);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace v4a

@@ -31,6 +31,20 @@ struct CompressArgs {
   RopeTab rope;
 };
 
+// Window-row preparation (attention prep kernel, fused decode front).
+struct LocalPrepArgs {
+  const uint16_t* src;   // prefill: kv_local [batch][n_loc][512]; decode: ring [batch][w][512]
+  uint16_t* ring;        // decode: ring to insert kv_new into (may alias src)
+  const uint16_t* kv_new;
+  const float* gamma;
+  uint16_t* ws;          // [batch][n_lrows][512]
+  int* redo;             // count of the recomputation list, cleared here
+  int64_t lrow_base, loc_base, n_loc, n_lrows, t;
+  int w, rope_dims, decode;
+  float eps, rope_base;
+  RopeTab rope;
+};
+
 struct IndexerArgs {
   const void* qI;
   const void* qI_scale;
@@ -69,6 +83,7 @@ struct AttnArgs {
   void* out;
   int64_t loc_base, n_loc, t0, E_cap;
   int batch, T, n_h, c, k, w, m_prime, rope_dims, dt, mode, num_splits;
+  int prep_done;  // window rows already prepared (fused decode front kernel)
   float eps, rope_base, scale;
   RopeTab rope;
 };
@@ -87,5 +102,13 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
 
 size_t attn_workspace(const AttnArgs& a, int policy);
 hipError_t launch_attention(const AttnArgs& a, void* ws, int policy, hipStream_t s);
+
+// Fused decode front (one launch: main and index tail compression, window-row prep and
+// ring insert).  Supported when the attention takes the matrix-core path and both
+// compressor instances take the register-resident path with bf16 inputs.
+bool decode_front_supported(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
+                            int policy);
+hipError_t launch_decode_front(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
+                               void* attn_ws, hipStream_t s);
 
 }  // namespace v4a

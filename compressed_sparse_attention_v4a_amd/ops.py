@@ -128,6 +128,38 @@ def sparse_mqa_decode(q, kv_comp, kv_ring, kv_new, idx, cnt, *, t, w, dt, sink=N
     return out
 
 
+def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI, KI_scale, qI,
+                    qI_scale, wI, q, kv_ring, kv_new, index_dt, gamma=None, gammaI=None, sink=None,
+                    q_gamma=None, kv_gamma=None, rope_dims=0, rope_dims_I=0, rope_base=10000.0,
+                    eps=1e-6, scale=0.0, num_splits=0, out=None, with_scores=True, stream=None,
+                    ws=None):
+    """One CSA decode step (tail compression of both instances, index top-k, ring insert and
+    attention) through v4a_csa_decode_step.  C, Z: [batch][n_buf][2c] bf16; CI, ZI likewise
+    with cI; qI [batch][n_hI][cI or cI/2]; q [batch][n_h][c].  Caches are updated in place.
+    Returns (out, idx, cnt, score)."""
+    batch, n_h, c = q.shape
+    n_hI = qI.shape[1]
+    cI = CI.shape[2] // 2
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    idx = torch.empty(batch, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(batch, dtype=torch.int32, device=dev)
+    sc = torch.empty(batch, k, dtype=torch.float32, device=dev) if with_scores else None
+    step = B.decode_step(
+        t=t, E_cap=kv_comp.shape[1], n_buf=C.shape[1], tok_base=tail_base, batch=batch, n_h=n_h,
+        c=c, n_hI=n_hI, cI=cI, m=m, k=k, w=w, num_splits=num_splits, rope_dims=rope_dims,
+        rope_dims_I=rope_dims_I, rope_base=rope_base, eps=eps, scale=scale, tail_dt=B.BF16,
+        index_dt=_NP_DT[index_dt], attn_dt=B.BF16, C=C, Z=Z, B=B_, gamma=gamma, CI=CI, ZI=ZI,
+        BI=BI, gammaI=gammaI, kv_comp=kv_comp, KI=KI, KI_scale=KI_scale, qI=qI,
+        qI_scale=qI_scale, wI=wI, q=q, sink=sink, q_gamma=q_gamma, kv_gamma=kv_gamma,
+        kv_ring=kv_ring, kv_new=kv_new, topk_idx=idx, topk_cnt=cnt, topk_score=sc, out=out)
+    nbytes = B.v4a_csa_decode_step_workspace(step)
+    if ws is None or ws.numel() < nbytes:
+        ws = workspace(nbytes, dev)
+    B.v4a_csa_decode_step(step, ws, nbytes, stream)
+    return out, idx, cnt, sc
+
+
 def hca_attn(q, kv_comp, kv_local, *, t0, m_prime, w, dt, loc_base=0, sink=None, q_gamma=None,
              kv_gamma=None, eps=1e-6, rope_dims=0, rope_base=10000.0, scale=0.0, out=None,
              stream=None):

@@ -242,6 +242,72 @@ V4A_API int v4a_hca_attn(const void* q, const void* kv_comp, const void* kv_loca
                  int T, int n_h, int c, int m_prime, int w, int64_t E_cap, void* out, v4a_dtype dt,
                  void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * v4a_csa_decode_step -- one CSA decode step for every sequence of the batch
+ * (new token at position t), as one call: [Def] section 7, steps 1, 4 and 5.
+ * The result is that of the sequence
+ *   v4a_compress(C, Z, tail_dt, B, batch, n_buf, tok_base, t, 1, c, m, 1, gamma,
+ *                eps, rope_dims, rope_base, kv_comp, NULL, attn_dt, E_cap)
+ *   v4a_compress(CI, ZI, tail_dt, BI, batch, n_buf, tok_base, t, 1, cI, m, 1,
+ *                gammaI, eps, rope_dims_I, rope_base, KI, KI_scale, index_dt, E_cap)
+ *   v4a_indexer_topk(qI, qI_scale, KI, KI_scale, index_dt, wI, batch, 1, t, n_hI,
+ *                    cI, m, k, E_cap, topk_idx, topk_cnt, topk_score)
+ *   v4a_sparse_mqa_decode(q, kv_comp, kv_ring, kv_new, t, topk_idx, topk_cnt, sink,
+ *                         q_gamma, kv_gamma, eps, rope_dims, rope_base, scale,
+ *                         batch, n_h, c, k, w, E_cap, num_splits, out, attn_dt)
+ * (bit for bit), with the same arguments, layouts and errors; workspaces are
+ * replaced by one.  Where the shapes allow (bf16 tails and attention rows of 512
+ * channels, heads in groups of 64), the two tail compressions and the window-row
+ * preparation run as one launch.  When (t+1) % m != 0 no entry is emitted and
+ * the compressor inputs are not read.
+ *   d        : host pointer to the description below (read during the call only).
+ *   ws       : device workspace of v4a_csa_decode_step_workspace(d) bytes,
+ *              256-byte aligned.
+ */
+typedef struct v4a_decode_step {
+  int64_t t;                 /* position of the new token (all sequences), 0 <= t < 2^31 - 1 */
+  int64_t E_cap;             /* rows of kv_comp and KI per sequence */
+  int64_t n_buf, tok_base;   /* tail buffers: n_buf rows, row r = position tok_base + r */
+  int batch, n_h, c, n_hI, cI, m, k, w;
+  int num_splits;            /* 0 = automatic */
+  int rope_dims, rope_dims_I;
+  float rope_base, eps, scale;
+  v4a_dtype tail_dt;         /* C, Z, CI, ZI: F32 or BF16 */
+  v4a_dtype index_dt;        /* qI, KI */
+  v4a_dtype attn_dt;         /* q, kv_comp, kv_ring, kv_new, out: F32 or BF16 */
+  const void* C;             /* main compressor: [batch][n_buf][2c] */
+  const void* Z;
+  const float* B;            /* [2m][c] */
+  const float* gamma;        /* [c] or NULL */
+  const void* CI;            /* index compressor: [batch][n_buf][2cI] */
+  const void* ZI;
+  const float* BI;           /* [2m][cI] */
+  const float* gammaI;       /* [cI] or NULL */
+  void* kv_comp;             /* [batch][E_cap][c], entry floor((t+1)/m) - 1 appended */
+  void* KI;                  /* [batch][E_cap][cI] (index_dt layout), appended likewise */
+  void* KI_scale;
+  const void* qI;            /* [batch][n_hI][cI] */
+  const void* qI_scale;
+  const float* wI;           /* [batch][n_hI] */
+  const void* q;             /* [batch][n_h][c] */
+  const float* sink;         /* [n_h] or NULL */
+  const float* q_gamma;      /* [c] or NULL */
+  const float* kv_gamma;     /* [c] or NULL */
+  void* kv_ring;             /* [batch][w][c], token j in slot j % w */
+  const void* kv_new;        /* [batch][c] or NULL */
+  int32_t* topk_idx;         /* [batch][k] */
+  int32_t* topk_cnt;         /* [batch] */
+  float* topk_score;         /* [batch][k] or NULL */
+  void* out;                 /* [batch][n_h][c] */
+} v4a_decode_step;
+
+/* Byte offsets of the fields of v4a_decode_step in declaration order, for bindings
+ * that mirror the struct: writes min(n, number of fields) offsets to off and
+ * returns the number of fields; sizeof(v4a_decode_step) goes to *size if non-NULL. */
+V4A_API int v4a_decode_step_layout(size_t* off, int n, size_t* size);
+V4A_API size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d);
+V4A_API int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (v4a_\w+)", out))
@@ -149,3 +149,54 @@ def test_attention_validation(lib):
     assert hca(E_cap=1) == EINVAL
     assert hca(m_prime=0) == EINVAL
     assert hca(kv_local=None) == EINVAL
+
+
+def test_decode_step_layout_and_validation(lib):
+    """The binding's mirror of v4a_decode_step matches the library's offsets (checked when
+    the library loads), and the one-call decode step validates like the separate calls."""
+    n = len(B.DecodeStep._fields_)
+    off = (ct.c_size_t * n)()
+    size = ct.c_size_t()
+    assert lib.v4a_decode_step_layout(ct.cast(off, ct.c_void_p), n,
+                                      ct.cast(ct.byref(size), ct.c_void_p)) == n
+    assert list(off) == [getattr(B.DecodeStep, f).offset for f, _ in B.DecodeStep._fields_]
+    assert size.value == ct.sizeof(B.DecodeStep)
+
+    class Fake:  # a non-null, aligned fake device address with the tensor interface
+        def __init__(self, addr=4096):
+            self.addr = addr
+
+        def data_ptr(self):
+            return self.addr
+
+    F = Fake()
+
+    def step(**kw):
+        a = dict(t=131071, E_cap=32768, n_buf=8, tok_base=131064, batch=2, n_h=64, c=512,
+                 n_hI=64, cI=128, m=4, k=512, w=128, num_splits=0, rope_dims=64, rope_dims_I=0,
+                 rope_base=1e4, eps=1e-6, scale=0.0, tail_dt=B.BF16, index_dt=B.FP8_E4M3,
+                 attn_dt=B.BF16, C=F, Z=F, B=F, gamma=F, CI=F, ZI=F, BI=F, gammaI=None,
+                 kv_comp=F, KI=F, KI_scale=F, qI=F, qI_scale=F, wI=F, q=F, sink=None, q_gamma=F,
+                 kv_gamma=F, kv_ring=F, kv_new=F, topk_idx=F, topk_cnt=F, topk_score=None, out=F)
+        a.update(kw)
+        return B.decode_step(**a)
+
+    def run(d, ws_bytes=1 << 34, ws=F):
+        return lib.v4a_csa_decode_step(ct.c_void_p(ct.addressof(d)), ct.c_void_p(ws.data_ptr()),
+                                       ws_bytes, None)
+
+    need = B.v4a_csa_decode_step_workspace(step())
+    # indexer workspace (scores of 2 x 32768 entries) plus the attention workspace
+    assert need >= 2 * 32768 * 4 + 2 * 128 * 512 * 2
+    assert run(step(q=None)) == EINVAL                  # attention inputs
+    assert run(step(kv_ring=None)) == EINVAL
+    assert run(step(CI=None)) == EINVAL                 # index compressor inputs
+    assert run(step(KI_scale=None)) == EINVAL           # FP8 keys need their scales
+    assert run(step(tok_base=131065)) == EINVAL         # tail buffer misses position 131064
+    assert run(step(E_cap=32767)) == EINVAL             # entry 32767 does not fit
+    assert run(step(attn_dt=B.FP8_E4M3)) == ENOTSUP
+    assert run(step(num_splits=65)) == EINVAL
+    assert run(step(t=-1)) == EINVAL
+    assert run(step(), ws_bytes=need - 1) == ENOSPC
+    assert run(step(), ws=Fake(4096 + 64)) == EINVAL    # workspace alignment
+    assert lib.v4a_csa_decode_step(None, ct.c_void_p(4096), 1 << 30, None) == EINVAL

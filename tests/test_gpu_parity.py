@@ -541,6 +541,43 @@ def _check_decode(cfg, d, r, check_seqs, sink=None):
                           rel_rms=REL_RMS_BF16, what=f"seq {b} output")
 
 
+def _run_decode_step(cfg, d, num_splits=0):
+    """The same decode step through the single v4a_csa_decode_step call."""
+    c, cI, m, k, w = (cfg[x] for x in ("c", "cI", "m", "k", "w"))
+    g, gI = up(d["gamma"]), up(d["gammaI"])
+    kv, KI, KIs, ring = up(d["kv_comp"]), up(d["KI"]), up(d["KI_scale"]), up(d["ring"])
+    qg = up(d["q_gamma"]) if "q_gamma" in d else g
+    out, idx, cnt, sc = ops.csa_decode_step(
+        t=d["t"], m=m, k=k, w=w, tail_base=d["tail_base"], C=up(d["C"]), Z=up(d["Z"]),
+        B_=up(d["B"]), CI=up(d["CI"]), ZI=up(d["ZI"]), BI=up(d["BI"]), kv_comp=kv, KI=KI,
+        KI_scale=KIs, qI=up(d["qI"]), qI_scale=up(d["qI_scale"]), wI=up(d["wI"]), q=up(d["q"]),
+        kv_ring=ring, kv_new=up(d["kv_new"]), index_dt=cfg["idt"], gamma=g, gammaI=gI,
+        q_gamma=qg, kv_gamma=g, rope_dims=cfg["rope_dims"], num_splits=num_splits)
+    torch.cuda.synchronize()
+    return dict(kv=kv, KI=KI, KIs=KIs, ring=ring, idx=idx, cnt=cnt, sc=sc, out=out)
+
+
+@pytest.mark.parametrize("name,batch,L", [("csa_decode_flash_128k", 4, 8192),
+                                          ("csa_decode_pro_1m", 2, 16384),
+                                          ("csa_decode_flash_128k", 3, 8190)])
+def test_decode_step_matches_separate_calls(name, batch, L):
+    """v4a_csa_decode_step (one call, fused front launch) equals the four separate calls bit
+    for bit -- caches, ring, selection, scores and output -- and passes the oracle checks.
+    L = 8190 puts the new token mid-block: nothing is emitted."""
+    cfg = synth.configs.workload(name, batch=batch, L=L)
+    cfg["id"] = 11
+    d = synth.configs.gen_csa_decode(cfg)
+    log(f"decode step vs separate calls {name} batch={batch} L={L}")
+    ref = _run_decode(cfg, d)
+    got = _run_decode_step(cfg, d)
+    for key in ("kv", "KI", "KIs", "ring", "idx", "cnt", "sc", "out"):
+        a, b = ref[key].reshape(-1), got[key].reshape(-1)
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), key
+    if (d["t"] + 1) % cfg["m"] == 0:
+        _check_decode(cfg, d, got, list(range(batch)))
+
+
 def test_decode_flash_128k_fp8():
     cfg, d = _decode_case("csa_decode_flash_128k")
     log("decode flash B=32 L=131072 fp8 keys")
