@@ -22,8 +22,9 @@
 //     maximum): probabilities are exp2(s - m_ref) < 2^64, so O is never rescaled;
 //     if a later chunk maximum exceeds the reference by more than that, the
 //     workgroup abandons the item and lists it for the exact general kernel, which
-//     recomputes it in float32 afterwards (never triggered for normalised queries
-//     and rows).  The
+//     recomputes it in float32 afterwards; a decode split instead raises its
+//     reference to that maximum and restarts (neither is triggered for normalised
+//     queries and rows).  The
 //     score accumulator layout of the 32x32 tile is already the A-operand layout
 //     of P V (candidate k-slots permuted identically on both sides), so each
 //     wave packs its P to bf16 and stores it to LDS as ready-made fragments.
@@ -487,10 +488,17 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           if (hl == 0) mx_s[wv][l32] = lmax;
           wait_lgkmcnt<0>();
           block_sync();
-          m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
+          if constexpr (MODE == kModeDecode) {
+            m_ref = fmaxf(m_ref, fmaxf(lmax, mx_s[wv ^ 1][l32]));  // raised by a restart
+          } else {
+            m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
+          }
           if (m_ref == -INFINITY) m_ref = 0.0f;
         } else {
           restart = lmax > m_ref + kLazy;
+          if constexpr (MODE == kModeDecode) {
+            if (hl == 0) mx_s[wv][l32] = lmax;  // a restart's new reference
+          }
         }
         float pr[16];
         float ls = 0.0f;
@@ -513,7 +521,14 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         }
         wait_lgkmcnt<0>();
         block_sync();  // P and flags of every wave visible
-        if (flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3]) return false;
+        if (uni(flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3])) {
+          if constexpr (MODE == kModeDecode) {
+            // the new reference of a restart: this chunk's maximum (the same in both
+            // candidate blocks' waves of a head tile)
+            m_ref = fmaxf(m_ref, fmaxf(lmax, mx_s[wv ^ 1][l32]));
+          }
+          return false;
+        }
 
         // O^T[channel tiles of wave wv][64 heads] += V^T P^T over 4 steps of 16 candidates:
         // the V fragments are the A operand, the P fragments the B operand, so a lane ends
@@ -658,7 +673,21 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     {
       f32x16 O[2][4];
       float l_part;
-      if (run(O, l_part)) {
+      if constexpr (MODE == kModeDecode) {
+        // decode splits restart instead of leaving the item to the exact kernel (which would
+        // cost every decode call a launch): run() has raised the reference; the gather in
+        // flight lands, chunk 0 is gathered again and the loop starts over.  Each restart
+        // raises some head's reference to one of its own chunk maxima, so restarts are
+        // finite.
+        if (__builtin_expect(!run(O, l_part), 0)) {
+          do {
+            wait_vmcnt<0>();
+            block_sync();
+            fill(cur, kvbuf + par * kChunkBytes, 0);
+          } while (!run(O, l_part));
+        }
+        finish(O, l_part);
+      } else if (run(O, l_part)) {
         finish(O, l_part);
       } else {
         // a chunk maximum ran past the reference: list the item for the exact general
@@ -876,8 +905,7 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
     const int64_t items = (int64_t)a.batch * hgroups * m.splits;
     hipLaunchKernelGGL(mqa_mfma_kernel<kModeDecode>, dim3((unsigned)items), dim3(kThreads), 0, s, m);
     err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    err = launch_attention_redo(a, part, redo, m.split_len, s);
+    // decode splits restart in place on a reference overflow: no recomputation launch
     if (err != hipSuccess || m.splits <= 1) return err;
     return launch_attention_merge(a, part, s);
   }
