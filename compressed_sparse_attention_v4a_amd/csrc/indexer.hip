@@ -92,7 +92,7 @@ struct TopkOut {
 __global__ __launch_bounds__(256) void topk_tile_kernel(IndexerArgs a, const float* scores,
                                                         int64_t ld, int tile, int n_tiles, int kc,
                                                         uint32_t* cand_key, int32_t* cand_idx) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[768];
   __shared__ int sh[16];
   const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
   const int64_t t = a.t0 + j;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void topk_tile_kernel(IndexerArgs a, const flo
 __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_tiles, int kc,
                                                           const uint32_t* cand_key,
                                                           const int32_t* cand_idx) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int j = blockIdx.x, b = blockIdx.y;
   const int64_t t = a.t0 + j;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(THREADS) void topk_tile_reg_kernel(IndexerArgs a, c
                                                             int64_t ld, int n_tiles, int kc,
                                                             uint32_t* cand_key, int32_t* cand_idx) {
   constexpr int PER = 16, kRegTile = PER * THREADS;
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
   const int64_t t = a.t0 + j;
@@ -244,7 +244,7 @@ template <int PER>
 __global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int n_tiles, int kc,
                                                               const uint32_t* cand_key,
                                                               const int32_t* cand_idx) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int j = blockIdx.x, b = blockIdx.y;
   const int64_t t = a.t0 + j;
@@ -285,6 +285,189 @@ __global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int
   if (threadIdx.x == 0) a.topk_cnt[q] = n;
 }
 
+// ---- decode top-k by threshold filter (one query row over E >> k entries) ----------
+// The scan also records the maximum order key of every group of Gs = 16 << gshift
+// consecutive entries.  Any K of those maxima are keys of K distinct entries, so the K-th
+// largest group maximum is at most the K-th largest key T of the row; its top 16 bits
+// (2 radix passes), low bits cleared, give a lower bound L <= T.  Every entry with key
+// >= L is a candidate; they include every selected entry.  With n_g = 2k .. 4k groups the
+// candidates number about k (1 + k Gs / 2E) plus the entries sharing T's top 16 bits.
+//   filter: workgroup (slice, query) recomputes L from the group maxima, then compacts its
+//           4096 entries with key >= L, in index order, into the slice's own region.
+//   final : one workgroup per query selects the k largest candidates exactly (ties to
+//           the lower index) and writes them in ascending index order: from registers
+//           up to 4096 candidates, else streaming them from the workspace.
+constexpr int kFiltSlice = 4096;      // entries per filter workgroup (256 threads x 16)
+constexpr int kFiltGroups = 4096;     // group maxima per query at most (256 threads x 16)
+constexpr int kFinalThreads = 256;    // final kernel: few waves keep its barriers and scans short
+constexpr int kFinalPer = 16;         // candidates per thread held in registers (x 256)
+
+__global__ __launch_bounds__(256) void topk_filter_kernel(IndexerArgs a, const float* scores,
+                                                          int64_t ld, const uint32_t* gmax,
+                                                          int64_t ng_ld, int gshift, int n_slices,
+                                                          int* counts, uint32_t* cand_key,
+                                                          int32_t* cand_idx) {
+  __shared__ uint32_t hist[768];
+  __shared__ int sh[40];
+  const int sl = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t q = (int64_t)b * a.T + j;
+  // lower bound L from the group maxima (every workgroup of the row computes the same)
+  const int ng = (int)((E + (16 << gshift) - 1) >> (4 + gshift));
+  // every load first (group maxima and this slice's scores), from clamped addresses with
+  // the absent elements masked afterwards, so that no load waits behind a branch
+  constexpr int GP = kFiltGroups / 256;
+  uint32_t gk[GP];
+  const uint32_t* gq = gmax + q * ng_ld;
+  // group maxima spread evenly over the threads (multiples of 4 for 16-byte loads)
+  const int gper = ((ng + 255) / 256 + 3) & ~3;
+  const int gb = threadIdx.x * gper;
+#pragma unroll
+  for (int v = 0; v < GP; v += 4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(gq + ((v < gper && gb + v < ng_ld) ? gb + v : 0));
+    gk[v] = x.x; gk[v + 1] = x.y; gk[v + 2] = x.z; gk[v + 3] = x.w;
+  }
+  const int64_t s0 = (int64_t)sl * kFiltSlice;
+  const int N = (int)max((int64_t)0, min((int64_t)kFiltSlice, E - s0));
+  const float* srow = scores + q * ld + s0;
+  const int base = threadIdx.x * 16;
+  float f[16];
+#pragma unroll
+  for (int v = 0; v < 16; v += 4) {
+    // the row has ld >= E entries allocated: clamp the slice into it
+    const int64_t o = s0 + base + v + 4 <= ld ? base + v : 0;
+    const float4 x = *reinterpret_cast<const float4*>(srow + o);
+    f[v] = x.x; f[v + 1] = x.y; f[v + 2] = x.z; f[v + 3] = x.w;
+  }
+#pragma unroll
+  for (int v = 0; v < GP; ++v) gk[v] = (v < gper && gb + v < ng) ? gk[v] : 0u;
+  uint32_t key[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) key[v] = base + v < N ? score_key(f[v]) : 0u;
+  // lower bound L from the group maxima (every workgroup of the row computes the same)
+  uint32_t L = 0u;
+  if (ng >= a.k) L = reg_radix_select(gk, ng, a.k, hist, sh, 16, gper).kth;
+  int mine = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mine += (base + v < N && key[v] >= L) ? 1 : 0;
+  int tot;
+  int pos = block_excl_sum(mine, sh, &tot);
+  const int64_t reg = (q * n_slices + sl) * kFiltSlice;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    if (base + v < N && key[v] >= L) {
+      cand_key[reg + pos] = key[v];
+      cand_idx[reg + pos] = (int32_t)(s0 + base + v);
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) counts[q * n_slices + sl] = tot;
+}
+
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a, int n_slices,
+                                                          const int* counts,
+                                                          const uint32_t* cand_key,
+                                                          const int32_t* cand_idx) {
+  __shared__ uint32_t hist[768];
+  __shared__ int sh[40];
+  __shared__ int pre[65];  // candidate offset of every slice (n_slices <= 64)
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int64_t t = a.t0 + j;
+  const int64_t E = (t + 1) / a.m;
+  const int64_t q = (int64_t)b * a.T + j;
+  const int k = a.k;
+  if (threadIdx.x < 64) {
+    // slice counts loaded by one wave at once, then an inclusive scan across its lanes
+    const int lane = threadIdx.x;
+    const int c = lane < n_slices ? counts[q * n_slices + lane] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane < n_slices) pre[lane + 1] = incl;
+    if (lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int total = pre[n_slices];
+  // candidates >= min(k, E) by construction; the minimum keeps the selection in range
+  const int n = (int)min(min((int64_t)k, E), (int64_t)total);
+  int32_t* oidx = a.topk_idx + q * k;
+  float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
+  // candidate p of the row (slice order = index order)
+  auto at = [&](int p) -> int64_t {
+    int lo = 0, hi = n_slices;  // pre[lo] <= p < pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= p) lo = mid; else hi = mid;
+    }
+    return (q * n_slices + lo) * kFiltSlice + (p - pre[lo]);
+  };
+  if (total <= kFinalThreads * kFinalPer) {
+    uint32_t key[kFinalPer];
+    int32_t ix[kFinalPer];
+    // the list spread evenly over the threads (thread t owns [t per, t per + per))
+    const int per = (total + kFinalThreads - 1) / kFinalThreads;
+    const int base = threadIdx.x * per;
+    if (base < total) {
+      // every load first, from clamped positions; absent elements masked afterwards.  The
+      // thread's candidates are consecutive, so after one search the slice only advances.
+      int64_t off[kFinalPer];
+      {
+        int lo = 0, hi = n_slices;  // pre[lo] <= base < pre[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] <= base) lo = mid; else hi = mid;
+        }
+        int sl = lo;
+#pragma unroll
+        for (int v = 0; v < kFinalPer; ++v) {
+          const int p = (v < per && base + v < total) ? base + v : total - 1;
+          while (pre[sl + 1] <= p) ++sl;
+          off[v] = (q * n_slices + sl) * kFiltSlice + (p - pre[sl]);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < kFinalPer; ++v) {
+        key[v] = cand_key[off[v]];
+        ix[v] = cand_idx[off[v]];
+      }
+#pragma unroll
+      for (int v = 0; v < kFinalPer; ++v) {
+        key[v] = (v < per && base + v < total) ? key[v] : 0u;
+        ix[v] = (v < per && base + v < total) ? ix[v] : -1;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < kFinalPer; ++v) {
+        key[v] = 0u;
+        ix[v] = -1;
+      }
+    }
+    Selection sel{0u, kFinalThreads * kFinalPer};  // every candidate (total == n)
+    if (total > n) sel = reg_radix_select(key, total, n, hist, sh, 0, per);
+    reg_select_emit_slot(key, total, sel, sh, [&](int pos, int v, uint32_t kk) {
+      oidx[pos] = ix[v];
+      if (osc) osc[pos] = key_score(kk);
+    }, per);
+  } else {
+    // many candidates (keys concentrated near the bound): select while streaming them
+    auto get = [&](int p) -> uint32_t { return cand_key[at(p)]; };
+    const Selection sel = block_radix_select(get, total, n, hist, sh);
+    block_select_emit(get, total, n, sel, sh, [&](int pos, int p, uint32_t kk) {
+      oidx[pos] = cand_idx[at(p)];
+      if (osc) osc[pos] = key_score(kk);
+    });
+  }
+  for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
+    oidx[p] = -1;
+    if (osc) osc[p] = 0.0f;
+  }
+  if (threadIdx.x == 0) a.topk_cnt[q] = n;
+}
+
 }  // namespace
 
 // MFMA paths (indexer_mfma.hip)
@@ -292,7 +475,7 @@ bool indexer_fused_supported(int64_t Emax, int n_hI, int cI, int dt);
 hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s);
 bool indexer_mfma_supported(int T, int n_hI, int cI, int dt);
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
-                                      hipStream_t s);
+                                      uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s);
 
 IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k, int dt,
                          int policy) {
@@ -315,7 +498,28 @@ IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, 
     return p;
   }
   p.score_bytes = ((size_t)batch * T * p.ld * sizeof(float) + 255) / 256 * 256;
-  p.cand_bytes = p.n_tiles > 1 ? (size_t)batch * T * p.n_tiles * p.kc * 8 : 0;
+  // one decode query over E >= 32 k entries: threshold filter with 2k .. 4k group maxima
+  // (the largest groups that keep at least 2k of them: fewer reductions in the scan)
+  p.filter = false;
+  if (p.mfma_scan && T == 1 && Emax >= 32 * (int64_t)k && Emax <= 64 * (int64_t)kFiltSlice) {
+    int gs = 0;
+    while (gs < 4 && (Emax + (32 << gs) - 1) / (32 << gs) >= 2 * (int64_t)k) ++gs;
+    const int64_t ng = (Emax + (16 << gs) - 1) / (16 << gs);
+    if (ng <= kFiltGroups && ng >= 2 * (int64_t)k) {
+      p.filter = true;
+      p.gshift = gs;
+      p.ng_ld = (ng + 63) / 64 * 64;
+      p.n_slices = (int)((Emax + kFiltSlice - 1) / kFiltSlice);
+    }
+  }
+  if (p.filter) {
+    const size_t rows = (size_t)batch * T;
+    const size_t gm = (rows * p.ng_ld * 4 + 255) / 256 * 256;
+    const size_t cn = (rows * p.n_slices * 4 + 255) / 256 * 256;
+    p.cand_bytes = gm + cn + rows * p.n_slices * kFiltSlice * 8;
+  } else {
+    p.cand_bytes = p.n_tiles > 1 ? (size_t)batch * T * p.n_tiles * p.kc * 8 : 0;
+  }
   p.total = p.score_bytes + p.cand_bytes;
   return p;
 }
@@ -328,9 +532,29 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
   const int64_t Emax = (a.t0 + a.T) / a.m;
   if (p.fused) return launch_indexer_fused(a, Emax, s);
   hipError_t err;
+  if (p.filter) {
+    // workspace after the scores: group maxima, slice counts, candidate keys and indices
+    const size_t rows = (size_t)a.batch * a.T;
+    char* w = reinterpret_cast<char*>(ws) + p.score_bytes;
+    uint32_t* gmax = reinterpret_cast<uint32_t*>(w);
+    w += (rows * p.ng_ld * 4 + 255) / 256 * 256;
+    int* counts = reinterpret_cast<int*>(w);
+    w += (rows * p.n_slices * 4 + 255) / 256 * 256;
+    uint32_t* fkey = reinterpret_cast<uint32_t*>(w);
+    int32_t* fidx = reinterpret_cast<int32_t*>(fkey + rows * p.n_slices * kFiltSlice);
+    err = launch_indexer_scores_mfma(a, scores, p.ld, gmax, p.ng_ld, p.gshift, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)p.n_slices, (unsigned)a.T, (unsigned)a.batch),
+                       dim3(256), 0, s, a, scores, p.ld, gmax, p.ng_ld, p.gshift, p.n_slices, counts,
+                       fkey, fidx);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)a.T, (unsigned)a.batch), dim3(kFinalThreads), 0,
+                       s, a, p.n_slices, counts, fkey, fidx);
+    return hipGetLastError();
+  }
   if (Emax > 0) {
     if (p.mfma_scan) {
-      err = launch_indexer_scores_mfma(a, scores, p.ld, s);
+      err = launch_indexer_scores_mfma(a, scores, p.ld, nullptr, 0, 0, s);
     } else {
       dim3 grid((unsigned)a.T, (unsigned)((Emax + kScoreThreads - 1) / kScoreThreads),
                 (unsigned)a.batch);

@@ -266,8 +266,11 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 constexpr int kScanEntries = 1024;  // per workgroup (4 waves x 16 tiles x 16 entries)
 constexpr int kScanTiles = kScanEntries / 4 / 16;  // 16-entry tiles per wave
 
-template <int DT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(IndexerArgs a, float* scores, int64_t ld) {
+// GS >= 0: also writes gmax, per query the maximum order key (score_key) of every group of
+// 16 << GS consecutive entries, for the threshold filter of the decode top-k.
+template <int DT, int GS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(
+    IndexerArgs a, float* scores, int64_t ld, uint32_t* gmax, int64_t ng_ld) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, jj = lane & 15;
@@ -326,6 +329,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   }
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.KI);
   float* srow = scores + q * ld;
+  const int64_t qg = q * ng_ld;  // this query's group maxima
+  uint32_t gacc = 0u;
   const int64_t kbase = (int64_t)b * a.E_cap;
   // The wave's 16 tiles go in batches: every key load of a batch is issued before its
   // first MFMA, so a wave waits for four (MXFP4: two) memory round trips instead of one per tile (the
@@ -414,6 +419,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
         if (g == 0 && s < E) srow[s] = res[t];
       }
     }
+    if constexpr (GS >= 0) {
+      // group maxima of the order keys: a lane keeps the maximum of its column over the
+      // group's tiles; at the group's last tile the 16 columns of a row (every row holds the
+      // same values) are reduced by row rotations.  Groups never straddle waves.
+#pragma unroll
+      for (int t = 0; t < kB; ++t) {
+        const int tw = b0 + t;
+        const int64_t s = e0 + 16 * tw + jj;
+        gacc = max(gacc, s < E ? score_key(res[t]) : 0u);
+        if (((tw + 1) & ((1 << GS) - 1)) == 0) {
+          uint32_t key = gacc;
+          key = max(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x128, 0xf, 0xf, false));
+          key = max(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x124, 0xf, 0xf, false));
+          key = max(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x122, 0xf, 0xf, false));
+          key = max(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0x121, 0xf, 0xf, false));
+          const int64_t grp = (e0 / 16 + tw) >> GS;  // e0 is a multiple of 256
+          if (lane == 0 && (grp << (4 + GS)) < E) gmax[qg + grp] = key;
+          gacc = 0u;
+        }
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -443,15 +469,29 @@ bool indexer_mfma_supported(int T, int n_hI, int cI, int dt) {
 }
 
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
-                                      hipStream_t s) {
+                                      uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s) {
   const int64_t Emax = (a.t0 + a.T) / a.m;
   dim3 grid((unsigned)((Emax + kScanEntries - 1) / kScanEntries), (unsigned)a.T, (unsigned)a.batch);
-  if (a.dt == kFP8)
-    hipLaunchKernelGGL(indexer_scan_kernel<kFP8>, grid, dim3(256), 0, s, a, scores, ld);
-  else if (a.dt == kMXFP4)
-    hipLaunchKernelGGL(indexer_scan_kernel<kMXFP4>, grid, dim3(256), 0, s, a, scores, ld);
-  else
-    hipLaunchKernelGGL(indexer_scan_kernel<kBF16>, grid, dim3(256), 0, s, a, scores, ld);
+  // GS template: the group size of the optional group maxima (-1: none)
+#define V4A_SCAN(gs)                                                                              \
+  do {                                                                                           \
+    if (a.dt == kFP8)                                                                            \
+      hipLaunchKernelGGL((indexer_scan_kernel<kFP8, gs>), grid, dim3(256), 0, s, a, scores, ld,  \
+                         gmax, ng_ld);                                                           \
+    else if (a.dt == kMXFP4)                                                                     \
+      hipLaunchKernelGGL((indexer_scan_kernel<kMXFP4, gs>), grid, dim3(256), 0, s, a, scores, ld, \
+                         gmax, ng_ld);                                                           \
+    else                                                                                         \
+      hipLaunchKernelGGL((indexer_scan_kernel<kBF16, gs>), grid, dim3(256), 0, s, a, scores, ld, \
+                         gmax, ng_ld);                                                           \
+  } while (0)
+  if (!gmax) V4A_SCAN(-1);
+  else if (gshift == 0) V4A_SCAN(0);
+  else if (gshift == 1) V4A_SCAN(1);
+  else if (gshift == 2) V4A_SCAN(2);
+  else if (gshift == 3) V4A_SCAN(3);
+  else V4A_SCAN(4);
+#undef V4A_SCAN
   return hipGetLastError();
 }
 

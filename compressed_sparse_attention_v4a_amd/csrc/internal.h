@@ -66,6 +66,10 @@ struct IndexerPlan {
   int kc;            // candidates kept per tile = min(k, tile)
   bool fused;        // MFMA fused score + top-k path (no score buffer)
   bool mfma_scan;    // MFMA score scan into the score buffer (else the general kernel)
+  bool filter;       // decode: threshold filter + final selection instead of tiles + merge
+  int gshift;        // filter: group maxima over 16 << gshift entries
+  int n_slices;      // filter: 4096-entry slices per query
+  int64_t ng_ld;     // filter: group maxima per query row (padded)
   size_t score_bytes, cand_bytes, total;
 };
 

@@ -115,16 +115,40 @@ __device__ void block_emit_all(GetKey get, int N, Emit emit) {
 // atomics would serialise on one address).  Emission needs two block-wide prefix counts
 // and keeps ascending index order with ties to the lower index.
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within 16-lane rows, then the
+// row broadcasts of lanes 15 and 31 (no LDS round trip, unlike a shuffle).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Bitwise AND and OR of x over the wave (row rotations, then the four row results),
+// returned in every lane.
+__device__ __forceinline__ void wave_and_or(uint32_t& a, uint32_t& o) {
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x128, 0xf, 0xf, false);  // row_ror:8
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x128, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x124, 0xf, 0xf, false);  // row_ror:4
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x124, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x122, 0xf, 0xf, false);  // row_ror:2
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x122, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x121, 0xf, 0xf, false);  // row_ror:1
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x121, 0xf, 0xf, false);
+  a = (uint32_t)__builtin_amdgcn_readlane((int)a, 0) & (uint32_t)__builtin_amdgcn_readlane((int)a, 16) &
+      (uint32_t)__builtin_amdgcn_readlane((int)a, 32) & (uint32_t)__builtin_amdgcn_readlane((int)a, 48);
+  o = (uint32_t)__builtin_amdgcn_readlane((int)o, 0) | (uint32_t)__builtin_amdgcn_readlane((int)o, 16) |
+      (uint32_t)__builtin_amdgcn_readlane((int)o, 32) | (uint32_t)__builtin_amdgcn_readlane((int)o, 48);
+}
+
 // Exclusive prefix sum of v over the block in thread order; *total gets the sum.
 // sh: LDS int[>= number of waves + 1].
 __device__ __forceinline__ int block_excl_sum(int v, int* sh, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_incl_sum(v);
   __syncthreads();
   if (lane == 63) sh[wid] = incl;
   __syncthreads();
@@ -138,90 +162,147 @@ __device__ __forceinline__ int block_excl_sum(int v, int* sh, int* total) {
   return before + incl - v;
 }
 
+// Per executed pass: run-length atomics into one of three 256-bin histograms, one barrier,
+// then every wave scans that histogram itself (no broadcast through LDS) and clears the
+// histogram of the pass after next, which is thus cleared one barrier after its last
+// readers and one barrier before its next writers: one barrier per pass.  Passes over
+// digits that every key shares (common leading bits, found by one block-wide AND/OR) are
+// skipped.  hist: LDS uint32[768].  per <= PER: elements per thread (thread t owns
+// [t per, t per + per)); a smaller per spreads a short list over more waves.
 template <int PER>
 __device__ Selection reg_radix_select(const uint32_t (&key)[PER], int N, int K, uint32_t* hist,
-                                      int* sh) {
-  const int lane = threadIdx.x & 63;
-  const int base = threadIdx.x * PER;
+                                      int* sh, int last_shift = 0, int per = PER) {
+  (void)sh;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  const int base = threadIdx.x * per;
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (j < per && base + j < N) {
+      kand &= key[j];
+      kor |= key[j];
+    }
+  }
+  wave_and_or(kand, kor);
+  uint32_t* slots = hist + 512;  // third histogram, first cleared by executed pass 0
+  if (lane == 0) {
+    slots[2 * wid] = kand;
+    slots[2 * wid + 1] = kor;
+  }
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  uint32_t all_and = 0xFFFFFFFFu, all_or = 0u;
+  for (int w = 0; w < nw; ++w) {
+    all_and &= slots[2 * w];
+    all_or |= slots[2 * w + 1];
+  }
+  const int common = (all_and ^ all_or) ? __builtin_clz(all_and ^ all_or) : 32;
   uint32_t prefix = 0, pmask = 0;
   int rem = K;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
+  // last_shift > 0 stops early: the result then holds only the key bits above last_shift
+  // (kth = those bits of the K-th largest key, low bits zero; need_eq is not meaningful)
+  int pass = 0;
+  for (int shift = 24; shift >= last_shift; shift -= 8) {
+    if (common >= 32 - shift) {
+      // every key has this digit: the bucket is all of them
+      prefix |= all_and & (255u << shift);
+      pmask |= 255u << shift;
+      continue;
+    }
+    uint32_t* h = hist + 256 * (pass % 3);
     uint32_t cur = 0u, run = 0u;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      if (base + j < N && (key[j] & pmask) == prefix) {
+      if (j < per && base + j < N && (key[j] & pmask) == prefix) {
         const uint32_t d = (key[j] >> shift) & 255u;
         if (run != 0u && d != cur) {
-          atomicAdd(&hist[cur], run);
+          atomicAdd(&h[cur], run);
           run = 0u;
         }
         cur = d;
         ++run;
       }
     }
-    if (run != 0u) atomicAdd(&hist[cur], run);
+    if (run != 0u) atomicAdd(&h[cur], run);
     __syncthreads();
-    if (threadIdx.x < 64) {
-      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                     c3 = hist[4 * lane + 3];
-      const uint32_t mine = c0 + c1 + c2 + c3;
-      uint32_t suf = mine;  // inclusive suffix sum over lanes >= lane
+    // lane l holds bins 255 - 4 l .. 252 - 4 l (descending), so a prefix sum over the
+    // lanes counts the elements in higher bins
+    uint32_t cs[4];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += v;
-      }
-      uint32_t above = suf - mine;  // elements in bins >= 4*lane + 4
-      const uint32_t cs[4] = {c0, c1, c2, c3};
+    for (int j = 0; j < 4; ++j) cs[j] = h[255 - 4 * lane - j];
+    const uint32_t mine = cs[0] + cs[1] + cs[2] + cs[3];
+    uint32_t above = (uint32_t)wave_incl_sum((int)mine) - mine;  // elements in bins > 255 - 4 l
+    int hit_bin = -1;
+    uint32_t hit_above = 0u;
 #pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
-          sh[0] = 4 * lane + j;
-          sh[1] = (int)above;
-        }
-        above += cs[j];
+    for (int j = 0; j < 4; ++j) {
+      if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
+        hit_bin = 255 - 4 * lane - j;
+        hit_above = above;
       }
+      above += cs[j];
     }
-    __syncthreads();
-    const uint32_t d = (uint32_t)sh[0];
-    rem -= sh[1];
+    // exactly one lane holds the bin that contains the rem-th largest remaining key
+    const uint64_t m = __ballot(hit_bin >= 0);
+    const int src = m ? (int)__builtin_ctzll(m) : 0;  // (no lane only for K > N: misuse)
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(hit_bin, src);
+    rem -= __builtin_amdgcn_readlane((int)hit_above, src);
     prefix |= d << shift;
     pmask |= 255u << shift;
-    __syncthreads();
+    uint32_t* h2 = hist + 256 * ((pass + 2) % 3);
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) h2[i] = 0u;
+    ++pass;
   }
+  __syncthreads();  // the last histogram is read before the caller reuses LDS
   return {prefix, rem};
 }
 
-// Emit the selection (keys > kth, then the first need_eq keys == kth): emit(pos, i, key)
-// with pos ascending in element index.  sh: LDS int[>= number of waves + 1].
+// Selected elements before thread t and their placement: the selection is every key > kth
+// plus the first need_eq keys == kth in element order, so the counts of keys > kth and
+// == kth before the thread place every element (for PER <= 16 one block-wide scan of the
+// two counts packed in 16-bit halves).  emit(pos, j, key) with j the register slot;
+// positions ascend in element order.
 template <int PER, class Emit>
-__device__ void reg_select_emit(const uint32_t (&key)[PER], int N, Selection sel, int* sh,
-                                Emit emit) {
-  const int base = threadIdx.x * PER;
+__device__ void reg_select_emit_slot(const uint32_t (&key)[PER], int N, Selection sel, int* sh,
+                                     Emit emit, int per = PER) {
+  const int base = threadIdx.x * per;
   int ngt = 0, neq = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    if (base + j < N) {
+    if (j < per && base + j < N) {
       ngt += key[j] > sel.kth ? 1 : 0;
       neq += key[j] == sel.kth ? 1 : 0;
     }
   }
-  int tot;
-  const int eq_before = block_excl_sum(neq, sh, &tot);
-  const int take_eq = max(0, min(neq, sel.need_eq - eq_before));
-  int pos = block_excl_sum(ngt + take_eq, sh, &tot);
-  int eq_seen = 0;
+  int tot, gt_before, eq_before;
+  if constexpr (PER <= 16) {
+    // at most 16 x 1024 elements: both counts fit 16 bits (one scan)
+    const uint32_t before = (uint32_t)block_excl_sum(ngt | (neq << 16), sh, &tot);
+    gt_before = (int)(before & 0xFFFFu);
+    eq_before = (int)(before >> 16);
+  } else {
+    eq_before = block_excl_sum(neq, sh, &tot);
+    gt_before = block_excl_sum(ngt, sh, &tot);
+  }
+  int pos = gt_before + min(eq_before, sel.need_eq);
+  int eq_seen = eq_before;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    if (base + j < N) {
+    if (j < per && base + j < N) {
       const bool gt = key[j] > sel.kth;
-      const bool eq = key[j] == sel.kth && eq_seen < take_eq;
+      const bool eq = key[j] == sel.kth && eq_seen < sel.need_eq;
       eq_seen += key[j] == sel.kth ? 1 : 0;
-      if (gt || eq) emit(pos++, base + j, key[j]);
+      if (gt || eq) emit(pos++, j, key[j]);
     }
   }
+}
+
+// As reg_select_emit_slot with emit(pos, i, key) given the element index i.
+template <int PER, class Emit>
+__device__ void reg_select_emit(const uint32_t (&key)[PER], int N, Selection sel, int* sh,
+                                Emit emit) {
+  const int base = threadIdx.x * PER;
+  reg_select_emit_slot(key, N, sel, sh, [&](int pos, int j, uint32_t k) { emit(pos, base + j, k); });
 }
 
 }  // namespace v4a

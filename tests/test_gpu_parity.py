@@ -229,6 +229,40 @@ def test_indexer_mfma_paths_bf16(t0, T, k):
                    what=f"row {r}")
 
 
+@pytest.mark.parametrize("case,batch", [("random", 3), ("equal", 1), ("rising", 1)])
+def test_indexer_decode_threshold_filter(case, batch):
+    """One decode query over E = 32768 >= 64 k entries takes the threshold-filter path (group
+    maxima from the scan, candidate compaction, final selection).  "equal": every score
+    ties, so all E entries pass the filter and the final kernel streams them (its path
+    beyond 16384 candidates); the lowest k indices must win.  "rising": the selection is
+    the last k entries, all inside the last few slices."""
+    rng = np.random.default_rng(len(case) * 101 + batch)
+    n_hI, cI, m, k = 64, 128, 4, 256
+    E = 32768
+    t0 = m * E - 1
+    qI = rng.standard_normal((batch, 1, n_hI, cI))
+    if case == "random":
+        KI = rng.standard_normal((batch, E, cI))
+    else:
+        u = np.abs(rng.standard_normal(cI)) + 0.5
+        qI[:] = u  # every head aligned with u: positive dot products
+        ramp = np.ones(E) if case == "equal" else 1.0 + np.arange(E) / E
+        KI = np.broadcast_to(u[None, None, :] * ramp[None, :, None], (batch, E, cI))
+    qI = synth.formats.bf16_bits(qI)
+    KI = synth.formats.bf16_bits(KI)
+    wI = rng.random((batch, 1, n_hI)).astype(np.float32)
+    log(f"indexer decode threshold filter {case} batch={batch} E={E} k={k}")
+    idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
+    torch.cuda.synchronize()
+    Kd = f64(KI, "bf16")
+    for b in range(batch):
+        ref = _oracle_scores(f64(qI[b], "bf16"), Kd[b], wI[b].astype(np.float64), t0, m, E)
+        check_topk(idx[b].cpu().numpy(), cnt[b].cpu().numpy(), ref, t0=t0, m=m, k=k,
+                   gpu_scores=sc[b].cpu().numpy(), what=f"{case} seq {b}")
+        if case == "equal":
+            assert np.array_equal(idx[b, 0].cpu().numpy(), np.arange(k)), "ties go to the lower index"
+
+
 def test_indexer_flash_prefill_sampled(csa8k):
     cfg, d = csa8k
     log("indexer flash n=8192 k=512 (all queries on GPU, sampled rows checked)")
