@@ -16,6 +16,7 @@
 // Workgroups are issued longest-first (late queries see the most entries).
 #include "device_common.h"
 #include "internal.h"
+#include "topk.h"
 
 namespace v4a {
 
@@ -56,6 +57,122 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x4 (&S)[4], const fl
   acc = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);  // rows r and r ^ 2
   const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
   return __uint_as_float(x16[0]) + __uint_as_float(x16[1]);  // rows r and r ^ 1
+}
+
+// Register form of the one-wave top-k for E <= 64 PER: lane l holds the contiguous keys
+// [l per, l per + per), per = ceil(E / 64).  Passes over digits shared by every key
+// (wave AND / OR) are skipped; the others count runs of equal digits before touching the
+// histogram (the wave's own, ordered by the wave's in-order LDS operations) and find the
+// bin with a DPP prefix sum.  Emission places each lane's run with one packed prefix sum
+// of (keys > kth, keys == kth).  Same result as wave_topk.
+template <int PER>
+__device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int32_t* oidx,
+                              float* osc, int32_t* ocnt) {
+  const int lane = threadIdx.x & 63;
+  const int n = E < k ? E : k;
+  if (E <= k) {
+    for (int i = lane; i < E; i += 64) {
+      oidx[i] = i;
+      if (osc) osc[i] = sc[i];
+    }
+  } else {
+    const int per = (E + 63) / 64;
+    const int base = lane * per;
+    // slots past the lane's range or past E hold key 0 ("absent"): below every real key
+    // except the one NaN pattern whose key is 0, so the passes need no per-slot validity;
+    // the absent keys land in bin 0 while the prefix is 0 and are subtracted there
+    uint32_t key[PER];
+    uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool v = j < per && base + j < E;
+      key[j] = v ? score_key(sc[base + j]) : 0u;
+      kand &= v ? key[j] : 0xFFFFFFFFu;
+      kor |= key[j];
+    }
+    wave_and_or(kand, kor);
+    const int common = (kand ^ kor) ? __builtin_clz(kand ^ kor) : 32;
+    const uint32_t n_absent = 64u * PER - (uint32_t)E;
+    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+    uint32_t prefix = 0, pmask = 0;
+    int rem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (common >= 32 - shift) {
+        prefix |= kand & (255u << shift);
+        pmask |= 255u << shift;
+        continue;
+      }
+      uint32_t cur = 0u, run = 0u;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if ((key[j] & pmask) == prefix) {
+          const uint32_t d = (key[j] >> shift) & 255u;
+          if (run != 0u && d != cur) {
+            atomicAdd(&hist[cur], run);
+            run = 0u;
+          }
+          cur = d;
+          ++run;
+        }
+      }
+      if (run != 0u) atomicAdd(&hist[cur], run);
+      if (lane == 0 && prefix == 0u && n_absent) atomicSub(&hist[0], n_absent);
+      __builtin_amdgcn_wave_barrier();
+      uint32_t cs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs[j] = hist[255 - 4 * lane - j];
+      const uint32_t mine = cs[0] + cs[1] + cs[2] + cs[3];
+      uint32_t above = (uint32_t)wave_incl_sum((int)mine) - mine;
+      int hit_bin = -1;
+      uint32_t hit_above = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
+          hit_bin = 255 - 4 * lane - j;
+          hit_above = above;
+        }
+        above += cs[j];
+      }
+      const uint64_t m = __ballot(hit_bin >= 0);
+      const int src = m ? (int)__builtin_ctzll(m) : 0;
+      prefix |= (uint32_t)__builtin_amdgcn_readlane(hit_bin, src) << shift;
+      pmask |= 255u << shift;
+      rem -= __builtin_amdgcn_readlane((int)hit_above, src);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hist[255 - 4 * lane - j] = 0u;  // the bins this lane read
+    }
+    const uint32_t kth = prefix;
+    const int need_eq = rem;
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool v = j < per && base + j < E;
+      ngt += (v && key[j] > kth) ? 1 : 0;
+      neq += (v && key[j] == kth) ? 1 : 0;
+    }
+    const int packed = ngt | (neq << 16);  // E <= 65535
+    const int before = wave_incl_sum(packed) - packed;
+    int pos = (before & 0xFFFF) + min(before >> 16, need_eq);
+    int eq_seen = before >> 16;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool v = j < per && base + j < E;
+      const bool gt = v && key[j] > kth;
+      const bool eq = v && key[j] == kth && eq_seen < need_eq;
+      eq_seen += (v && key[j] == kth) ? 1 : 0;
+      if (gt || eq) {
+        oidx[pos] = base + j;
+        if (osc) osc[pos] = key_score(key[j]);
+        ++pos;
+      }
+    }
+  }
+  for (int p = n + lane; p < k; p += 64) {
+    oidx[p] = -1;
+    if (osc) osc[p] = 0.0f;
+  }
+  if (lane == 0) *ocnt = n;
 }
 
 // Exact top-k of one query over its scores sc[0..E) by one wave; writes the
@@ -243,8 +360,8 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
   // per-query top-k by its own wave (no workgroup barrier needed from here on)
   if (qvalid) {
     const int64_t q = (int64_t)b * a.T + j;
-    wave_topk(scw, (int)Eq, a.k, hist[wv], shw[wv], a.topk_idx + q * a.k,
-              a.topk_score ? a.topk_score + q * a.k : nullptr, a.topk_cnt + q);
+    wave_topk_reg<CAP / 64>(scw, (int)Eq, a.k, hist[wv], a.topk_idx + q * a.k,
+                            a.topk_score ? a.topk_score + q * a.k : nullptr, a.topk_cnt + q);
   }
 }
 
