@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "36233cb6076ed39974942adfd7fce72bf080cee1ae425be4fdcbc97c70ddec79",
-           "fetch_bytes": 859598890, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "be743ca0dd8f2a8397086fa9acd6b6688e597025928d3839d0b350b4dd405041",
+           "fetch_bytes": 859848122, "write_bytes": 536870912}
 
 
 def parse():
@@ -51,6 +51,11 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 4 device-to-device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--decode-only", default="", metavar="WORKLOAD",
+                    help="only time one decode workload (5 cold + 5 warm rounds, for profiling)")
+    ap.add_argument("--flush-probe", action="store_true",
+                    help="only measure a 128 MiB streaming read after no flush, after the "
+                         "decode timing's 512 MiB write flush and after a 512 MiB read flush")
     return ap.parse_args()
 
 
@@ -78,6 +83,34 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": 4}))
 
 
+def flush_probe(rounds=12):
+    """Read bandwidth of a plain 128 MiB reduction (torch's float sum) in three cache states:
+    warm (back to back), after writing a 512 MiB buffer (the decode timing's cold state: the
+    last-level cache then holds dirty lines that the reads must evict) and after reading
+    one (clean lines)."""
+    import torch
+    x = torch.ones(32 << 20, dtype=torch.float32, device="cuda")
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    flush_f = flush.view(torch.float32)
+    out = {}
+    for mode in ("warm", "after_write_flush", "after_read_flush"):
+        ms = []
+        for _ in range(rounds):
+            if mode == "after_write_flush":
+                flush.zero_()
+            elif mode == "after_read_flush":
+                flush_f.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            x.sum()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        med = sorted(ms[2:])[(rounds - 2) // 2]
+        out[mode] = {"us": round(med * 1e3, 2), "GB_per_s": round(x.numel() * 4 / (med * 1e-3) / 1e9, 1)}
+    print(json.dumps({"flush_probe": out, "bytes_read": x.numel() * 4}))
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -92,6 +125,16 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.flush_probe:
+        flush_probe()
+        return
+    if args.decode_only:
+        import torch
+        from compressed_sparse_attention_v4a_amd import binding as B
+        B.lib()  # fail loudly if the HIP library is missing
+        res = decode_timing(args.decode_only, torch.cuda.current_stream(), rounds=5, warmup=2)
+        print(json.dumps({args.decode_only: res}))
         return
 
     import numpy as np
