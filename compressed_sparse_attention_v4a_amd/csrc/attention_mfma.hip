@@ -61,7 +61,9 @@ constexpr int kHG = 64;        // heads per workgroup
 constexpr int kNC = 64;        // candidates per chunk
 constexpr int kRowBytes = kC * 2;
 constexpr int kChunkBytes = kNC * kRowBytes;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;      // two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = kNC / kWaves;  // rows of a chunk gathered by each wave
 constexpr int kMaxCand = 2048; // candidate-list capacity of one workgroup (k + w)
 // Probabilities are exp2(s - m_ref) with m_ref fixed after the first chunk.  They
 // stay below 2^kLazy; O (|v| < 2^6, at most 2^11 candidates) stays below 2^81, far
@@ -164,14 +166,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // Candidate <-> k-slot map of one P V step (16 candidates): slot 8 hl + 4 e + r holds
 // candidate 8 e + 4 hl + r.  A score tile's elements 8 p' .. 8 p' + 7 are then exactly
 // the A fragment of P V step p' of its 32-row block.
+//
+// Wave roles (8 waves, two per SIMD): wave w = 4 hh + 2 cc + kx scores head tile hh
+// against candidate block cc over the channel half kx; the two halves of a tile trade
+// the partial sums of the elements the other one owns (elements 8 kx' .. 8 kx' + 7 go to
+// the wave with kx = kx'), so each wave ends with the full scores of one P V step of its
+// block.  In P V, wave w owns the output channels 64 w .. 64 w + 63 of all 64 heads.
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kChunkBytes];  // chunk buffers / query rows
-  __shared__ __attribute__((aligned(16))) char pbuf[2 * 4 * 64 * 16];     // P [head tile][step][lane]
-  __shared__ __attribute__((aligned(16))) int rawidx_s[MODE == kModeHCA ? 4 : kMaxCand];  // top-k row
-  __shared__ float mx_s[4][32];   // chunk maximum per (wave, head of its tile)
-  __shared__ float lsum_s[4][32]; // softmax sums per (wave, head of its tile)
-  __shared__ int flag_s[4];
+  __shared__ __attribute__((aligned(16))) char xbuf[kWaves * 2 * 64 * 16]; // partial scores [wave][half][lane]
+  __shared__ __attribute__((aligned(16))) char pbuf[2 * 4 * 64 * 16];      // P [head tile][step][lane]
+  __shared__ float mx_s[kWaves][32];    // chunk maximum per (wave, head of its tile)
+  __shared__ float lsum_s[kWaves][32];  // softmax sums per (wave, head of its tile)
+  __shared__ int flag_s[kWaves];
   __shared__ __attribute__((aligned(16))) float den_s[kHG];
   __shared__ float mref_s[kHG];
   __shared__ __attribute__((aligned(16))) float rope_c[kMaxRopeDims / 2], rope_s[kMaxRopeDims / 2];
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int hh = wv >> 1, cc = wv & 1;
+  const int hh = wv >> 2, cc = (wv >> 1) & 1, kx = wv & 1;
   const int hl = lane >> 5, l32 = lane & 31;
   const bool decode = MODE == kModeDecode;
   const int nq = decode ? 1 : a.T;
@@ -188,9 +196,8 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   const int64_t n_items = decode ? (int64_t)a.batch * hgroups * a.splits : (int64_t)a.batch * hgroups * a.T;
 
   // ---- work items -----------------------------------------------------------
-  // Persistent workgroups take items blockIdx.x, +gridDim.x, ...  Prefill items run
-  // from the latest position (longest candidate list) down; decode items are
-  // (sequence, head group, candidate split).
+  // Prefill items run from the latest position (longest candidate list) down; decode
+  // items are (sequence, head group, candidate split).
   struct Item {
     int b, hgrp, qi, split;
     int64_t t, ncomp, lo, ub, nrows, nchunks;
@@ -241,49 +248,44 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     return it;
   };
 
-  // Query rows (64 heads x 1 KiB) of an item into chunk buffer qbuf, 16 rows per wave,
-  // 16-byte chunks swizzled like candidate rows; and its top-k row into rawidx_s.
-  auto issue_item_loads = [&](int64_t j, int qbuf) {
-    Item it;
-    if (decode) {
-      const int64_t r = j / a.splits;
-      it.hgrp = uni((int)(r % hgroups));
-      it.b = uni((int)(r / hgroups));
-      it.qi = 0;
-    } else {
-      const int64_t bh = (int64_t)a.batch * hgroups;
-      const int64_t r = j % bh;
-      it.b = uni((int)(r / hgroups));
-      it.hgrp = uni((int)(r % hgroups));
-      it.qi = uni(a.T - 1 - (int)(j / bh));
-    }
-    if (MODE != kModeHCA) {
-      const int32_t* irow = a.idx + ((int64_t)it.b * nq + it.qi) * a.k;
-      for (int j0 = 64 * wv; j0 < a.k; j0 += kThreads) {
-        if (j0 + lane < a.k) dma_b32(irow + j0, (uint32_t)lane * 4u, rawidx_s + j0);
-      }
-    }
+  // Query rows (64 heads x 1 KiB) of an item into chunk buffer qbuf, 8 rows per wave,
+  // 16-byte chunks swizzled like candidate rows.
+  auto issue_query_loads = [&](const Item& it, int qbuf) {
     const char* qrows = reinterpret_cast<const char*>(
         a.q + (((int64_t)it.b * nq + it.qi) * a.n_h + (int64_t)it.hgrp * kHG) * kC);
     char* dst = kvbuf + qbuf * kChunkBytes;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = 16 * wv + r;
-      const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const int h = kRowsPerWave * wv + r;
+      const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;  // swz(h) = swz(r)
       dma_b128(qrows + (int64_t)h * kRowBytes, voff, dst + h * kRowBytes);
     }
   };
 
-  // wave wv gathers rows [16 wv, 16 wv + 16) of the chunk starting at candidate r0;
-  // lane i of a row load carries chunk i of the global row into LDS chunk i ^ swz.
-  auto fill = [&](const Item& it, char* dst, int64_t r0) {
+  // Top-k entry of the row that lane j < 8 of wave wv gathers for the chunk starting at
+  // candidate r0 (row r0 + 8 wv + j), loaded a chunk ahead into a register.  Clamped to
+  // the top-k row; the value is only used for rows inside the compressed part.
+  auto load_raw = [&](const Item& it, int64_t r0) -> int {
+    if constexpr (MODE == kModeHCA) {
+      return 0;
+    } else {
+      if (a.k <= 0) return 0;
+      const int32_t* irow = a.idx + ((int64_t)it.b * nq + it.qi) * a.k;
+      const int64_t u = it.ub + r0 + kRowsPerWave * wv + (lane & 7);
+      return irow[u < a.k ? u : a.k - 1];
+    }
+  };
+
+  // wave wv gathers rows [8 wv, 8 wv + 8) of the chunk starting at candidate r0; lane i
+  // of a row load carries chunk i of the global row into LDS chunk i ^ swz.
+  // Address of row r0 + 8 wv + (lane & 7) of the candidate list (lanes j < 8 matter):
+  // each row load of gather_row takes it from lane j into scalar registers (the lane
+  // offset stays a 32-bit vector operand of the scalar-base form of the load)
+  auto row_addr = [&](const Item& it, int64_t r0, int raw) -> uint64_t {
     const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)it.b * a.E_cap * kC);
     const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)it.b * a.n_lrows * kC);
-    // lane j < 16 forms the address of row 16 wv + j; each row load then takes it
-    // from that lane into scalar registers (the lane offset stays a 32-bit vector
-    // operand of the scalar-base form of the load)
     int myid = -1 - (int)(it.t - a.lrow_base);  // past the list end: the query's own window row
-    const int64_t rr = r0 + 16 * wv + (lane & 15);
+    const int64_t rr = r0 + kRowsPerWave * wv + (lane & 7);
     if (rr < it.nrows) {
       const int64_t u = it.ub + rr;
       if (u < it.ncomp) {
@@ -291,60 +293,69 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           myid = (int)u;
         } else {
           // out-of-range indices must not fault
-          myid = (int)min(max((int64_t)rawidx_s[u], (int64_t)0), a.E_cap - 1);
+          myid = (int)min(max((int64_t)raw, (int64_t)0), a.E_cap - 1);
         }
       } else {
         myid = -1 - (int)(it.lo + (u - it.ncomp) - a.lrow_base);
       }
     }
-    const uint64_t myaddr = myid >= 0 ? (uint64_t)kvc_b + (uint64_t)myid * kRowBytes
-                                      : (uint64_t)kvl_b + (uint64_t)(-1 - myid) * kRowBytes;
-    const uint32_t alo = (uint32_t)myaddr, ahi = (uint32_t)(myaddr >> 32);
+    return myid >= 0 ? (uint64_t)kvc_b + (uint64_t)myid * kRowBytes
+                     : (uint64_t)kvl_b + (uint64_t)(-1 - myid) * kRowBytes;
+  };
+  // row 8 wv + r of a chunk into chunk buffer dst; lane i carries chunk i of the global
+  // row into LDS chunk i ^ swz(r) (row 8 wv + r has swz(r))
+  auto gather_row = [&](uint64_t addr, char* dst, int r) {
+    // readlane returns int: go through uint32_t so the low half is not sign-extended
+    const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(addr >> 32), r) << 32) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)addr, r);
+    // the lane offset is formed at each use from an opaque copy: hoisted, the eight
+    // per-row offsets would hold eight registers across the loop
+    uint32_t lb = (uint32_t)lane << 4;
+    asm volatile("" : "+v"(lb));
+    dma_b128(reinterpret_cast<const char*>(ra), lb ^ ((uint32_t)swz(r) << 4), dst + (kRowsPerWave * wv + r) * kRowBytes);
+  };
+  auto fill = [&](const Item& it, char* dst, int64_t r0, int raw) {
+    const uint64_t addr = row_addr(it, r0, raw);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // readlane returns int: go through uint32_t so the low half is not sign-extended
-      const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(ahi, r) << 32) |
-                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(alo, r);
-      const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;  // rows 16 wv + r share swz(r)
-      dma_b128(reinterpret_cast<const char*>(ra), voff, dst + (16 * wv + r) * kRowBytes);
-    }
+    for (int r = 0; r < kRowsPerWave; ++r) gather_row(addr, dst, r);
   };
 
   // ---- per-lane LDS byte offsets (everything step-dependent is an immediate) --
-  // score reads: row 32 cc + l32, chunk 2 s + hl = 8 (s >> 2) + (2 (s & 3) + hl), swizzled
+  // score reads: row 32 cc + l32, channels 256 kx + 16 s + 8 hl .. + 7, i.e. chunk
+  // 8 (4 kx + (s >> 2)) + (2 (s & 3) + hl), swizzled within its 128-byte group
   const int srow = 32 * cc + l32;
   int sb[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4);
+  for (int u = 0; u < 4; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4) + 512 * kx;
   // transposing V reads, 16-lane group G = lane >> 4, J = lane & 15 = 4 i + q:
-  //   row 16 p + 8 e + 4 (G >> 1) + i, channels 32 T + 16 (G & 1) + 4 q .. +3, T = 4 wv + nt
-  //   (wave wv owns the 128 contiguous channels 128 wv ..); chunk 16 wv + 4 nt + x lies at
-  //   byte 256 wv + 128 (nt >> 1) + 16 ((4 (nt & 1) + x) ^ swz(row)) of its row
+  //   row 16 p + 8 e + 4 (G >> 1) + i, channels 32 T + 16 (G & 1) + 4 q .. +3, T = 2 wv + nt
+  //   (wave wv owns the 64 contiguous channels 64 wv ..); chunk 8 wv + 4 nt + x lies at
+  //   byte 128 wv + 16 ((4 nt + x) ^ swz(row)) of its row
   int vbase[2];
   {
     const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
     const int x = 2 * (G & 1) + (q >> 1);
     const int y = (i << 1) | (G >> 1);  // swz of the row
 #pragma unroll
-    for (int odd = 0; odd < 2; ++odd)
-      vbase[odd] = (4 * (G >> 1) + i) * kRowBytes + 256 * wv + (((4 * odd + x) ^ y) << 4) + 8 * (q & 1);
+    for (int nt = 0; nt < 2; ++nt)
+      vbase[nt] = (4 * (G >> 1) + i) * kRowBytes + 128 * wv + (((4 * nt + x) ^ y) << 4) + 8 * (q & 1);
   }
   const int pbase = lane * 16;
 
   const int64_t item = blockIdx.x;
   if (item >= n_items) return;
-  // every load of the prologue goes out at once: top-k row and query rows (direct to
-  // LDS), then the query RMSNorm weights and the RoPE frequencies
   constexpr int par = 0;  // chunk c lives in buffer c & 1; the query rows land in buffer 1
-  issue_item_loads(item, 1);
+  const Item cur = describe(item);
+  // every load of the prologue goes out at once: query rows (direct to LDS), the top-k
+  // entries of the first two chunks, the query RMSNorm weights
+  issue_query_loads(cur, 1);
   __builtin_amdgcn_sched_barrier(0);
-  float2 g = make_float2(1.0f, 1.0f);
-  if (a.q_gamma) g = *reinterpret_cast<const float2*>(a.q_gamma + 2 * tid);
+  const int raw0 = load_raw(cur, 0);
+  const int raw1 = load_raw(cur, kNC);
+  const float g = a.q_gamma ? a.q_gamma[tid] : 1.0f;
   const double f = tid < kMaxRopeDims / 2 ? a.rope.inv_freq[tid] : 0.0;
   {
-    const Item cur = describe(item);
-    *reinterpret_cast<float2*>(qg_s + 2 * tid) = g;
-    wait_vmcnt<0>();
+    qg_s[tid] = g;
     // RoPE angles at t for the 32 frequencies (the inverse rotation of the output uses
     // -sin); without RoPE the table is the identity, so the rotations below need no branch
     if (tid < kMaxRopeDims / 2) {
@@ -353,33 +364,34 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       rope_c[tid] = cs;
       rope_s[tid] = sn;
     }
+    wait_vmcnt<0>();
     wait_lgkmcnt<0>();
-    block_sync();  // query rows, top-k row, angles (and gamma) visible
-    if (cur.nchunks > 0) fill(cur, kvbuf + par * kChunkBytes, 0);
+    block_sync();  // query rows, angles and gamma visible
+    if (cur.nchunks > 0) fill(cur, kvbuf + par * kChunkBytes, 0, raw0);
 
     // ---- query rows: q * gamma, rotated at t on the last 64 channels, bf16, in place ----
-    // Wave wv prepares heads 16 wv + l16 (l16 = lane & 15); lane quarter g4 = lane >> 4
-    // takes the 16-byte chunks g4 + 4 u.  The per-head factor scale * log2 e / rms(q) is
-    // applied to the float32 scores instead.
+    // Wave wv prepares heads 8 wv + l8 (l8 = lane & 7); lane group g8 = lane >> 3 takes
+    // the 16-byte chunks g8 + 8 u.  The per-head factor scale * log2 e / rms(q) is applied
+    // to the float32 scores instead.
     char* qbufp = kvbuf + (par ^ 1) * kChunkBytes;
     {
-      const int l16 = lane & 15, g4 = lane >> 4;
-      const int hq = 16 * wv + l16;
+      const int l8 = lane & 7, g8 = lane >> 3;
+      const int hq = kRowsPerWave * wv + l8;
       float ss = 0.0f;
 #pragma unroll
-      for (int u0 = 0; u0 < 16; u0 += 4) {
+      for (int u0 = 0; u0 < 8; u0 += 4) {
         u32x4 v[4];
         float4 gm[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int j = g4 + 4 * (u0 + u);
-          v[u] = __builtin_bit_cast(u32x4, lds_read_b128(qbufp, hq * kRowBytes + ((j ^ swz(l16)) << 4)));
+          const int j = g8 + 8 * (u0 + u);
+          v[u] = __builtin_bit_cast(u32x4, lds_read_b128(qbufp, hq * kRowBytes + ((j ^ swz(l8)) << 4)));
           gm[u][0] = *reinterpret_cast<const float4*>(qg_s + 8 * j);
           gm[u][1] = *reinterpret_cast<const float4*>(qg_s + 8 * j + 4);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int j = g4 + 4 * (u0 + u);
+          const int j = g8 + 8 * (u0 + u);
           float x[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -390,11 +402,11 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
           float y[8] = {x[0] * gm[u][0].x, x[1] * gm[u][0].y, x[2] * gm[u][0].z, x[3] * gm[u][0].w,
                         x[4] * gm[u][1].x, x[5] * gm[u][1].y, x[6] * gm[u][1].z, x[7] * gm[u][1].w};
-          if (u0 + u >= 14) {
-            // chunks 56 .. 63: pairs (8 j + 2 e, +1) use frequency 4 (j - 56) + e (identity
+          if (u0 + u == 7) {
+            // chunk j = 56 + g8: pairs (8 j + 2 e, +1) use frequency 4 g8 + e (identity
             // angles when RoPE is off)
-            const float4 c4 = *reinterpret_cast<const float4*>(rope_c + 4 * (j - 56));
-            const float4 s4 = *reinterpret_cast<const float4*>(rope_s + 4 * (j - 56));
+            const float4 c4 = *reinterpret_cast<const float4*>(rope_c + 4 * g8);
+            const float4 s4 = *reinterpret_cast<const float4*>(rope_s + 4 * g8);
             const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
             const float sj[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
@@ -405,22 +417,24 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
             }
           }
           const u32x4 pk = {pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]), pk_bf16(y[4], y[5]), pk_bf16(y[6], y[7])};
-          *reinterpret_cast<u32x4*>(qbufp + hq * kRowBytes + ((j ^ swz(l16)) << 4)) = pk;
+          *reinterpret_cast<u32x4*>(qbufp + hq * kRowBytes + ((j ^ swz(l8)) << 4)) = pk;
         }
       }
+      ss += __shfl_xor(ss, 8, 64);
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
-      if (g4 == 0) qinv_s[hq] = a.q_gamma ? a.qscale / sqrtf(ss / (float)kC + a.eps) : a.qscale;
+      if (g8 == 0) qinv_s[hq] = a.q_gamma ? a.qscale / sqrtf(ss / (float)kC + a.eps) : a.qscale;
     }
     wait_lgkmcnt<0>();
     block_sync();  // prepared query rows and factors visible
 
     // ---- resident query heads: B fragments of S^T = K Q^T ------------------
-    // lane (hl, l32): head 32 hh + l32, k-step s covers channels 16 s + 8 hl .. +7
-    bf16x8 qb[32];
+    // lane (hl, l32): head 32 hh + l32, k-step s covers channels 256 kx + 16 s + 8 hl .. +7
+    bf16x8 qb[16];
 #pragma unroll
-    for (int s = 0; s < 32; ++s)
-      qb[s] = lds_read_b128(qbufp, (32 * hh + l32) * kRowBytes + (((2 * (s & 3) + hl) ^ swz(l32)) << 4) + 128 * (s >> 2));
+    for (int s = 0; s < 16; ++s)
+      qb[s] = lds_read_b128(qbufp, (32 * hh + l32) * kRowBytes + (((2 * (s & 3) + hl) ^ swz(l32)) << 4) +
+                                       128 * (4 * kx + (s >> 2)));
     const float qinv = qinv_s[32 * hh + l32];
     // the next chunk's gather overwrites the query rows: every fragment read has returned
     // before the first loop barrier
@@ -431,8 +445,24 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     // a later chunk maximum exceeds it by more than kLazy.
     float m_ref = -INFINITY;  // head 32 hh + l32 (log2 units)
     const int64_t nchunks = cur.nchunks;
+    // largest of the four chunk maxima of this wave's head tile
+    auto tile_max = [&]() {
+      return fmaxf(fmaxf(mx_s[4 * hh][l32], mx_s[4 * hh + 1][l32]),
+                   fmaxf(mx_s[4 * hh + 2][l32], mx_s[4 * hh + 3][l32]));
+    };
 
-    auto run = [&](f32x16 (&O)[2][4], float& l_part) -> bool {
+    // Whether a wave saw a chunk maximum past the reference (read after the barrier that
+    // follows the flags, once per pass over the list); a decode split then takes the
+    // largest chunk maximum of the tile as its new reference, so that the next pass
+    // cannot overflow.
+    auto overflowed = [&]() -> bool {
+      if (!uni(flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3] | flag_s[4] | flag_s[5] | flag_s[6] | flag_s[7]))
+        return false;
+      if constexpr (MODE == kModeDecode) m_ref = fmaxf(m_ref, tile_max());
+      return true;
+    };
+
+    auto run = [&](f32x16 (&O)[2][2], float& l_part, int raw_n) -> bool {
       {
         // zero the accumulators with the matrix unit, so that every value reaching the
         // loop-carried accumulators is defined by an MFMA (keeps them in AGPRs)
@@ -443,100 +473,131 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) O[ht][nt] = mfma32(z8, z8, z16);
+          for (int nt = 0; nt < 2; ++nt) O[ht][nt] = mfma32(z8, z8, z16);
       }
       l_part = 0.0f;
-      for (int64_t c = 0; c < nchunks; ++c) {
+      bool ovf = false;          // a chunk maximum past the reference (this lane's head)
+      float mx_run = -INFINITY;  // largest chunk maximum so far (decode restarts)
+      // one chunk; MORE: a next chunk exists (compile time, so that the gathers interleaved
+      // below need no branches; the last chunk is a copy without them)
+      auto chunk = [&](int64_t c, auto more_t) -> bool {
+        constexpr bool more = decltype(more_t)::value;
         const int64_t r0 = c * kNC;
         const int bi = (int)((c + par) & 1);
         const char* buf = kvbuf + bi * kChunkBytes;
         char* nbuf = kvbuf + (bi ^ 1) * kChunkBytes;
         wait_vmcnt<0>();
         block_sync();  // chunk c landed for every wave; chunk c - 1 fully consumed
-        if (c + 1 < nchunks) fill(cur, nbuf, r0 + kNC);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // scores: 32 k-steps, fragment reads two steps ahead
+        // partial scores over this wave's channel half: 16 k-steps, fragment reads two
+        // steps ahead
         f32x16 S;
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[i] = 0.0f;
         bf16x8 ka[3];
         ka[0] = lds_read_b128(buf, sb[0]);
         ka[1] = lds_read_b128(buf, sb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        // the next chunk's rows are gathered one at a time between the matrix
+        // instructions (rows 0-3 in the score steps, 4-7 early in the P V steps), so that
+        // no wave stalls on a burst of loads while its SIMD's matrix unit idles and the
+        // address unit is never saturated; the row addresses are formed while the first
+        // fragments are read
+        uint64_t naddr = 0;
+        if constexpr (more) {
+          naddr = row_addr(cur, r0 + kNC, raw_n);
+          if (c + 2 < nchunks) raw_n = load_raw(cur, r0 + 2 * kNC);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 32; ++s) {
-          if (s + 2 < 32) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 3] + 128 * ((s + 2) >> 2));
+        for (int s = 0; s < 16; ++s) {
+          if (s + 2 < 16) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 3] + 128 * ((s + 2) >> 2));
           __builtin_amdgcn_sched_barrier(0);
           S = mfma32(ka[s % 3], qb[s], S);
+          if ((s & 3) == 1 && more) gather_row(naddr, nbuf, s >> 2);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // candidates past the end of the list (last chunk only)
+        // trade halves with the other channel half of the tile (wave wv ^ 1): send the
+        // elements it owns, keep elements 8 kx .. 8 kx + 7
+        // (bit selects with a wave-uniform mask: a conditional on kx becomes indexed
+        // register moves)
+        float own[8], snd[8];
+        const uint32_t km = 0u - (uint32_t)kx;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = __float_as_uint(S[i]), hi = __float_as_uint(S[8 + i]);
+          own[i] = __uint_as_float((hi & km) | (lo & ~km));
+          snd[i] = __uint_as_float((lo & km) | (hi & ~km));
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          *reinterpret_cast<float4*>(xbuf + ((wv * 2 + h2) * 64 + lane) * 16) =
+              make_float4(snd[4 * h2], snd[4 * h2 + 1], snd[4 * h2 + 2], snd[4 * h2 + 3]);
+        wait_lgkmcnt<0>();
+        block_sync();  // partial scores of every wave visible
+        float sc[8];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float4 rv = *reinterpret_cast<const float4*>(xbuf + (((wv ^ 1) * 2 + h2) * 64 + lane) * 16);
+          sc[4 * h2] = own[4 * h2] + rv.x;
+          sc[4 * h2 + 1] = own[4 * h2 + 1] + rv.y;
+          sc[4 * h2 + 2] = own[4 * h2 + 2] + rv.z;
+          sc[4 * h2 + 3] = own[4 * h2 + 3] + rv.w;
+        }
+        // candidates past the end of the list (last chunk only): element i is candidate
+        // 32 cc + 16 kx + 8 (i >> 2) + 4 hl + (i & 3) of the chunk
         if (__builtin_expect(r0 + kNC > cur.nrows, 0)) {
           asm volatile("" ::: "memory");  // keep this a branch: only the last chunk is partial
-          const int lim = (int)(cur.nrows - r0) - 32 * cc - 4 * hl;
+          const int lim = (int)(cur.nrows - r0) - 32 * cc - 16 * kx - 4 * hl;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) >= lim) S[i] = -INFINITY;
+          for (int i = 0; i < 8; ++i)
+            if (8 * (i >> 2) + (i & 3) >= lim) sc[i] = -INFINITY;
         }
-        float lmax = S[0];
+        float lmax = sc[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, S[i]);
-        lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64)) * qinv;  // qinv > 0: order kept
-        bool restart = false;
+        for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, sc[i]);
+        {
+          // the other half-wave's maximum for the same head (row swap, no LDS round trip)
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax), false, false);
+          lmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * qinv;  // qinv > 0: order kept
+        }
+        if constexpr (MODE == kModeDecode) mx_run = fmaxf(mx_run, lmax);
         if (c == 0) {
-          // reference maximum: this chunk's maximum over both candidate blocks
+          // reference maximum: this chunk's maximum over the tile's four waves
           if (hl == 0) mx_s[wv][l32] = lmax;
           wait_lgkmcnt<0>();
           block_sync();
           if constexpr (MODE == kModeDecode) {
-            m_ref = fmaxf(m_ref, fmaxf(lmax, mx_s[wv ^ 1][l32]));  // raised by a restart
+            m_ref = fmaxf(m_ref, tile_max());  // raised by a restart
           } else {
-            m_ref = fmaxf(lmax, mx_s[wv ^ 1][l32]);
+            m_ref = tile_max();
           }
           if (m_ref == -INFINITY) m_ref = 0.0f;
         } else {
-          restart = lmax > m_ref + kLazy;
-          if constexpr (MODE == kModeDecode) {
-            if (hl == 0) mx_s[wv][l32] = lmax;  // a restart's new reference
-          }
+          ovf = ovf || lmax > m_ref + kLazy;
         }
-        float pr[16];
+        float pr[8];
         float ls = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(fmaf(S[i], qinv, -m_ref));
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], qinv, -m_ref));
           ls += pr[i];
         }
         l_part += ls;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const float* p0 = pr + 8 * pp;
-          const u32x4 pk = {pk_bf16(p0[0], p0[1]), pk_bf16(p0[2], p0[3]), pk_bf16(p0[4], p0[5]),
-                            pk_bf16(p0[6], p0[7])};
-          *reinterpret_cast<u32x4*>(pbuf + ((hh * 4 + 2 * cc + pp) * 64) * 16 + pbase) = pk;
-        }
         {
-          const bool any = __ballot(restart) != 0;
-          if (lane == 0) flag_s[wv] = any ? 1 : 0;
+          const u32x4 pk = {pk_bf16(pr[0], pr[1]), pk_bf16(pr[2], pr[3]), pk_bf16(pr[4], pr[5]),
+                            pk_bf16(pr[6], pr[7])};
+          *reinterpret_cast<u32x4*>(pbuf + ((hh * 4 + 2 * cc + kx) * 64) * 16 + pbase) = pk;
         }
         wait_lgkmcnt<0>();
-        block_sync();  // P and flags of every wave visible
-        if (uni(flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3])) {
-          if constexpr (MODE == kModeDecode) {
-            // the new reference of a restart: this chunk's maximum (the same in both
-            // candidate blocks' waves of a head tile)
-            m_ref = fmaxf(m_ref, fmaxf(lmax, mx_s[wv ^ 1][l32]));
-          }
-          return false;
-        }
+        block_sync();  // P of every wave visible
 
         // O^T[channel tiles of wave wv][64 heads] += V^T P^T over 4 steps of 16 candidates:
         // the V fragments are the A operand, the P fragments the B operand, so a lane ends
-        // with 4 consecutive channels of one head (stored without staging)
+        // with 4 consecutive channels of one head
         __builtin_amdgcn_sched_barrier(0);
         auto vread = [&](int it) -> bf16x8 {
-          // it = 4 p + nt
-          const int off = vbase[it & 1] + 16384 * (it >> 2) + 128 * ((it & 3) >> 1);
+          // it = 2 p + nt
+          const int off = vbase[it & 1] + 16384 * (it >> 1);
           const u32x2 v1 = lds_read_tr(buf, off);
           const u32x2 v2 = lds_read_tr(buf, off + 8 * kRowBytes);
           const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
@@ -549,29 +610,46 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         vb[0] = vread(0);
         vb[1] = vread(1);
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int p = it >> 2, nt = it & 3;
+        for (int it = 0; it < 8; ++it) {
+          const int p = it >> 1, nt = it & 1;
           if (nt == 0 && p + 1 < 4) {
             pa[(p + 1) & 1][0] = lds_read_b128(pbuf, pbase + (p + 1) * 1024);
             pa[(p + 1) & 1][1] = lds_read_b128(pbuf, pbase + 4 * 1024 + (p + 1) * 1024);
           }
-          if (it + 2 < 16) vb[(it + 2) % 3] = vread(it + 2);
+          if (it + 2 < 8) vb[(it + 2) % 3] = vread(it + 2);
           __builtin_amdgcn_sched_barrier(0);
           O[0][nt] = mfma32(vb[it % 3], pa[p & 1][0], O[0][nt]);
+          if (it < 4 && more) gather_row(naddr, nbuf, 4 + it);
           O[1][nt] = mfma32(vb[it % 3], pa[p & 1][1], O[1][nt]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        return true;
+      };
+      for (int64_t c = 0; c + 1 < nchunks; ++c)
+        if (!chunk(c, std::true_type{})) return false;
+      if (nchunks > 0 && !chunk(nchunks - 1, std::false_type{})) return false;
+      // an overflow is acted on once the pass is over: the item is abandoned (prefill) or
+      // the pass restarts with a larger reference (decode); the values computed meanwhile
+      // are discarded
+      {
+        const bool any = __ballot(ovf) != 0;
+        if (lane == 0) flag_s[wv] = any ? 1 : 0;
+        if constexpr (MODE == kModeDecode) {
+          if (hl == 0) mx_s[wv][l32] = mx_run;
+        }
       }
-      return true;
+      wait_lgkmcnt<0>();
+      block_sync();  // flags visible
+      return !(nchunks > 0 && overflowed());
     };
 
     // ---- epilogue -------------------------------------------------------------
-    auto finish = [&](f32x16 (&O)[2][4], float l_part) {
+    auto finish = [&](f32x16 (&O)[2][2], float l_part) {
       {
         const float l = l_part + __shfl_xor(l_part, 32, 64);
         if (hl == 0) {
           lsum_s[wv][l32] = l;
-          if (cc == 0) mref_s[32 * hh + l32] = m_ref;
+          if (cc == 0 && kx == 0) mref_s[32 * hh + l32] = m_ref;
         }
       }
       wait_lgkmcnt<0>();
@@ -579,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       const bool partial = decode && a.splits > 1;
       if (tid < kHG) {
         const int ht = tid >> 5, h = tid & 31;
-        const float l = lsum_s[2 * ht][h] + lsum_s[2 * ht + 1][h];
+        const float l = (lsum_s[4 * ht][h] + lsum_s[4 * ht + 1][h]) + (lsum_s[4 * ht + 2][h] + lsum_s[4 * ht + 3][h]);
         if (partial) {
           den_s[tid] = l;
         } else {
@@ -590,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       }
       wait_lgkmcnt<0>();
       block_sync();  // per-head denominators visible
-      // lane (hl, l32) holds, for head tile ht and channel tile T = 4 wv + nt, head
+      // lane (hl, l32) holds, for head tile ht and channel tile T = 2 wv + nt, head
       // 32 ht + l32 at channels 32 T + 8 j + 4 hl + (0..3) in O[ht][nt][4 j .. 4 j + 3]
       if (partial) {
         // partial state: [b][split][h][c + 2] = (O unnormalised, reference max, sum)
@@ -599,11 +677,11 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         for (int ht = 0; ht < 2; ++ht) {
           float* prow = pg + (int64_t)(32 * ht + l32) * (kC + 2);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
+          for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               // rows are c + 2 floats long, so only 8-byte alignment is guaranteed
-              float* d = prow + 128 * wv + 32 * nt + 8 * j + 4 * hl;
+              float* d = prow + 64 * wv + 32 * nt + 8 * j + 4 * hl;
               *reinterpret_cast<float2*>(d) = make_float2(O[ht][nt][4 * j], O[ht][nt][4 * j + 1]);
               *reinterpret_cast<float2*>(d + 2) = make_float2(O[ht][nt][4 * j + 2], O[ht][nt][4 * j + 3]);
             }
@@ -615,26 +693,27 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         }
         return;
       }
-      // normalise, inverse RoPE on the last 64 channels (wave 3, channel tiles 2 and 3), bf16;
-      // the two half-waves swap 4-channel groups so each lane holds 8 consecutive channels,
-      // and each wave transposes its 64 heads x 128 channels through its own 16 KiB of the
-      // chunk buffers (row = head, 16-byte chunk 4 nt + 2 jp + hl at position chunk ^ (head
-      // & 7)), so that every store instruction writes 4 whole 256-byte head segments
-      char* tb = kvbuf + wv * 16384;
+      // normalise, inverse RoPE on the last 64 channels (wave 7), bf16; the two half-waves
+      // swap 4-channel groups so each lane holds 8 consecutive channels, and each wave
+      // transposes its 64 heads x 64 channels through its own 8 KiB of the chunk buffers
+      // (row = head, 16-byte chunk 4 nt + 2 jp + hl at position chunk ^ (head & 7)), so
+      // that every store instruction writes 8 whole 128-byte head segments
+      char* tb = kvbuf + wv * 8192;
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         const float inv = den_s[32 * ht + l32];
         const int h = 32 * ht + l32;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 2; ++nt) {
           uint32_t pk[4][2];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float x[4] = {O[ht][nt][4 * j] * inv, O[ht][nt][4 * j + 1] * inv, O[ht][nt][4 * j + 2] * inv,
                           O[ht][nt][4 * j + 3] * inv};
-            if (nt >= 2 && wv == 3) {
-              // pairs (ch, ch + 1), ch = 32 T + 8 j + 4 hl + 2 e, use frequency (ch - (c - 64)) / 2
-              const int f = 16 * (nt - 2) + 4 * j + 2 * hl;
+            if (wv == kWaves - 1) {
+              // pairs (ch, ch + 1), ch = 448 + 32 nt + 8 j + 4 hl + 2 e, use frequency
+              // (ch - 448) / 2
+              const int f = 16 * nt + 4 * j + 2 * hl;
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
                 const float cs = rope_c[f + e], sn = rope_s[f + e];
@@ -654,24 +733,24 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
             const auto w1 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][1], pk[2 * jp + 1][1], false, false);
             const u32x4 v = {w0[0], w1[0], w0[1], w1[1]};
             const int cidx = 4 * nt + 2 * jp + hl;
-            *reinterpret_cast<u32x4*>(tb + h * 256 + ((cidx ^ (h & 7)) << 4)) = v;
+            *reinterpret_cast<u32x4*>(tb + h * 128 + ((cidx ^ (h & 7)) << 4)) = v;
           }
         }
       }
       asm volatile("" ::: "memory");  // LDS operations of a wave complete in order
       uint16_t* dst = a.out + (((int64_t)cur.b * nq + cur.qi) * a.n_h + (int64_t)cur.hgrp * kHG) * kC;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // lanes 16 k .. 16 k + 15: head 4 i + k, chunk cidx = lane & 15 = channels
-        // 128 wv + 8 cidx .. + 7
-        const int h = 4 * i + (lane >> 4), cidx = lane & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(tb + h * 256 + ((cidx ^ (h & 7)) << 4));
-        *reinterpret_cast<u32x4*>(dst + (int64_t)h * kC + 128 * wv + 8 * cidx) = v;
+      for (int i = 0; i < 8; ++i) {
+        // lanes 8 k .. 8 k + 7: head 8 i + k, chunk cidx = lane & 7 = channels
+        // 64 wv + 8 cidx .. + 7
+        const int h = 8 * i + (lane >> 3), cidx = lane & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tb + h * 128 + ((cidx ^ (h & 7)) << 4));
+        *reinterpret_cast<u32x4*>(dst + (int64_t)h * kC + 64 * wv + 8 * cidx) = v;
       }
     };
 
     {
-      f32x16 O[2][4];
+      f32x16 O[2][2];
       float l_part;
       if constexpr (MODE == kModeDecode) {
         // decode splits restart instead of leaving the item to the exact kernel (which would
@@ -679,19 +758,21 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         // flight lands, chunk 0 is gathered again and the loop starts over.  Each restart
         // raises some head's reference to one of its own chunk maxima, so restarts are
         // finite.
-        if (__builtin_expect(!run(O, l_part), 0)) {
+        if (__builtin_expect(!run(O, l_part, raw1), 0)) {
           do {
             wait_vmcnt<0>();
             block_sync();
-            fill(cur, kvbuf + par * kChunkBytes, 0);
-          } while (!run(O, l_part));
+            fill(cur, kvbuf + par * kChunkBytes, 0, raw0);
+          } while (!run(O, l_part, raw1));
         }
         finish(O, l_part);
-      } else if (run(O, l_part)) {
+      } else if (run(O, l_part, raw1)) {
         finish(O, l_part);
       } else {
         // a chunk maximum ran past the reference: list the item for the exact general
-        // kernel, which recomputes it after this one, and move on
+        // kernel, which recomputes it after this one, and move on (after the gather in
+        // flight has landed)
+        wait_vmcnt<0>();
         if (tid == 0) {
           const int slot = atomicAdd(a.redo, 1);
           a.redo[1 + slot] = (int)item;
