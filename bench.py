@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "be743ca0dd8f2a8397086fa9acd6b6688e597025928d3839d0b350b4dd405041",
-           "fetch_bytes": 859848122, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "c56f5ec7fcc2cf96a36fdcb35b287cf34a26da12f7fc8e80563b44d673601876",
+           "fetch_bytes": 857497388, "write_bytes": 536870912}
 
 
 def parse():

@@ -7,30 +7,33 @@
 // row serving as key and value of every head, a sink logit in the denominator,
 // and inverse RoPE at t on the output.
 //
-// Work decomposition (one workgroup = one query position x 64 heads, 4 waves,
-// all products on v_mfma_f32_32x32x16_bf16):
+// Work decomposition (one workgroup = one query position x 64 heads, 8 waves, two
+// per SIMD, all products on v_mfma_f32_32x32x16_bf16):
 //   * Candidate rows (1 KiB each) stream through LDS 64 at a time, double
 //     buffered, gathered with direct global->LDS 16-byte loads (one row per
-//     instruction, row address in scalar registers).  The 16-byte chunks of a
-//     row are XOR-swizzled by a function of the row so that both read patterns
-//     below are bank-conflict free.
-//   * Scores S^T = K Q^T: wave w = 2 hh + cc computes head tile hh (32 heads)
-//     against candidate block cc (32 rows) of the chunk, with its 32 query heads
-//     resident in registers as B fragments (RMS-normalised, rotated at t,
-//     pre-scaled by scale * log2 e).  Each K byte is read from LDS twice.
+//     instruction, row address in scalar registers), one row at a time between
+//     the matrix instructions of the chunk before.  The 16-byte chunks of a row
+//     are XOR-swizzled by a function of the row so that both read patterns below
+//     are bank-conflict free.  The top-k entries of the rows are loaded into
+//     registers a chunk ahead.
+//   * Scores S^T = K Q^T: wave w = 4 hh + 2 cc + kx computes head tile hh (32
+//     heads) against candidate block cc (32 rows) of the chunk over channel half
+//     kx, with its query fragments resident in registers (RMS-normalised scale
+//     applied to the float32 scores, rotated at t).  The two halves of a tile
+//     trade the partial sums of the elements the other one owns through LDS.
 //   * Softmax with a fixed reference maximum per head (the first chunk's
-//     maximum): probabilities are exp2(s - m_ref) < 2^64, so O is never rescaled;
-//     if a later chunk maximum exceeds the reference by more than that, the
-//     workgroup abandons the item and lists it for the exact general kernel, which
-//     recomputes it in float32 afterwards; a decode split instead raises its
-//     reference to that maximum and restarts (neither is triggered for normalised
-//     queries and rows).  The
-//     score accumulator layout of the 32x32 tile is already the A-operand layout
-//     of P V (candidate k-slots permuted identically on both sides), so each
-//     wave packs its P to bf16 and stores it to LDS as ready-made fragments.
-//   * O += P V: wave w owns output channel tiles 32 (w + 4 nt), nt < 4, of all
-//     64 heads (8 accumulator tiles), reading P fragments from LDS and V straight
-//     from the row-major chunk with the gfx950 transposing LDS read.
+//     maximum): probabilities are exp2(s - m_ref) < 2^64, so O is never rescaled.
+//     A chunk maximum past the reference by more than that is noted and acted on
+//     after the pass: the workgroup lists the item for the exact general kernel,
+//     which recomputes it in float32 afterwards; a decode split instead restarts
+//     with the pass maximum as reference (neither is triggered for normalised
+//     queries and rows).  The score accumulator layout of the 32x32 tile is
+//     already the A-operand layout of P V (candidate k-slots permuted identically
+//     on both sides), so each wave packs its P to bf16 and stores it to LDS as a
+//     ready-made fragment.
+//   * O += P V: wave w owns output channels 64 w .. 64 w + 63 of all 64 heads (4
+//     accumulator tiles), reading P fragments from LDS and V straight from the
+//     row-major chunk with the gfx950 transposing LDS read.
 //   * Epilogue: normalisation (+ sink), inverse RoPE, bf16 output staged through
 //     LDS for coalesced 16-byte stores; the decode form writes float32 partial
 //     states (unnormalised O, reference max, sum) for the merge kernel.
@@ -64,7 +67,7 @@ constexpr int kChunkBytes = kNC * kRowBytes;
 constexpr int kWaves = 8;      // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = kNC / kWaves;  // rows of a chunk gathered by each wave
-constexpr int kMaxCand = 2048; // candidate-list capacity of one workgroup (k + w)
+constexpr int kMaxCand = 2048; // longest candidate list (k + w) served here; longer lists take the general kernel
 // Probabilities are exp2(s - m_ref) with m_ref fixed after the first chunk.  They
 // stay below 2^kLazy; O (|v| < 2^6, at most 2^11 candidates) stays below 2^81, far
 // from float32 overflow.  A chunk maximum that grows further sends the item to the
@@ -367,7 +370,10 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();
     block_sync();  // query rows, angles and gamma visible
-    if (cur.nchunks > 0) fill(cur, kvbuf + par * kChunkBytes, 0, raw0);
+    // chunk 0 is gathered during the query preparation, four rows before each of its two
+    // halves (a burst of eight loads per wave would hold the preparation back)
+    const bool first = cur.nchunks > 0;
+    const uint64_t addr0 = row_addr(cur, 0, raw0);
 
     // ---- query rows: q * gamma, rotated at t on the last 64 channels, bf16, in place ----
     // Wave wv prepares heads 8 wv + l8 (l8 = lane & 7); lane group g8 = lane >> 3 takes
@@ -380,6 +386,10 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       float ss = 0.0f;
 #pragma unroll
       for (int u0 = 0; u0 < 8; u0 += 4) {
+        if (first) {
+#pragma unroll
+          for (int r = u0; r < u0 + 4; ++r) gather_row(addr0, kvbuf + par * kChunkBytes, r);
+        }
         u32x4 v[4];
         float4 gm[4][2];
 #pragma unroll
