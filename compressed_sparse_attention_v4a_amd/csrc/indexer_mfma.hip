@@ -319,6 +319,18 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
   const int bb1 = jj * kRowB + (((2 * g + 1) ^ (jj & 7)) << 4);
   float* scw = sc[wv];
 
+  // The ReLU-weighted head sum of each 16-entry tile runs on the vector unit while the
+  // matrix unit multiplies the next tile (three vector instructions per MFMA), so the
+  // accumulators of one tile wait in Sp; the first tile's predecessor is a dummy with no
+  // entry to store.
+  f32x4 Sp[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) Sp[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t sp = -1;  // entry of this lane's previous tile (-1: none)
+  auto reduce_prev = [&]() {
+    const float acc = relu_weighted_sum(Sp, wgt);
+    if (g == 0 && sp >= 0 && sp < Eq) scw[sp] = acc;
+  };
   for (int c = 0; c < nchunks; ++c) {
     const int cur = (c & 1) * (kNE * kRowB);
     const char* buf = kbuf + cur;
@@ -350,12 +362,19 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
         for (int mt = 0; mt < 4; ++mt)
           S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv[et & 1][ks], S[mt], 0, 0, 0);
       }
+      reduce_prev();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector ALU instructions
+      }
       __builtin_amdgcn_sched_barrier(0);
-      const float acc = relu_weighted_sum(S, wgt);
-      const int64_t s = (int64_t)c * kNE + 16 * et + jj;
-      if (g == 0 && s < Eq) scw[s] = acc;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Sp[mt] = S[mt];
+      sp = (int64_t)c * kNE + 16 * et + jj;
     }
   }
+  reduce_prev();  // the last tile
 
   // per-query top-k by its own wave (no workgroup barrier needed from here on)
   if (qvalid) {
