@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the reported extra rows (HCA prefill at 64K, the 128-query point)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -220,6 +222,10 @@ def main():
                  "indexer_topk": round(st[2].elapsed_time(ev_extra[0]), 4),
                  "sparse_mqa": round(ev_extra[0].elapsed_time(ev_extra[1]), 4)}
 
+    extra = None
+    if not args.no_extra:
+        extra = point_timing(B, ops, stream, qI4, KI, wI3, q4, kv, loc3, T["gamma"], cfg)
+
     counts = costmodel.csa_prefill_counts(n, m, k, w, n_h, c, n_hI, cI)
     attn_tflops = counts["attn_flops"] / (attn_ms * 1e-3) / 1e12
     tokens_per_s = n / (ms_step * 1e-3)
@@ -258,9 +264,125 @@ def main():
         torch.cuda.empty_cache()
         line["decode"] = {name: decode_timing(name, stream) for name in
                           ("csa_decode_flash_128k", "csa_decode_pro_1m")}
+    if extra is not None:
+        if args.no_decode:
+            del T, kv, KI, idx, cnt, out, ws_i, ws_a, q4, qI4, wI3, loc3
+            torch.cuda.empty_cache()
+        line["extra"] = {"prefill_t0_896_T128": extra, "hca_prefill_n65536": hca_timing(stream)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def point_timing(B, ops, stream, qI4, KI, wI3, q4, kv, loc3, gamma, cfg, rounds=20, warmup=3):
+    """The pages' own prefill point: 128 queries at positions 896 .. 1023 with the C2
+    shapes (at most 256 visible entries, so the top-k keeps all of them), indexer top-k and
+    sparse attention timed separately (HIP events, mean over the rounds).  Context only: the
+    pages measured it on other hardware."""
+    import torch
+    from compressed_sparse_attention_v4a_amd import costmodel
+    t0, T = 896, 128
+    c, n_h, n_hI, cI, m, k, w = (cfg[x] for x in ("c", "n_h", "n_hI", "cI", "m", "k", "w"))
+    n = q4.shape[1]
+    E = KI.shape[1]
+    dev = q4.device
+    idx = torch.empty(1, T, k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, T, dtype=torch.int32, device=dev)
+    out = torch.empty(1, T, n_h, c, dtype=torch.bfloat16, device=dev)
+    wsi_b = B.v4a_indexer_topk_workspace(1, T, t0, n_hI, cI, m, k, B.BF16)
+    wsi = ops.workspace(wsi_b, dev)
+    wsa_b = B.v4a_sparse_mqa_prefill_workspace(1, t0, T, 0, n, n_h, c, k, w, B.BF16)
+    wsa = ops.workspace(wsa_b, dev)
+    qI = qI4[:, t0:t0 + T]
+    wI = wI3[:, t0:t0 + T]
+    q = q4[:, t0:t0 + T]
+
+    def indexer():
+        B.v4a_indexer_topk(qI, None, KI, None, B.BF16, wI, 1, T, t0, n_hI, cI, m, k, E, idx, cnt,
+                           None, wsi, wsi_b, stream)
+
+    def attn():
+        B.v4a_sparse_mqa_prefill(q, kv, loc3, 0, n, idx, cnt, None, gamma, gamma, 1e-6, 64,
+                                 10000.0, 0.0, 1, t0, T, n_h, c, k, w, E, out, B.BF16, wsa, wsa_b,
+                                 stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(rounds):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / rounds * 1e3
+    log(f"prefill point t0={t0} T={T}")
+    us_i = timed(indexer)
+    us_a = timed(attn)
+    counts = costmodel.csa_prefill_counts(T, m, k, w, n_h, c, n_hI, cI, t0=t0)
+    return {"t0": t0, "T": T, "indexer_topk_us": round(us_i, 2), "sparse_mqa_us": round(us_a, 2),
+            "index_gflop": round(counts["index_flops"] / 1e9, 3),
+            "attn_gflop": round(counts["attn_flops"] / 1e9, 3)}
+
+
+def hca_timing(stream, rounds=5, warmup=2):
+    """HCA prefill over n = 65536 (V4-Flash shapes): the compressor (m' = 128) and the dense
+    HCA attention, timed separately (HIP events, mean over the rounds).  C, Z, B and the
+    window rows come from the seeded workload generator; q (4 GiB) is drawn on the device
+    from torch's seeded normal generator with the same distribution, N(0, 1/512)."""
+    import math
+    import torch
+    import synth
+    from compressed_sparse_attention_v4a_amd import binding as B
+    from compressed_sparse_attention_v4a_amd import costmodel, ops
+    cfg = synth.configs.workload("hca_prefill_flash_64k")
+    n, c, n_h, mp, w = (cfg[x] for x in ("n", "c", "n_h", "m_prime", "w"))
+    log(f"generating inputs ({cfg['name']})")
+    d = synth.configs.gen_hca_prefill(cfg, q_rows=(0, 1))
+    dev = "cuda"
+    up = lambda x: ops.upload(x, None, dev)
+    C, Z, Bb, loc, g = up(d["C"]), up(d["Z"]), up(d["B"]), up(d["local"]), up(d["gamma"])
+    E = n // mp
+    kv = torch.empty(1, E, c, dtype=torch.bfloat16, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x5EED0000 + 3 * 256 + 7)
+    q = (torch.randn(1, n, n_h, c, device=dev, generator=gen) / math.sqrt(c)).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws_b = B.v4a_hca_attn_workspace(1, 0, n, 0, n, n_h, c, mp, w, B.BF16)
+    ws = ops.workspace(ws_b, dev)
+    loc3 = loc.view(1, n, c)
+
+    def compress():
+        B.v4a_compress(C.view(1, n, c), Z.view(1, n, c), B.BF16, Bb, 1, n, 0, 0, n, c, mp, 0, g,
+                       1e-6, 64, 10000.0, kv, None, B.BF16, E, stream)
+
+    def attn():
+        B.v4a_hca_attn(q, kv, loc3, 0, n, None, g, g, 1e-6, 64, 10000.0, 0.0, 1, 0, n, n_h, c, mp,
+                       w, E, out, B.BF16, ws, ws_b, stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(rounds):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / rounds
+    log("timing the HCA prefill")
+    ms_c = timed(compress)
+    ms_a = timed(attn)
+    counts = costmodel.hca_prefill_counts(n, mp, w, n_h, c)
+    tf = counts["attn_flops"] / (ms_a * 1e-3) / 1e12
+    gbs = counts["compress_bytes"] / (ms_c * 1e-3) / 1e9
+    res = {"n": n, "m_prime": mp, "w": w, "n_h": n_h, "compress_ms": round(ms_c, 4),
+           "attn_ms": round(ms_a, 4), "tokens_per_s": round(n / ((ms_c + ms_a) * 1e-3), 1),
+           "attn_tflops": round(tf, 2), "attn_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "compress_gb_per_s": round(gbs, 1), "compress_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del q, out, ws, kv
+    torch.cuda.empty_cache()
+    return res
 
 
 def _quant_rows(x, dt):
