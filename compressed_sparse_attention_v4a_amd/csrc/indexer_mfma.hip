@@ -64,7 +64,8 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x4 (&S)[4], const fl
 // (wave AND / OR) are skipped; the others count runs of equal digits before touching the
 // histogram (the wave's own, ordered by the wave's in-order LDS operations) and find the
 // bin with a DPP prefix sum.  Emission places each lane's run with one packed prefix sum
-// of (keys > kth, keys == kth).  Same result as wave_topk.
+// of (keys > kth, keys == kth).  The passes stop once the k-th key's bin holds exactly the
+// keys still needed.  Same result as wave_topk.
 template <int PER>
 __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int32_t* oidx,
                               float* osc, int32_t* ocnt) {
@@ -124,12 +125,13 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
       const uint32_t mine = cs[0] + cs[1] + cs[2] + cs[3];
       uint32_t above = (uint32_t)wave_incl_sum((int)mine) - mine;
       int hit_bin = -1;
-      uint32_t hit_above = 0u;
+      uint32_t hit_above = 0u, hit_count = 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
           hit_bin = 255 - 4 * lane - j;
           hit_above = above;
+          hit_count = cs[j];
         }
         above += cs[j];
       }
@@ -138,18 +140,24 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
       prefix |= (uint32_t)__builtin_amdgcn_readlane(hit_bin, src) << shift;
       pmask |= 255u << shift;
       rem -= __builtin_amdgcn_readlane((int)hit_above, src);
+      const bool whole = (uint32_t)__builtin_amdgcn_readlane((int)hit_count, src) == (uint32_t)rem;
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int j = 0; j < 4; ++j) hist[255 - 4 * lane - j] = 0u;  // the bins this lane read
+      // the bin holds exactly the keys still needed: all of them are selected, whatever
+      // their lower digits (the same set the remaining passes would find)
+      if (whole) break;
     }
+    // selection on the resolved digits: keys above the prefix, then the first rem keys equal
+    // to it in index order (all of them when the passes stopped early)
     const uint32_t kth = prefix;
     const int need_eq = rem;
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const bool v = j < per && base + j < E;
-      ngt += (v && key[j] > kth) ? 1 : 0;
-      neq += (v && key[j] == kth) ? 1 : 0;
+      ngt += (v && (key[j] & pmask) > kth) ? 1 : 0;
+      neq += (v && (key[j] & pmask) == kth) ? 1 : 0;
     }
     const int packed = ngt | (neq << 16);  // E <= 65535
     const int before = wave_incl_sum(packed) - packed;
@@ -158,9 +166,9 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const bool v = j < per && base + j < E;
-      const bool gt = v && key[j] > kth;
-      const bool eq = v && key[j] == kth && eq_seen < need_eq;
-      eq_seen += (v && key[j] == kth) ? 1 : 0;
+      const bool gt = v && (key[j] & pmask) > kth;
+      const bool eq = v && (key[j] & pmask) == kth && eq_seen < need_eq;
+      eq_seen += (v && (key[j] & pmask) == kth) ? 1 : 0;
       if (gt || eq) {
         oidx[pos] = base + j;
         if (osc) osc[pos] = key_score(key[j]);

@@ -11,8 +11,9 @@
 namespace v4a {
 
 struct Selection {
-  uint32_t kth;  // key of the K-th largest element
+  uint32_t kth;  // key of the K-th largest element (its bits under mask)
   int need_eq;   // how many elements equal to kth are taken (lowest indices first)
+  uint32_t mask = 0xFFFFFFFFu;  // key bits the comparisons with kth use
 };
 
 // Exclusive prefix count of `flag` over the block in thread order; *total gets
@@ -233,12 +234,13 @@ __device__ Selection reg_radix_select(const uint32_t (&key)[PER], int N, int K, 
     const uint32_t mine = cs[0] + cs[1] + cs[2] + cs[3];
     uint32_t above = (uint32_t)wave_incl_sum((int)mine) - mine;  // elements in bins > 255 - 4 l
     int hit_bin = -1;
-    uint32_t hit_above = 0u;
+    uint32_t hit_above = 0u, hit_count = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
         hit_bin = 255 - 4 * lane - j;
         hit_above = above;
+        hit_count = cs[j];
       }
       above += cs[j];
     }
@@ -249,12 +251,17 @@ __device__ Selection reg_radix_select(const uint32_t (&key)[PER], int N, int K, 
     rem -= __builtin_amdgcn_readlane((int)hit_above, src);
     prefix |= d << shift;
     pmask |= 255u << shift;
+    // a full selection stops once the bin holds exactly the keys still needed: all of them
+    // are taken whatever their lower digits (the set the remaining passes would give)
+    const bool whole =
+        last_shift == 0 && (uint32_t)__builtin_amdgcn_readlane((int)hit_count, src) == (uint32_t)rem;
     uint32_t* h2 = hist + 256 * ((pass + 2) % 3);
     for (int i = threadIdx.x; i < 256; i += blockDim.x) h2[i] = 0u;
     ++pass;
+    if (whole) break;
   }
   __syncthreads();  // the last histogram is read before the caller reuses LDS
-  return {prefix, rem};
+  return {prefix, rem, pmask};
 }
 
 // Selected elements before thread t and their placement: the selection is every key > kth
@@ -270,8 +277,8 @@ __device__ void reg_select_emit_slot(const uint32_t (&key)[PER], int N, Selectio
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if (j < per && base + j < N) {
-      ngt += key[j] > sel.kth ? 1 : 0;
-      neq += key[j] == sel.kth ? 1 : 0;
+      ngt += (key[j] & sel.mask) > sel.kth ? 1 : 0;
+      neq += (key[j] & sel.mask) == sel.kth ? 1 : 0;
     }
   }
   int tot, gt_before, eq_before;
@@ -289,9 +296,10 @@ __device__ void reg_select_emit_slot(const uint32_t (&key)[PER], int N, Selectio
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if (j < per && base + j < N) {
-      const bool gt = key[j] > sel.kth;
-      const bool eq = key[j] == sel.kth && eq_seen < sel.need_eq;
-      eq_seen += key[j] == sel.kth ? 1 : 0;
+      const uint32_t kk = key[j] & sel.mask;
+      const bool gt = kk > sel.kth;
+      const bool eq = kk == sel.kth && eq_seen < sel.need_eq;
+      eq_seen += kk == sel.kth ? 1 : 0;
       if (gt || eq) emit(pos++, j, key[j]);
     }
   }
