@@ -49,7 +49,8 @@ def compress(C, Z, B_, *, c, m, overlap, in_dt, out_dt="bf16", t0=0, T=None, tok
         C, Z = C.unsqueeze(0), Z.unsqueeze(0)
     batch, n_buf = C.shape[0], C.shape[1]
     T = (n_buf + tok_base - t0) if T is None else T
-    E_cap = (t0 + T) // m if E_cap is None else E_cap
+    if E_cap is None:  # rows per sequence of the output cache
+        E_cap = out.shape[1] if out is not None else (t0 + T) // m
     dev = C.device
     if out is None:
         if out_dt in ("f32", "bf16"):

@@ -334,6 +334,7 @@ def _small_prefill(seed, n, n_h, c, k, w, t0=0, sink=False, rd=64, norm=True):
 @pytest.mark.parametrize("n,n_h,c,k,w,t0,sink,rd", [
     (300, 16, 512, 64, 128, 0, True, 64),
     (257, 64, 512, 512, 128, 896, False, 64),    # the pages' 128-token chunk at start 896, ragged
+    (257, 64, 512, 512, 128, 896, True, 64),     # the same on the matrix-core kernel with a sink
     (200, 8, 128, 24, 16, 5000, True, 0),
 ])
 def test_sparse_mqa_prefill_bf16(n, n_h, c, k, w, t0, sink, rd):
@@ -440,7 +441,8 @@ def test_csa_prefill_flash_8k_sampled(csa8k):
 # ---------------------------------------------------------------- HCA attention --- #
 
 @pytest.mark.parametrize("n,n_h,c,mp,w,t0,sink", [(700, 16, 512, 128, 128, 0, True),
-                                                  (300, 8, 256, 16, 32, 1000, False)])
+                                                  (300, 8, 256, 16, 32, 1000, False),
+                                                  (300, 64, 512, 128, 128, 200, True)])
 def test_hca_attn_bf16(n, n_h, c, mp, w, t0, sink):
     rng = np.random.default_rng(n)
     E = (t0 + n) // mp
@@ -593,11 +595,14 @@ def _run_decode_step(cfg, d, num_splits=0):
 
 @pytest.mark.parametrize("name,batch,L", [("csa_decode_flash_128k", 4, 8192),
                                           ("csa_decode_pro_1m", 2, 16384),
-                                          ("csa_decode_flash_128k", 3, 8190)])
+                                          ("csa_decode_flash_128k", 3, 8190),
+                                          ("csa_decode_flash_128k", 2, 131072)])
 def test_decode_step_matches_separate_calls(name, batch, L):
     """v4a_csa_decode_step (one call, fused front launch) equals the four separate calls bit
     for bit -- caches, ring, selection, scores and output -- and passes the oracle checks.
-    L = 8190 puts the new token mid-block: nothing is emitted."""
+    L = 8190 puts the new token mid-block: nothing is emitted.  L = 131072 (E = 32768) is the
+    128K workload's shape, where the selection takes the threshold-filter path that the
+    timed decode call uses."""
     cfg = synth.configs.workload(name, batch=batch, L=L)
     cfg["id"] = 11
     d = synth.configs.gen_csa_decode(cfg)
@@ -656,3 +661,143 @@ def test_decode_split_merge(splits):
     log(f"decode split-merge splits={splits}")
     r = _run_decode(cfg, d, num_splits=splits)
     _check_decode(cfg, d, r, [0, 1], sink=d["sink"])
+
+
+# ------------------------------------------------- decode at the first positions --- #
+
+_NAN_BF16 = np.uint16(0x7FC0)
+
+
+def _early_state(t, batch=2, n_h=64, c=512, n_hI=64, cI=128, m=4, k=512, w=128, seed=0):
+    """Decode state of `batch` sequences whose new token is at position t (any t >= 0):
+    entries 0 .. floor(t/m)-1 in both caches (fp8 index keys), the ring holding tokens
+    max(0, t-w) .. t-1, every other ring slot and cache row NaN (a read of a token or entry
+    that does not exist poisons the output), and the raw tail rows of the block that t
+    completes (when it completes one)."""
+    rng = np.random.default_rng(seed + t)
+    sc = 1 / math.sqrt(c)
+    E_before, i = t // m, t // m
+    E_cap = E_before + 2
+    kv = np.full((batch, E_cap, c), np.nan)
+    kv[:, :E_before] = rng.standard_normal((batch, E_before, c))
+    KI = rng.standard_normal((batch, E_cap, cI))
+    ring = np.full((batch, w, c), np.nan)
+    for j in range(max(0, t - w), t):
+        ring[:, j % w] = sc * rng.standard_normal((batch, c))
+    base = max(0, m * (i - 1))
+    n_buf = m * (i + 1) - base
+    d = dict(t=t, tail_base=base)
+    d["kv_comp"] = synth.formats.bf16_bits(kv)
+    d["KI"], d["KI_scale"] = synth.formats.fp8_e4m3_rows(KI)
+    d["qI"], d["qI_scale"] = synth.formats.fp8_e4m3_rows(rng.standard_normal((batch, n_hI, cI)))
+    d["ring"] = synth.formats.bf16_bits(ring)
+    d["kv_new"] = synth.formats.bf16_bits(sc * rng.standard_normal((batch, c)))
+    d["C"] = synth.formats.bf16_bits(sc * rng.standard_normal((batch, n_buf, 2 * c)))
+    d["Z"] = synth.formats.bf16_bits(rng.standard_normal((batch, n_buf, 2 * c)))
+    d["CI"] = synth.formats.bf16_bits(rng.standard_normal((batch, n_buf, 2 * cI)))
+    d["ZI"] = synth.formats.bf16_bits(rng.standard_normal((batch, n_buf, 2 * cI)))
+    d["B"] = (math.sqrt(0.1) * rng.standard_normal((2 * m, c))).astype(np.float32)
+    d["BI"] = (math.sqrt(0.1) * rng.standard_normal((2 * m, cI))).astype(np.float32)
+    d["q"] = synth.formats.bf16_bits(sc * rng.standard_normal((batch, n_h, c)))
+    d["wI"] = rng.random((batch, n_hI)).astype(np.float32)
+    d["gamma"] = np.ones(c, np.float32)
+    d["gammaI"] = np.ones(cI, np.float32)
+    cfg = dict(c=c, cI=cI, m=m, k=k, w=w, n_h=n_h, idt="fp8", rope_dims=64)
+    return cfg, d
+
+
+@pytest.mark.parametrize("t", [0, 2, 3, 7, 70, 2047, 2100])
+def test_decode_step_early_positions(t):
+    """The decode step at the first positions of a sequence: no entry yet (t < 3), the first
+    entry emitted without a preceding block (t = 3), a partly filled ring (t < 127), fewer
+    visible entries than k (t < 2051), E = k exactly (t = 2047) and E > k without emission
+    (t = 2100).  One call equals the separate calls bit for bit and the oracle's decode step."""
+    cfg, d = _early_state(t)
+    m, k, w, c, cI = cfg["m"], cfg["k"], cfg["w"], cfg["c"], cfg["cI"]
+    log(f"decode step at early position t={t}")
+    ref = _run_decode(cfg, d)
+    got = _run_decode_step(cfg, d)
+    for key in ("kv", "KI", "KIs", "ring", "idx", "cnt", "sc", "out"):
+        a, b = ref[key].reshape(-1), got[key].reshape(-1)
+        a = a.view(torch.uint8) if a.dtype == torch.bfloat16 else a
+        b = b.view(torch.uint8) if b.dtype == torch.bfloat16 else b
+        assert torch.equal(a, b) or (a.dtype.is_floating_point and
+                                     torch.equal(torch.nan_to_num(a, 7.0), torch.nan_to_num(b, 7.0))), key
+    E = (t + 1) // m
+    emitted = (t + 1) % m == 0
+    for b in range(2):
+        if emitted:
+            tail = dict(tok_base=d["tail_base"], i_begin=E - 1, i_end=E, m=m, overlap=True)
+            ref_kv = oracle.compress(f64(d["C"][b], "bf16"), f64(d["Z"][b], "bf16"), d["B"], c=c,
+                                     gamma=d["gamma"], rope_dims=64, **tail)[0]
+            assert_bf16_close(decode_stored(got["kv"][b, E - 1], "bf16"), ref_kv,
+                              what=f"t={t} seq {b} emitted entry")
+            ref_ki = oracle.compress(f64(d["CI"][b], "bf16"), f64(d["ZI"][b], "bf16"), d["BI"],
+                                     c=cI, gamma=d["gammaI"], **tail)[0]
+            check_quantised(got["KI"][b, E - 1:E], got["KIs"][b, E - 1:E], ref_ki[None], "fp8")
+        cnt = int(got["cnt"][b])
+        assert cnt == min(k, E), f"t={t} seq {b}: count {cnt}"
+        idx = got["idx"][b].cpu().numpy()
+        assert np.all(idx[cnt:] == -1)
+        if E > 0:
+            KId = decode_stored(got["KI"][b, :E], "fp8", got["KIs"][b, :E])
+            qId = oracle.decode(d["qI"][b], "fp8", d["qI_scale"][b])
+            ref_s = oracle.index_scores(qId[None], KId, d["wI"][b][None].astype(np.float64), t0=t,
+                                        m=m, ld=E)
+            check_topk(idx[None], got["cnt"][b:b + 1].cpu().numpy(), ref_s, t0=t, m=m, k=k,
+                       gpu_scores=got["sc"][b:b + 1].cpu().numpy(), what=f"t={t} seq {b}")
+        ringd = decode_stored(got["ring"][b], "bf16")
+        assert np.array_equal(ringd[t % w], f64(d["kv_new"][b], "bf16")), "ring insert"
+        kvd = decode_stored(got["kv"][b][got["idx"][b, :cnt].long()], "bf16")
+        ref_o = oracle.attend_decode(f64(d["q"][b], "bf16"), kvd, ringd,
+                                     np.arange(cnt, dtype=np.int32), cnt, t=t, w=w,
+                                     q_gamma=d["gamma"], kv_gamma=d["gamma"], q_norm=True,
+                                     kv_norm=True, rope_dims=64)
+        o = decode_stored(got["out"][b], "bf16")
+        assert np.all(np.isfinite(o)), f"t={t} seq {b}: a nonexistent token or entry was read"
+        assert_attn_close(o, ref_o, atol=ATOL_BF16, rel_rms=REL_RMS_BF16, what=f"t={t} seq {b}")
+
+
+# ------------------------------------------------------------------ determinism --- #
+
+def _bits(x):
+    return x.view(torch.uint8) if x.dtype == torch.bfloat16 else x
+
+
+def test_prefill_chain_bitwise_reproducible(csa8k):
+    """The 8K CSA prefill chain (both compressors, indexer top-k, attention) gives the same
+    bits when run twice; so does the attention with query RMSNorm weights of 4, whose
+    overflowing items are listed in arbitrary order for the exact recomputation."""
+    cfg, d = csa8k
+    log("determinism: csa prefill n=8192 twice")
+    g, gI = up(d["gamma"]), up(d["gammaI"])
+    args = [up(x) for x in (d["C"], d["Z"], d["B"], d["CI"], d["ZI"], d["BI"], d["qI"], d["wI"],
+                            d["q"], d["local"])]
+    C, Z, B_, CI, ZI, BI, qI, wI, q, local = args
+
+    def chain(qg):
+        kv, _ = ops.compress(C, Z, B_, c=512, m=4, overlap=True, in_dt="bf16", out_dt="bf16",
+                             gamma=g, rope_dims=64)
+        KI, _ = ops.compress(CI, ZI, BI, c=128, m=4, overlap=True, in_dt="bf16", out_dt="bf16",
+                             gamma=gI)
+        idx, cnt, sc = ops.indexer_topk(qI, KI[0], wI, dt="bf16", m=4, k=512)
+        out = ops.sparse_mqa_prefill(q, kv[0], local, idx[0], cnt[0], t0=0, w=128, dt="bf16",
+                                     q_gamma=qg, kv_gamma=g, rope_dims=64)
+        torch.cuda.synchronize()
+        return [kv, KI, idx, cnt, sc, out]
+
+    for qg in (g, up(np.full(512, 4.0, np.float32))):
+        a, b = chain(qg), chain(qg)
+        for x, y, nm in zip(a, b, ("kv", "KI", "idx", "cnt", "score", "out")):
+            assert torch.equal(_bits(x), _bits(y)), nm
+
+
+def test_decode_step_bitwise_reproducible():
+    """One decode step of the 128K workload shape (batch 2) run twice from the same state."""
+    cfg = synth.configs.workload("csa_decode_flash_128k", batch=2, L=131072)
+    cfg["id"] = 12
+    d = synth.configs.gen_csa_decode(cfg)
+    log("determinism: decode step B=2 L=131072 twice")
+    a, b = _run_decode_step(cfg, d), _run_decode_step(cfg, d)
+    for key in ("kv", "KI", "KIs", "ring", "idx", "cnt", "sc", "out"):
+        assert torch.equal(_bits(a[key]), _bits(b[key])), key

@@ -227,3 +227,84 @@ def test_scale_and_query_norm_invariance():
     c1 = oracle.attend_csa(2.0 * P["q"], P["kv"], P["local"], P["idx"], P["cnt"], scale=0.25, **kw)
     c2 = oracle.attend_csa(P["q"], P["kv"], P["local"], P["idx"], P["cnt"], scale=0.5, **kw)
     assert np.allclose(c1, c2, rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------ RoPE positions --- #
+
+def _rot_complex(x, pos, rd, base=10000.0):
+    """Partial RoPE written in complex form: the pair (x[c-rd+2i], x[c-rd+2i+1]) is the
+    complex number a + ib, multiplied by exp(i * pos * base^(-2i/rd))."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    c = y.shape[-1]
+    z = y[..., c - rd::2] + 1j * y[..., c - rd + 1::2]
+    z = z * np.exp(1j * pos * base ** (-2.0 * np.arange(rd // 2) / rd))
+    y[..., c - rd::2], y[..., c - rd + 1::2] = z.real, z.imag
+    return y
+
+
+def _norm(x):
+    return x / np.sqrt(np.mean(x ** 2, axis=-1, keepdims=True))
+
+
+def _attention_by_positions(q_t, t, comp_rows, local_rows, local_pos, sink, rd, c):
+    """Dense softmax over [compressed rows as stored || window rows rotated at their own
+    position], query rotated at t, output rotated back at t ("CSA And HCA" section 5.2)."""
+    cands = np.concatenate([comp_rows.reshape(-1, c),
+                            _rot_complex(_norm(local_rows), np.asarray(local_pos)[:, None], rd)])
+    out = np.empty_like(q_t)
+    for h in range(q_t.shape[0]):
+        qh = _rot_complex(_norm(q_t[h]), t, rd)
+        z = cands @ qh / math.sqrt(c)
+        mx = max(z.max(), sink[h]) if sink is not None else z.max()
+        e = np.exp(z - mx)
+        den = e.sum() + (math.exp(sink[h] - mx) if sink is not None else 0.0)
+        out[h] = _rot_complex((e / den) @ cands, -t, rd)
+    return out
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "decode"])
+def test_rope_positions_in_attention(kind):
+    """Several candidates, w >= 3, RoPE on: the query turns at t, window row j at j, stored
+    compressed rows are not turned again, and the output turns back at t.  Rotating a
+    window row at t, or leaving the query unrotated, changes the result (checked)."""
+    c, rd, n_h, m, w, k, n = 16, 8, 2, 4, 4, 3, 28
+    rng = np.random.default_rng(123)
+    q = rng.standard_normal((n, n_h, c))
+    local = rng.standard_normal((n, c))
+    E = n // m
+    # stored entries: already normalised and turned at their anchor m*s
+    kv = _rot_complex(_norm(rng.standard_normal((E, c))), (m * np.arange(E))[:, None], rd)
+    sink = np.array([0.4, -0.7])
+    idx = -np.ones((n, k), np.int32)
+    cnt = np.zeros(n, np.int32)
+    for t in range(n):
+        e = min(k, (t + 1) // m)
+        idx[t, :e] = np.sort(rng.choice((t + 1) // m, e, replace=False)) if e else []
+        cnt[t] = e
+    kw = dict(q_norm=True, kv_norm=True, eps=0.0, rope_dims=rd, sink=sink)
+    if kind == "csa":
+        got = oracle.attend_csa(q, kv, local, idx, cnt, loc_base=0, t0=0, w=w, **kw)
+    elif kind == "hca":
+        got = oracle.attend_hca(q, kv, local, loc_base=0, t0=0, m_prime=m, w=w, **kw)
+    else:
+        got = np.empty((n, n_h, c))
+        for t in range(n):
+            ring = np.full((w, c), np.nan)
+            for j in range(max(0, t - w + 1), t + 1):
+                ring[j % w] = local[j]
+            got[t] = oracle.attend_decode(q[t], kv, ring, idx[t], int(cnt[t]), t=t, w=w, **kw)
+    sens_win = sens_q = 0.0
+    for t in range(n):
+        lo = max(0, t - w + 1)
+        pos = np.arange(lo, t + 1)
+        comp = kv[: (t + 1) // m] if kind == "hca" else kv[idx[t, :cnt[t]]]
+        ref = _attention_by_positions(q[t], t, comp, local[lo:t + 1], pos, sink, rd, c)
+        assert np.allclose(got[t], ref, rtol=1e-12, atol=1e-13), (kind, t)
+        # the two plausible mistakes move the result far beyond that tolerance
+        wrong_win = _attention_by_positions(q[t], t, comp, local[lo:t + 1], np.full(pos.size, t),
+                                            sink, rd, c)
+        sens_win = max(sens_win, np.abs(wrong_win - ref).max())
+        wrong_q = _attention_by_positions(_rot_complex(q[t], -t, rd), t, comp, local[lo:t + 1],
+                                          pos, sink, rd, c)
+        sens_q = max(sens_q, np.abs(wrong_q - ref).max())
+    assert sens_win > 1e-3 and sens_q > 1e-3

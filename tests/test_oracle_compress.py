@@ -201,3 +201,44 @@ def test_norm_and_rope_epilogue_order():
         # pair 0 turns by exactly m*i radians (theta_0 = 1)
         ang = math.atan2(pr[0, 1], pr[0, 0]) - math.atan2(py[0, 1], py[0, 0])
         assert math.remainder(ang - m * i, 2 * math.pi) == pytest.approx(0.0, abs=1e-12)
+
+
+@pytest.mark.parametrize("overlap,m", [(True, 4), (False, 4), (False, 8)])
+def test_bias_rows_follow_position_in_block(overlap, m):
+    """Bias row j belongs to position j of its block ("CSA And HCA" section 2.1: B^a with
+    block i, B^b with block i-1; section 2.2: B with the one stream).  Zero gate logits and
+    one large bias per channel make the softmax one-hot, so channel ch of entry i must equal
+    the value row m*i + tgt[ch] (stream a) or m*(i-1) + tgt[ch] (stream b); a reversed or
+    shifted row order picks another row."""
+    c, n = 8, 6 * m
+    rng = np.random.default_rng(31 + m + overlap)
+    width = 2 * c if overlap else c
+    C = rng.standard_normal((n, width))
+    Z = np.zeros((n, width))
+    tgt = rng.integers(0, m, c)
+    if m == 4:
+        tgt[:4] = [0, 1, 2, 3]  # every row of the block is somebody's target
+    use_b = np.array([overlap and ch % 2 == 1 for ch in range(c)])
+    B = np.zeros(((2 if overlap else 1) * m, c))
+    for ch in range(c):
+        B[(m if use_b[ch] else 0) + tgt[ch], ch] = 60.0
+    out = oracle.compress(C, Z, B, tok_base=0, i_begin=0, i_end=n // m, c=c, m=m,
+                          overlap=overlap)
+    for i in range(n // m):
+        for ch in range(c):
+            if use_b[ch]:
+                if i == 0:  # no preceding block: plain mean of the a-stream rows
+                    expect = C[0:m, ch].mean()
+                else:
+                    expect = C[m * (i - 1) + tgt[ch], c + ch]
+            else:
+                expect = C[m * i + tgt[ch], ch]
+            assert out[i, ch] == pytest.approx(expect, rel=1e-12, abs=1e-12), (i, ch)
+    # sensitivity: the bias rows reversed inside the block select other rows
+    Brev = B.copy()
+    Brev[:m] = B[:m][::-1]
+    if overlap:
+        Brev[m:] = B[m:][::-1]
+    out_rev = oracle.compress(C, Z, Brev, tok_base=0, i_begin=0, i_end=n // m, c=c, m=m,
+                              overlap=overlap)
+    assert np.abs(out_rev - out).max() > 1e-2
