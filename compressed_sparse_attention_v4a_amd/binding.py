@@ -63,6 +63,7 @@ def lib() -> ct.CDLL:
         L.v4a_csa_decode_step_workspace.restype = sz
         L.v4a_csa_decode_step_workspace.argtypes = [vp]
         L.v4a_csa_decode_step.argtypes = [vp, vp, sz, vp]
+        L.v4a_csa_decode_step_noalloc.argtypes = [vp, vp]
         _check_step_layout(L)
         _lib = L
     return _lib
@@ -112,6 +113,14 @@ def v4a_csa_decode_step_workspace(step: DecodeStep) -> int:
 def v4a_csa_decode_step(step: DecodeStep, ws, ws_bytes, stream=None):
     _check("v4a_csa_decode_step", lib().v4a_csa_decode_step(
         ct.c_void_p(ct.addressof(step)), _p(ws), ws_bytes, _s(stream)))
+
+
+def v4a_csa_decode_step_noalloc(step: DecodeStep, stream=None):
+    _check("v4a_csa_decode_step_noalloc", lib().v4a_csa_decode_step_noalloc(
+        ct.c_void_p(ct.addressof(step)), _s(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # V4A_NOALLOC_SCRATCH_BYTES
 
 
 def _p(t):

@@ -63,6 +63,8 @@ int check_attn_common(const void* q, const void* kv_comp, const void* out, int n
 }  // namespace
 
 namespace v4a {
+int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
 void rope_table(RopeTab& tab, int rope_dims, float rope_base) {
   for (int i = 0; i < kMaxRopeDims / 2; ++i)
     tab.inv_freq[i] = (2 * i < rope_dims) ? std::pow((double)rope_base, -2.0 * (double)i / (double)rope_dims)
@@ -370,6 +372,14 @@ size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d) {
 }
 
 int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream) {
+  return v4a::decode_step_run(d, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// The decode step with a given workspace (the caller's, or the fixed device scratch of
+// v4a_csa_decode_step_noalloc).
+int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream) {
   REQUIRE(d, V4A_EINVAL, "null step description");
   REQUIRE(d->t >= 0 && d->t < INT32_MAX, V4A_EINVAL, "t out of range");
   REQUIRE(d->num_splits >= 0 && d->num_splits <= 64, V4A_EINVAL, "num_splits must be in [0, 64]");
@@ -418,5 +428,3 @@ int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, voi
   if (e == hipSuccess) e = v4a::launch_attention(aa, ws_a, policy, s);
   return hip_status(e, "v4a_csa_decode_step");
 }
-
-}  // extern "C"

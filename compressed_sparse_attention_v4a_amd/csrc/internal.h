@@ -6,7 +6,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct v4a_decode_step;
+
 namespace v4a {
+
+// The whole decode step of v4a_csa_decode_step with the workspace `ws` (validation,
+// launches, error reporting).
+int decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream);
+// Sets the calling thread's v4a_last_error() message; returns code.
+int report_error(int code, const char* msg);
 
 enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
 

@@ -133,11 +133,12 @@ def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI,
                     qI_scale, wI, q, kv_ring, kv_new, index_dt, gamma=None, gammaI=None, sink=None,
                     q_gamma=None, kv_gamma=None, rope_dims=0, rope_dims_I=0, rope_base=10000.0,
                     eps=1e-6, scale=0.0, num_splits=0, out=None, with_scores=True, stream=None,
-                    ws=None):
+                    ws=None, noalloc=False):
     """One CSA decode step (tail compression of both instances, index top-k, ring insert and
     attention) through v4a_csa_decode_step.  C, Z: [batch][n_buf][2c] bf16; CI, ZI likewise
     with cI; qI [batch][n_hI][cI or cI/2]; q [batch][n_h][c].  Caches are updated in place.
-    Returns (out, idx, cnt, score)."""
+    noalloc=True calls v4a_csa_decode_step_noalloc (the library's fixed scratch, no
+    workspace).  Returns (out, idx, cnt, score)."""
     batch, n_h, c = q.shape
     n_hI = qI.shape[1]
     cI = CI.shape[2] // 2
@@ -154,6 +155,9 @@ def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI,
         BI=BI, gammaI=gammaI, kv_comp=kv_comp, KI=KI, KI_scale=KI_scale, qI=qI,
         qI_scale=qI_scale, wI=wI, q=q, sink=sink, q_gamma=q_gamma, kv_gamma=kv_gamma,
         kv_ring=kv_ring, kv_new=kv_new, topk_idx=idx, topk_cnt=cnt, topk_score=sc, out=out)
+    if noalloc:
+        B.v4a_csa_decode_step_noalloc(step, stream)
+        return out, idx, cnt, sc
     nbytes = B.v4a_csa_decode_step_workspace(step)
     if ws is None or ws.numel() < nbytes:
         ws = workspace(nbytes, dev)

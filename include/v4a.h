@@ -10,7 +10,8 @@
  *     torch CUDA tensors); all are row-major and densely packed as stated.
  *   - The caller allocates and owns every buffer, including workspaces.  The
  *     library never allocates device memory, never frees, and keeps no pointer
- *     after a call returns.  Buffers must stay alive until the work queued on
+ *     after a call returns (the one exception is the fixed scratch array of
+ *     v4a_csa_decode_step_noalloc, part of the loaded library itself).  Buffers must stay alive until the work queued on
  *     `stream` completes.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Calls are asynchronous: they validate arguments on the host, enqueue
@@ -307,6 +308,24 @@ typedef struct v4a_decode_step {
 V4A_API int v4a_decode_step_layout(size_t* off, int n, size_t* size);
 V4A_API size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d);
 V4A_API int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * v4a_csa_decode_step_noalloc -- v4a_csa_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid allocation).  Same description `d`, same results bit for bit, same
+ * errors; the workspace is a fixed device array inside the library of
+ * V4A_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held until the process
+ * ends.  The call allocates and frees nothing.
+ *   - V4A_ENOSPC (with a message naming both sizes) when
+ *     v4a_csa_decode_step_workspace(d) exceeds the array.  64 MiB covers batch 64 at
+ *     128K context with the V4-Flash shapes (about 32 MiB at batch 32) and batch 4 at
+ *     1M context with the V4-Pro shapes (about 21 MiB).
+ *   - Every call on one GPU uses that GPU's array, which keeps the last call's
+ *     contents (nothing in it needs clearing between calls).  Calls that overlap in
+ *     time on one GPU (several streams or threads) race on it: serialise them.
+ */
+#define V4A_NOALLOC_SCRATCH_BYTES (64u << 20)
+V4A_API int v4a_csa_decode_step_noalloc(const v4a_decode_step* d, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (v4a_\w+)", out))
@@ -200,3 +200,25 @@ def test_decode_step_layout_and_validation(lib):
     assert run(step(), ws_bytes=need - 1) == ENOSPC
     assert run(step(), ws=Fake(4096 + 64)) == EINVAL    # workspace alignment
     assert lib.v4a_csa_decode_step(None, ct.c_void_p(4096), 1 << 30, None) == EINVAL
+
+
+def test_decode_step_noalloc_validation(lib):
+    """The no-allocation decode step rejects a step whose scratch need exceeds its fixed
+    64 MiB array (batch 128 at 128K context needs ~97 MiB) before any device call."""
+    class Fake:
+        def data_ptr(self):
+            return 4096
+
+    F = Fake()
+    big = B.decode_step(t=131071, E_cap=32768, n_buf=8, tok_base=131064, batch=128, n_h=64,
+                        c=512, n_hI=64, cI=128, m=4, k=512, w=128, rope_dims=64, rope_base=1e4,
+                        eps=1e-6, tail_dt=B.BF16, index_dt=B.FP8_E4M3, attn_dt=B.BF16, C=F, Z=F,
+                        B=F, CI=F, ZI=F, BI=F, kv_comp=F, KI=F, KI_scale=F, qI=F, qI_scale=F, wI=F,
+                        q=F, kv_ring=F, topk_idx=F, topk_cnt=F, out=F)
+    assert B.v4a_csa_decode_step_workspace(big) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.v4a_csa_decode_step_noalloc(ct.c_void_p(ct.addressof(big)), None) == ENOSPC
+    msg = B.v4a_last_error()
+    assert "67108864" in msg and str(B.v4a_csa_decode_step_workspace(big)) in msg
+    assert lib.v4a_csa_decode_step_noalloc(None, None) == EINVAL
+    hdr = open(HEADER).read()
+    assert f"#define V4A_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr
