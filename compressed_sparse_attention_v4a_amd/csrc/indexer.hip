@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a
 }  // namespace
 
 // MFMA paths (indexer_mfma.hip)
-bool indexer_fused_supported(int64_t Emax, int n_hI, int cI, int dt);
+bool indexer_fused_supported(int64_t Emax, int T, int n_hI, int cI, int k, int dt);
 hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s);
 bool indexer_mfma_supported(int T, int n_hI, int cI, int dt);
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
@@ -491,7 +491,7 @@ IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, 
   p.n_tiles = (int)((Emax + p.tile - 1) / p.tile);
   if (p.n_tiles < 1) p.n_tiles = 1;
   p.kc = k < p.tile ? k : p.tile;
-  p.fused = policy == 0 && indexer_fused_supported(Emax, n_hI, cI, dt);
+  p.fused = policy == 0 && indexer_fused_supported(Emax, T, n_hI, cI, k, dt);
   p.mfma_scan = policy == 0 && indexer_mfma_supported(T, n_hI, cI, dt);
   if (p.fused) {
     p.score_bytes = p.cand_bytes = p.total = 0;

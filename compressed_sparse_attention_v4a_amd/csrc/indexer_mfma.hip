@@ -59,13 +59,126 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x4 (&S)[4], const fl
   return __uint_as_float(x16[0]) + __uint_as_float(x16[1]);  // rows r and r ^ 1
 }
 
+// Radix select of the k-th largest of the keys held in registers by one wave: lane l
+// holds the contiguous keys [l per, l per + per) of E (slots past per or E hold key 0,
+// "absent", below every real key except the one NaN pattern whose key is 0).  Passes over
+// digits shared by every key (wave AND / OR) are skipped; the others count runs of equal
+// digits before touching the histogram (the wave's own, ordered by the wave's in-order LDS
+// operations) and find the bin with a DPP prefix sum.  The passes stop once the k-th key's
+// bin holds exactly the keys still needed.  On return the selection is: keys whose
+// resolved digits (key & pmask) exceed kth, then the first need_eq keys equal to it in
+// position order.  Needs E > k.
+template <int PER>
+__device__ __forceinline__ void radix_kth(const uint32_t (&key)[PER], int E, int k, uint32_t* hist,
+                                          uint32_t& kth, uint32_t& pmask_out, int& need_eq) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int base = lane * per;
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool v = j < per && base + j < E;
+    kand &= v ? key[j] : 0xFFFFFFFFu;
+    kor |= key[j];
+  }
+  wave_and_or(kand, kor);
+  const int common = (kand ^ kor) ? __builtin_clz(kand ^ kor) : 32;
+  const uint32_t n_absent = 64u * PER - (uint32_t)E;
+  for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+  uint32_t prefix = 0, pmask = 0;
+  int rem = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (common >= 32 - shift) {
+      prefix |= kand & (255u << shift);
+      pmask |= 255u << shift;
+      continue;
+    }
+    uint32_t cur = 0u, run = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if ((key[j] & pmask) == prefix) {
+        const uint32_t d = (key[j] >> shift) & 255u;
+        if (run != 0u && d != cur) {
+          atomicAdd(&hist[cur], run);
+          run = 0u;
+        }
+        cur = d;
+        ++run;
+      }
+    }
+    if (run != 0u) atomicAdd(&hist[cur], run);
+    if (lane == 0 && prefix == 0u && n_absent) atomicSub(&hist[0], n_absent);
+    __builtin_amdgcn_wave_barrier();
+    uint32_t cs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cs[j] = hist[255 - 4 * lane - j];
+    const uint32_t mine = cs[0] + cs[1] + cs[2] + cs[3];
+    uint32_t above = (uint32_t)wave_incl_sum((int)mine) - mine;
+    int hit_bin = -1;
+    uint32_t hit_above = 0u, hit_count = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
+        hit_bin = 255 - 4 * lane - j;
+        hit_above = above;
+        hit_count = cs[j];
+      }
+      above += cs[j];
+    }
+    const uint64_t m = __ballot(hit_bin >= 0);
+    const int src = m ? (int)__builtin_ctzll(m) : 0;
+    prefix |= (uint32_t)__builtin_amdgcn_readlane(hit_bin, src) << shift;
+    pmask |= 255u << shift;
+    rem -= __builtin_amdgcn_readlane((int)hit_above, src);
+    const bool whole = (uint32_t)__builtin_amdgcn_readlane((int)hit_count, src) == (uint32_t)rem;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[255 - 4 * lane - j] = 0u;  // the bins this lane read
+    // the bin holds exactly the keys still needed: all of them are selected, whatever
+    // their lower digits (the same set the remaining passes would find)
+    if (whole) break;
+  }
+  kth = prefix;
+  pmask_out = pmask;
+  need_eq = rem;
+}
+
+// Output slot of each selected key of a lane (position order, ties to the lower
+// position): calls emit(j, slot) for every selected register j.
+template <int PER, typename F>
+__device__ __forceinline__ void radix_emit(const uint32_t (&key)[PER], int E, uint32_t kth,
+                                           uint32_t pmask, int need_eq, F&& emit) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int base = lane * per;
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool v = j < per && base + j < E;
+    ngt += (v && (key[j] & pmask) > kth) ? 1 : 0;
+    neq += (v && (key[j] & pmask) == kth) ? 1 : 0;
+  }
+  const int packed = ngt | (neq << 16);  // E <= 65535
+  const int before = wave_incl_sum(packed) - packed;
+  int pos = (before & 0xFFFF) + min(before >> 16, need_eq);
+  int eq_seen = before >> 16;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool v = j < per && base + j < E;
+    const bool gt = v && (key[j] & pmask) > kth;
+    const bool eq = v && (key[j] & pmask) == kth && eq_seen < need_eq;
+    eq_seen += (v && (key[j] & pmask) == kth) ? 1 : 0;
+    if (gt || eq) {
+      emit(j, pos);
+      ++pos;
+    }
+  }
+}
+
 // Register form of the one-wave top-k for E <= 64 PER: lane l holds the contiguous keys
-// [l per, l per + per), per = ceil(E / 64).  Passes over digits shared by every key
-// (wave AND / OR) are skipped; the others count runs of equal digits before touching the
-// histogram (the wave's own, ordered by the wave's in-order LDS operations) and find the
-// bin with a DPP prefix sum.  Emission places each lane's run with one packed prefix sum
-// of (keys > kth, keys == kth).  The passes stop once the k-th key's bin holds exactly the
-// keys still needed.  Same result as wave_topk.
+// [l per, l per + per), per = ceil(E / 64); radix_kth finds the k-th key and radix_emit
+// places each lane's selected keys with one packed prefix sum of (keys > kth, keys ==
+// kth).  Same result as wave_topk.
 template <int PER>
 __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int32_t* oidx,
                               float* osc, int32_t* ocnt) {
@@ -79,108 +192,56 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
   } else {
     const int per = (E + 63) / 64;
     const int base = lane * per;
-    // slots past the lane's range or past E hold key 0 ("absent"): below every real key
-    // except the one NaN pattern whose key is 0, so the passes need no per-slot validity;
-    // the absent keys land in bin 0 while the prefix is 0 and are subtracted there
     uint32_t key[PER];
-    uint32_t kand = 0xFFFFFFFFu, kor = 0u;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool v = j < per && base + j < E;
-      key[j] = v ? score_key(sc[base + j]) : 0u;
-      kand &= v ? key[j] : 0xFFFFFFFFu;
-      kor |= key[j];
-    }
-    wave_and_or(kand, kor);
-    const int common = (kand ^ kor) ? __builtin_clz(kand ^ kor) : 32;
-    const uint32_t n_absent = 64u * PER - (uint32_t)E;
-    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
-    uint32_t prefix = 0, pmask = 0;
-    int rem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (common >= 32 - shift) {
-        prefix |= kand & (255u << shift);
-        pmask |= 255u << shift;
-        continue;
-      }
-      uint32_t cur = 0u, run = 0u;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if ((key[j] & pmask) == prefix) {
-          const uint32_t d = (key[j] >> shift) & 255u;
-          if (run != 0u && d != cur) {
-            atomicAdd(&hist[cur], run);
-            run = 0u;
-          }
-          cur = d;
-          ++run;
-        }
-      }
-      if (run != 0u) atomicAdd(&hist[cur], run);
-      if (lane == 0 && prefix == 0u && n_absent) atomicSub(&hist[0], n_absent);
-      __builtin_amdgcn_wave_barrier();
-      uint32_t cs[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cs[j] = hist[255 - 4 * lane - j];
-      const uint32_t mine = cs[0] + cs[1] + cs[2] + cs[3];
-      uint32_t above = (uint32_t)wave_incl_sum((int)mine) - mine;
-      int hit_bin = -1;
-      uint32_t hit_above = 0u, hit_count = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (above < (uint32_t)rem && above + cs[j] >= (uint32_t)rem) {
-          hit_bin = 255 - 4 * lane - j;
-          hit_above = above;
-          hit_count = cs[j];
-        }
-        above += cs[j];
-      }
-      const uint64_t m = __ballot(hit_bin >= 0);
-      const int src = m ? (int)__builtin_ctzll(m) : 0;
-      prefix |= (uint32_t)__builtin_amdgcn_readlane(hit_bin, src) << shift;
-      pmask |= 255u << shift;
-      rem -= __builtin_amdgcn_readlane((int)hit_above, src);
-      const bool whole = (uint32_t)__builtin_amdgcn_readlane((int)hit_count, src) == (uint32_t)rem;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hist[255 - 4 * lane - j] = 0u;  // the bins this lane read
-      // the bin holds exactly the keys still needed: all of them are selected, whatever
-      // their lower digits (the same set the remaining passes would find)
-      if (whole) break;
-    }
-    // selection on the resolved digits: keys above the prefix, then the first rem keys equal
-    // to it in index order (all of them when the passes stopped early)
-    const uint32_t kth = prefix;
-    const int need_eq = rem;
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool v = j < per && base + j < E;
-      ngt += (v && (key[j] & pmask) > kth) ? 1 : 0;
-      neq += (v && (key[j] & pmask) == kth) ? 1 : 0;
-    }
-    const int packed = ngt | (neq << 16);  // E <= 65535
-    const int before = wave_incl_sum(packed) - packed;
-    int pos = (before & 0xFFFF) + min(before >> 16, need_eq);
-    int eq_seen = before >> 16;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool v = j < per && base + j < E;
-      const bool gt = v && (key[j] & pmask) > kth;
-      const bool eq = v && (key[j] & pmask) == kth && eq_seen < need_eq;
-      eq_seen += (v && (key[j] & pmask) == kth) ? 1 : 0;
-      if (gt || eq) {
-        oidx[pos] = base + j;
-        if (osc) osc[pos] = key_score(key[j]);
-        ++pos;
-      }
-    }
+    for (int j = 0; j < PER; ++j) key[j] = (j < per && base + j < E) ? score_key(sc[base + j]) : 0u;
+    uint32_t kth, pmask;
+    int need_eq;
+    radix_kth<PER>(key, E, k, hist, kth, pmask, need_eq);
+    radix_emit<PER>(key, E, kth, pmask, need_eq, [&](int j, int pos) {
+      oidx[pos] = base + j;
+      if (osc) osc[pos] = key_score(key[j]);
+    });
   }
   for (int p = n + lane; p < k; p += 64) {
     oidx[p] = -1;
     if (osc) osc[p] = 0.0f;
   }
   if (lane == 0) *ocnt = n;
+}
+
+// Candidate buffer of one wave for long key lists: the n > k (key, entry) pairs in
+// ckey/cidx[0..n), in ascending entry order, are cut to the k best (larger key first,
+// ties to the lower entry), kept in ascending entry order in [0, k).  Returns the
+// smallest key kept: a later entry (higher index) can only displace a kept one with a
+// strictly larger key.  One wave; n <= 64 PER.
+template <int PER>
+__device__ uint32_t wave_shrink_pairs(uint32_t* ckey, int32_t* cidx, int n, int k, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  const int per = (n + 63) / 64;
+  const int base = lane * per;
+  uint32_t key[PER];
+  int32_t ent[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool v = j < per && base + j < n;
+    key[j] = v ? ckey[base + j] : 0u;
+    ent[j] = v ? cidx[base + j] : 0;
+  }
+  uint32_t kth, pmask;
+  int need_eq;
+  radix_kth<PER>(key, n, k, hist, kth, pmask, need_eq);
+  uint32_t kmin = 0xFFFFFFFFu;
+  // every lane has loaded its pairs before any slot is rewritten (slot <= position)
+  __builtin_amdgcn_wave_barrier();
+  radix_emit<PER>(key, n, kth, pmask, need_eq, [&](int j, int pos) {
+    ckey[pos] = key[j];
+    cidx[pos] = ent[j];
+    kmin = min(kmin, key[j]);
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+  return kmin;
 }
 
 // Exact top-k of one query over its scores sc[0..E) by one wave; writes the
@@ -265,12 +326,21 @@ __device__ void wave_topk(const float* sc, int E, int k, uint32_t* hist, int* sh
   (void)sh;
 }
 
-template <int CAP>
-__global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16_kernel(IndexerArgs a) {
+// CAPC == 0: every score of a query stays in LDS (CAP of them) and one register top-k
+// runs after the scan.  CAPC > 0 (long key lists, any length): each wave keeps only a
+// candidate buffer of CAPC (key, entry) pairs: a scored entry enters when its key
+// exceeds the k-th key of the last cut (every entry before the first cut), and the
+// buffer is cut back to its k best whenever the next chunk could overflow it.  The
+// entries arrive in ascending order, so buffer order is entry order and ties keep going
+// to the lower entry; the scores never reach HBM.
+template <int CAP, int CAPC>
+__global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 1) void indexer_prefill_bf16_kernel(
+    IndexerArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * kNE * kRowB];
-  __shared__ float sc[kQ][CAP];
+  __shared__ float sc[kQ][CAPC > 0 ? 1 : CAP];
+  __shared__ uint32_t ckey[kQ][CAPC > 0 ? CAPC : 1];
+  __shared__ int32_t cidx[kQ][CAPC > 0 ? CAPC : 1];
   __shared__ uint32_t hist[kQ][256];
-  __shared__ int shw[kQ][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,6 +396,11 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
   const int bb0 = jj * kRowB + (((2 * g) ^ (jj & 7)) << 4);
   const int bb1 = jj * kRowB + (((2 * g + 1) ^ (jj & 7)) << 4);
   float* scw = sc[wv];
+  uint32_t* ckw = ckey[wv];
+  int32_t* ciw = cidx[wv];
+  int ncand = 0;            // candidates in this wave's buffer (CAPC > 0)
+  uint32_t tau = 0u;        // a scored entry enters when its key exceeds tau ...
+  bool have_tau = false;    // ... once the buffer has been cut at least once
 
   // The ReLU-weighted head sum of each 16-entry tile runs on the vector unit while the
   // matrix unit multiplies the next tile (three vector instructions per MFMA), so the
@@ -337,9 +412,37 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
   int64_t sp = -1;  // entry of this lane's previous tile (-1: none)
   auto reduce_prev = [&]() {
     const float acc = relu_weighted_sum(Sp, wgt);
-    if (g == 0 && sp >= 0 && sp < Eq) scw[sp] = acc;
+    if constexpr (CAPC == 0) {
+      if (g == 0 && sp >= 0 && sp < Eq) scw[sp] = acc;
+    } else {
+      // lanes 0..15 hold the 16 entries of the tile in ascending order: ballot compaction
+      const uint32_t key = score_key(acc);
+      const bool pass = g == 0 && sp >= 0 && sp < Eq && (!have_tau || key > tau);
+      const uint64_t bm = __ballot(pass);
+      if (pass) {
+        const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+        ckw[pos] = key;
+        ciw[pos] = (int32_t)sp;
+      }
+      ncand += __popcll(bm);
+    }
+  };
+  // cut the buffer back to the k best when the next chunk (at most kNE entries) could
+  // overflow it
+  auto cut = [&]() {
+    if constexpr (CAPC > 0) {
+      if (ncand > a.k) {
+        tau = wave_shrink_pairs<CAPC / 64>(ckw, ciw, ncand, a.k, hist[wv]);
+        have_tau = true;
+        ncand = a.k;
+      }
+    }
   };
   for (int c = 0; c < nchunks; ++c) {
+    if constexpr (CAPC > 0) {
+      if (ncand > CAPC - kNE) cut();
+    }
     const int cur = (c & 1) * (kNE * kRowB);
     const char* buf = kbuf + cur;
     wait_vmcnt<0>();
@@ -387,8 +490,21 @@ __global__ __launch_bounds__(256, CAP <= 2048 ? 2 : 1) void indexer_prefill_bf16
   // per-query top-k by its own wave (no workgroup barrier needed from here on)
   if (qvalid) {
     const int64_t q = (int64_t)b * a.T + j;
-    wave_topk_reg<CAP / 64>(scw, (int)Eq, a.k, hist[wv], a.topk_idx + q * a.k,
-                            a.topk_score ? a.topk_score + q * a.k : nullptr, a.topk_cnt + q);
+    if constexpr (CAPC == 0) {
+      wave_topk_reg<CAP / 64>(scw, (int)Eq, a.k, hist[wv], a.topk_idx + q * a.k,
+                              a.topk_score ? a.topk_score + q * a.k : nullptr, a.topk_cnt + q);
+    } else {
+      cut();
+      // ncand = min(k, Eq): every entry entered before the first cut, k stay after it
+      int32_t* oi = a.topk_idx + q * a.k;
+      float* os = a.topk_score ? a.topk_score + q * a.k : nullptr;
+      for (int p = lane; p < a.k; p += 64) {
+        const bool v = p < ncand;
+        oi[p] = v ? ciw[p] : -1;
+        if (os) os[p] = v ? key_score(ckw[p]) : 0.0f;
+      }
+      if (lane == 0) a.topk_cnt[q] = ncand;
+    }
   }
 }
 
@@ -590,20 +706,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 
 }  // namespace
 
-// The fused prefill kernel covers bf16 keys of 128 channels, 64 heads, and up to
-// 4096 visible entries per query.
-bool indexer_fused_supported(int64_t Emax, int n_hI, int cI, int dt) {
-  return dt == kBF16 && cI == kCI && n_hI == kHeads && Emax <= 4096;
+// The fused prefill kernel covers bf16 keys of 128 channels and 64 heads: with all
+// scores in LDS up to 4096 visible entries per query, with the streaming candidate
+// buffer beyond that (k <= 1024; multi-query chunks, T > 1).
+bool indexer_fused_supported(int64_t Emax, int T, int n_hI, int cI, int k, int dt) {
+  if (dt != kBF16 || cI != kCI || n_hI != kHeads) return false;
+  return Emax <= 4096 || (T > 1 && k <= 1024);
 }
 
 hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s) {
   const unsigned nblk = (unsigned)((a.T + kQ - 1) / kQ);
+  const dim3 grid(nblk, (unsigned)a.batch);
   if (Emax <= 2048)
-    hipLaunchKernelGGL(indexer_prefill_bf16_kernel<2048>, dim3(nblk, (unsigned)a.batch), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL((indexer_prefill_bf16_kernel<2048, 0>), grid, dim3(256), 0, s, a);
+  else if (Emax <= 4096)
+    hipLaunchKernelGGL((indexer_prefill_bf16_kernel<4096, 0>), grid, dim3(256), 0, s, a);
+  else if (a.k <= 512)
+    hipLaunchKernelGGL((indexer_prefill_bf16_kernel<0, 1280>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(indexer_prefill_bf16_kernel<4096>, dim3(nblk, (unsigned)a.batch), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL((indexer_prefill_bf16_kernel<0, 2560>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

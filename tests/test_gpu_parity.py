@@ -801,3 +801,56 @@ def test_decode_step_bitwise_reproducible():
     a, b = _run_decode_step(cfg, d), _run_decode_step(cfg, d)
     for key in ("kv", "KI", "KIs", "ring", "idx", "cnt", "sc", "out"):
         assert torch.equal(_bits(a[key]), _bits(b[key])), key
+
+
+# ------------------------------------------- streaming indexer (long key lists) --- #
+
+@pytest.mark.parametrize("case,t0,T,k", [
+    ("random", 20000, 40, 512),      # E ~ 5000: the first lists past the all-in-LDS form
+    ("random", 131008, 64, 512),     # the last queries of a 128K prefill (E = 32752 .. 32768)
+    ("random", 60000, 24, 1024),     # k = 1024 (the V4-Pro k), the larger candidate buffer
+    ("equal", 40000, 8, 512),        # every score equal: the first k entries, every cut a tie
+    ("rising", 40000, 8, 512),       # every entry beats the buffer: a cut every few chunks
+    ("falling", 40000, 8, 512),      # after the first cut nothing enters
+])
+def test_indexer_stream_bf16(case, t0, T, k):
+    """Prefill chunks whose queries see more than 4096 entries: each wave streams its
+    query's scores through a candidate buffer that is cut back to the k best whenever it
+    could overflow, so no score reaches HBM.  Exact sets where the gap rule applies; equal
+    scores must give the lowest k indices."""
+    rng = np.random.default_rng(hash((case, t0, T, k)) % (1 << 32))
+    n_hI, cI, m = 64, 128, 4
+    E = (t0 + T) // m
+    if case == "random":
+        qI = rng.standard_normal((T, n_hI, cI))
+        KI = rng.standard_normal((E + 3, cI))
+    else:
+        u = np.abs(rng.standard_normal(cI)) + 0.5
+        qI = np.broadcast_to(u, (T, n_hI, cI)).copy()
+        s = np.arange(E + 3)
+        ramp = {"equal": np.ones(E + 3), "rising": 1.0 + s / (E + 3),
+                "falling": 2.0 - s / (E + 3)}[case]
+        KI = u[None, :] * ramp[:, None]
+    qI = synth.formats.bf16_bits(qI)
+    KI = synth.formats.bf16_bits(KI)
+    wI = rng.random((T, n_hI)).astype(np.float32)
+    log(f"indexer stream bf16 {case} t0={t0} T={T} k={k} E={E}")
+    idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
+    torch.cuda.synchronize()
+    Kd = f64(KI, "bf16")
+    rows = range(T) if T <= 24 else np.unique(np.concatenate([np.arange(6), np.arange(T - 6, T),
+                                                              np.random.default_rng(1).integers(0, T, 8)]))
+    for r in rows:
+        Er = (t0 + int(r) + 1) // m
+        ref = _oracle_scores(f64(qI[r:r + 1], "bf16"), Kd[:Er], wI[r:r + 1].astype(np.float64),
+                             t0 + int(r), m, Er)
+        got_i = idx[0, r:r + 1].cpu().numpy()
+        check_topk(got_i, cnt[0, r:r + 1].cpu().numpy(), ref, t0=t0 + int(r), m=m, k=k,
+                   gpu_scores=sc[0, r:r + 1].cpu().numpy(), what=f"{case} row {r}")
+        if case != "random":
+            # identical bf16 rows give identical scores on both sides, so ties are exact
+            # and the lower entry must win them: the oracle's selection, bit for bit
+            ref_i, _ = oracle.topk(ref, t0=t0 + int(r), m=m, k=k)
+            assert np.array_equal(got_i[0], ref_i[0]), f"{case} row {r}: selection differs"
+        if case in ("equal", "falling"):
+            assert np.array_equal(got_i[0], np.arange(k)), f"{case} row {r}: not the first k"
