@@ -55,6 +55,8 @@ def parse():
                     help="only run 4 device-to-device copies of MIB MiB (counter calibration)")
     ap.add_argument("--decode-only", default="", metavar="WORKLOAD",
                     help="only time one decode workload (5 cold + 5 warm rounds, for profiling)")
+    ap.add_argument("--prefill-128k-only", action="store_true",
+                    help="only time the 128K chunked CSA prefill")
     ap.add_argument("--flush-probe", action="store_true",
                     help="only measure a 128 MiB streaming read after no flush, after the "
                          "decode timing's 512 MiB write flush and after a 512 MiB read flush")
@@ -130,6 +132,12 @@ def main():
         return
     if args.flush_probe:
         flush_probe()
+        return
+    if args.prefill_128k_only:
+        import torch
+        from compressed_sparse_attention_v4a_amd import binding as B
+        B.lib()
+        print(json.dumps({"csa_prefill_n131072_chunked": prefill_128k_timing(torch.cuda.current_stream())}))
         return
     if args.decode_only:
         import torch
@@ -268,7 +276,8 @@ def main():
         if args.no_decode:
             del T, kv, KI, idx, cnt, out, ws_i, ws_a, q4, qI4, wI3, loc3
             torch.cuda.empty_cache()
-        line["extra"] = {"prefill_t0_896_T128": extra, "hca_prefill_n65536": hca_timing(stream)}
+        line["extra"] = {"prefill_t0_896_T128": extra, "hca_prefill_n65536": hca_timing(stream),
+                         "csa_prefill_n131072_chunked": prefill_128k_timing(stream)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -381,6 +390,68 @@ def hca_timing(stream, rounds=5, warmup=2):
            "attn_tflops": round(tf, 2), "attn_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
            "compress_gb_per_s": round(gbs, 1), "compress_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
     del q, out, ws, kv
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_128k_timing(stream, rounds=3, warmup=1, chunk=8192):
+    """CSA prefill of one 131072-token sequence (V4-Flash shapes) in chunks of 8192
+    queries: per chunk both compressors, the streaming indexer top-k (up to 32768 visible
+    entries, scores never in HBM) and the sparse attention.  Inputs (19 GiB with q and the
+    output) are drawn on the device from torch's seeded normal generator with the 8K
+    workload's distributions.  Reported: tokens/s of the whole prefill, per-stage time
+    summed over the chunks, and the indexer and attention rates against the bf16 peak."""
+    import torch
+    from compressed_sparse_attention_v4a_amd import costmodel, ops
+    n, c, n_h, n_hI, cI, m, k, w = 131072, 512, 64, 64, 128, 4, 512, 128
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x5EED0000 + 6 * 256)
+    sc = 1.0 / math.sqrt(c)
+    log("generating the 128K prefill inputs on the device")
+    rn = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+    C, Z = rn(n, 2 * c, std=sc), rn(n, 2 * c)
+    CI, ZI = rn(n, 2 * cI), rn(n, 2 * cI)
+    Bm = torch.randn(2 * m, c, generator=gen, device=dev) * math.sqrt(0.1)
+    BI = torch.randn(2 * m, cI, generator=gen, device=dev) * math.sqrt(0.1)
+    local = rn(n, c, std=sc)
+    q = rn(n, n_h, c, std=sc)
+    qI = rn(n, n_hI, cI)
+    wI = torch.rand(n, n_hI, generator=gen, device=dev)
+    g, gI = torch.ones(c, device=dev), torch.ones(cI, device=dev)
+    kw = dict(chunk=chunk, m=m, k=k, w=w, gamma=g, gammaI=gI, q_gamma=g, kv_gamma=g, rope_dims=64,
+              stream=stream)
+    bufs = None
+    for _ in range(warmup):
+        bufs = ops.csa_prefill_chunked(C, Z, Bm, CI, ZI, BI, q, qI, wI, local, bufs=bufs, **kw)["bufs"]
+    torch.cuda.synchronize()
+    log("timing the 128K chunked prefill")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(rounds):
+        ops.csa_prefill_chunked(C, Z, Bm, CI, ZI, BI, q, qI, wI, local, bufs=bufs, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / rounds
+    # one more pass with events around every stage of every chunk (not in the timed region)
+    evs = []
+    ops.csa_prefill_chunked(C, Z, Bm, CI, ZI, BI, q, qI, wI, local, bufs=bufs, events=evs, **kw)
+    torch.cuda.synchronize()
+    stage = {}
+    for name, a, b in evs:
+        stage[name] = stage.get(name, 0.0) + a.elapsed_time(b)
+    counts = costmodel.csa_prefill_counts(n, m, k, w, n_h, c, n_hI, cI)
+    ti = counts["index_flops"] / (stage["indexer_topk"] * 1e-3) / 1e12
+    ta = counts["attn_flops"] / (stage["sparse_mqa"] * 1e-3) / 1e12
+    ideal_ms = (counts["index_flops"] + counts["attn_flops"]) / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    res = {"n": n, "chunk": chunk, "ms": round(ms, 3), "tokens_per_s": round(n / (ms * 1e-3), 1),
+           "stages_ms": {x: round(v, 3) for x, v in stage.items()},
+           "index_tflop": round(counts["index_flops"] / 1e12, 3),
+           "attn_tflop": round(counts["attn_flops"] / 1e12, 3),
+           "indexer_tflops": round(ti, 1), "indexer_frac_bf16_peak": round(ti / PEAK_BF16_TFLOPS, 4),
+           "attn_tflops": round(ta, 1), "attn_frac_bf16_peak": round(ta / PEAK_BF16_TFLOPS, 4),
+           "ideal_ms": round(ideal_ms, 3), "frac_of_ideal": round(ideal_ms / ms, 4)}
+    del C, Z, CI, ZI, local, q, qI, wI, bufs
     torch.cuda.empty_cache()
     return res
 

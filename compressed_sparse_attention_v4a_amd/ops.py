@@ -182,3 +182,71 @@ def hca_attn(q, kv_comp, kv_local, *, t0, m_prime, w, dt, loc_base=0, sink=None,
                    rope_dims, rope_base, scale, batch, t0, T, n_h, c, m_prime, w, E_cap, out,
                    _NP_DT[dt], ws, nbytes, stream)
     return out
+
+
+def csa_prefill_chunked(C, Z, B_, CI, ZI, BI, q, qI, wI, local, *, chunk, m, k, w, gamma=None,
+                        gammaI=None, q_gamma=None, kv_gamma=None, sink=None, rope_dims=0,
+                        rope_dims_I=0, rope_base=10000.0, eps=1e-6, bufs=None, stream=None,
+                        events=None):
+    """CSA prefill of one sequence of n tokens in chunks of `chunk` queries, in the order of
+    "CSA And HCA: Definition, State, And Cost Model" section 3 per chunk [t0, t0 + T):
+    emit the main and indexer entries completed inside the chunk (from the C/Z rows of the
+    whole sequence, row r = position r), index top-k of the chunk's queries over every entry
+    visible to them, then sparse attention.  The long-context chunks take the streaming
+    indexer, so no score matrix reaches HBM.
+
+    C, Z [n][2c]; CI, ZI [n][2cI]; q [n][n_h][c]; qI [n][n_hI][cI]; wI [n][n_hI];
+    local [n][c]; all bf16 (wI float32).  bufs: optional dict of preallocated outputs and
+    workspaces (from a previous call with the same shapes).  events: optional list that
+    receives (stage, start, end) CUDA events per stage and chunk.
+    Returns dict(kv [1][E][c], KI [1][E][cI], idx [1][n][k], cnt [1][n], out [1][n][n_h][c],
+    bufs)."""
+    n, n_h, c = q.shape
+    n_hI, cI = qI.shape[1], qI.shape[2]
+    E = n // m
+    dev = q.device
+    if bufs is None:
+        bufs = dict(
+            kv=torch.empty(1, E, c, dtype=torch.bfloat16, device=dev),
+            KI=torch.empty(1, E, cI, dtype=torch.bfloat16, device=dev),
+            idx=torch.empty(1, n, k, dtype=torch.int32, device=dev),
+            cnt=torch.empty(1, n, dtype=torch.int32, device=dev),
+            out=torch.empty(1, n, n_h, c, dtype=torch.bfloat16, device=dev))
+        wi = max(B.v4a_indexer_topk_workspace(1, min(chunk, n - t0), t0, n_hI, cI, m, k, B.BF16)
+                 for t0 in range(0, n, chunk))
+        wa = max(B.v4a_sparse_mqa_prefill_workspace(1, t0, min(chunk, n - t0), 0, n, n_h, c, k, w,
+                                                    B.BF16) for t0 in range(0, n, chunk))
+        bufs["ws_i"], bufs["ws_i_bytes"] = workspace(wi, dev), wi
+        bufs["ws_a"], bufs["ws_a_bytes"] = workspace(wa, dev), wa
+    kv, KI, idx, cnt, out = (bufs[x] for x in ("kv", "KI", "idx", "cnt", "out"))
+    s = stream if stream is not None else torch.cuda.current_stream()
+    C3, Z3, CI3, ZI3 = C.view(1, n, 2 * c), Z.view(1, n, 2 * c), CI.view(1, n, 2 * cI), ZI.view(1, n, 2 * cI)
+    loc3 = local.view(1, n, c)
+
+    def mark(name, fn):
+        if events is None:
+            fn()
+            return
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        events.append((name, a, b))
+
+    for t0 in range(0, n, chunk):
+        T = min(chunk, n - t0)
+        mark("compress_main", lambda: B.v4a_compress(
+            C3, Z3, B.BF16, B_, 1, n, 0, t0, T, c, m, 1, gamma, eps, rope_dims, rope_base, kv,
+            None, B.BF16, E, s))
+        mark("compress_index", lambda: B.v4a_compress(
+            CI3, ZI3, B.BF16, BI, 1, n, 0, t0, T, cI, m, 1, gammaI, eps, rope_dims_I, rope_base,
+            KI, None, B.BF16, E, s))
+        mark("indexer_topk", lambda: B.v4a_indexer_topk(
+            qI[t0:t0 + T].unsqueeze(0), None, KI, None, B.BF16, wI[t0:t0 + T].unsqueeze(0), 1, T,
+            t0, n_hI, cI, m, k, E, idx[:, t0:t0 + T], cnt[:, t0:t0 + T], None, bufs["ws_i"],
+            bufs["ws_i_bytes"], s))
+        mark("sparse_mqa", lambda: B.v4a_sparse_mqa_prefill(
+            q[t0:t0 + T].unsqueeze(0), kv, loc3, 0, n, idx[:, t0:t0 + T], cnt[:, t0:t0 + T], sink,
+            q_gamma, kv_gamma, eps, rope_dims, rope_base, 0.0, 1, t0, T, n_h, c, k, w, E,
+            out[:, t0:t0 + T], B.BF16, bufs["ws_a"], bufs["ws_a_bytes"], s))
+    return dict(kv=kv, KI=KI, idx=idx, cnt=cnt, out=out, bufs=bufs)

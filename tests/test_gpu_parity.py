@@ -854,3 +854,60 @@ def test_indexer_stream_bf16(case, t0, T, k):
             assert np.array_equal(got_i[0], ref_i[0]), f"{case} row {r}: selection differs"
         if case in ("equal", "falling"):
             assert np.array_equal(got_i[0], np.arange(k)), f"{case} row {r}: not the first k"
+
+
+# ------------------------------------------------ 128K-context chunked CSA prefill --- #
+
+def test_csa_prefill_128k_chunked_sampled():
+    """V4-Flash CSA prefill of n = 131072 tokens in chunks of 8192 queries (the 128K
+    prefill the benchmark times): per chunk both compressors emit the chunk's entries, the
+    streaming indexer selects over up to 32768 entries, and the sparse attention runs.
+    Inputs are drawn on the device from torch's seeded normal generator with the C2
+    distributions; sampled rows are checked against the oracle fed the GPU's entries (and,
+    for attention, the GPU's selection)."""
+    n, c, n_h, n_hI, cI, m, k, w, chunk = 131072, 512, 64, 64, 128, 4, 512, 128, 8192
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(0x5EED0000 + 5 * 256)
+    sc = 1 / math.sqrt(c)
+    rn = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=DEV) * std).to(torch.bfloat16)
+    log("generating the 128K prefill inputs on the device")
+    C, Z = rn(n, 2 * c, std=sc), rn(n, 2 * c)
+    CI, ZI = rn(n, 2 * cI), rn(n, 2 * cI)
+    Bm = (torch.randn(2 * m, c, generator=gen, device=DEV) * math.sqrt(0.1)).contiguous()
+    BI = (torch.randn(2 * m, cI, generator=gen, device=DEV) * math.sqrt(0.1)).contiguous()
+    local = rn(n, c, std=sc)
+    q = rn(n, n_h, c, std=sc)
+    qI = rn(n, n_hI, cI)
+    wI = torch.rand(n, n_hI, generator=gen, device=DEV)
+    g, gI = torch.ones(c, device=DEV), torch.ones(cI, device=DEV)
+    log("chunked prefill n=131072 chunk=8192")
+    r = ops.csa_prefill_chunked(C, Z, Bm, CI, ZI, BI, q, qI, wI, local, chunk=chunk, m=m, k=k,
+                                w=w, gamma=g, gammaI=gI, q_gamma=g, kv_gamma=g, rope_dims=64)
+    torch.cuda.synchronize()
+    kvd = decode_stored(r["kv"][0], "bf16")
+    KId = decode_stored(r["KI"][0], "bf16")
+    Bh, BIh = Bm.cpu().numpy(), BI.cpu().numpy()
+    dl = lambda t: decode_stored(t, "bf16")
+    # sampled entries of both compressors (their pooled rows only)
+    for i in (0, 1, 2047, 2048, 20000, 32767):
+        lo = max(0, 4 * (i - 1))
+        for nm, CC, ZZ, Bx, cc, rd, ref_rows in (("main", C, Z, Bh, c, 64, kvd), ("index", CI, ZI, BIh, cI, 0, KId)):
+            ref = oracle.compress(dl(CC[lo:4 * i + 4]), dl(ZZ[lo:4 * i + 4]), Bx, tok_base=lo,
+                                  i_begin=i, i_end=i + 1, c=cc, m=m, overlap=True,
+                                  gamma=np.ones(cc), rope_dims=rd)[0]
+            assert_bf16_close(ref_rows[i], ref, what=f"{nm} entry {i}")
+    rows = [5, 2047, 12000, 65537, 98303, 126000, 131070, 131071]
+    idx_h, cnt_h = r["idx"][0].cpu().numpy(), r["cnt"][0].cpu().numpy()
+    ld = dl(local)
+    for t in rows:
+        Et = (t + 1) // m
+        qIt = dl(qI[t:t + 1])
+        ref_s = oracle.index_scores(qIt, KId[:Et], wI[t:t + 1].double().cpu().numpy(), t0=t, m=m,
+                                    ld=Et)
+        check_topk(idx_h[t:t + 1], cnt_h[t:t + 1], ref_s, t0=t, m=m, k=k, what=f"128K row {t}")
+        lb = max(0, t - w + 1)
+        ref_o = oracle.attend_csa(dl(q[t:t + 1]), kvd, ld[lb:t + 1], idx_h[t:t + 1], cnt_h[t:t + 1],
+                                  loc_base=lb, t0=t, w=w, q_gamma=np.ones(c), kv_gamma=np.ones(c),
+                                  q_norm=True, kv_norm=True, rope_dims=64)
+        assert_attn_close(dl(r["out"][0, t:t + 1]), ref_o, atol=ATOL_BF16, rel_rms=REL_RMS_BF16,
+                          what=f"128K row {t}")
