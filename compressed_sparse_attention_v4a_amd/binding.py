@@ -64,6 +64,12 @@ def lib() -> ct.CDLL:
         L.v4a_csa_decode_step_workspace.argtypes = [vp]
         L.v4a_csa_decode_step.argtypes = [vp, vp, sz, vp]
         L.v4a_csa_decode_step_noalloc.argtypes = [vp, vp]
+        L.v4a_linear_workspace.restype = sz
+        L.v4a_linear_workspace.argtypes = [i32, i32, i32]
+        L.v4a_linear.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, sz, vp]
+        L.v4a_grouped_out_proj_workspace.restype = sz
+        L.v4a_grouped_out_proj_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.v4a_grouped_out_proj.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         _check_step_layout(L)
         _lib = L
     return _lib
@@ -215,3 +221,21 @@ def v4a_hca_attn(q, kv_comp, kv_local, loc_base, n_loc, sink, q_gamma, kv_gamma,
         _p(q), _p(kv_comp), _p(kv_local), loc_base, n_loc, _p(sink), _p(q_gamma), _p(kv_gamma),
         eps, rope_dims, rope_base, scale, batch, t0, T, n_h, c, m_prime, w, E_cap, _p(out), dt,
         _p(ws), ws_bytes, _s(stream)))
+
+
+def v4a_linear_workspace(T, K, N) -> int:
+    return lib().v4a_linear_workspace(T, K, N)
+
+
+def v4a_linear(X, W, T, K, N, Y, out_dt, ws, ws_bytes, stream=None):
+    _check("v4a_linear", lib().v4a_linear(_p(X), _p(W), T, K, N, _p(Y), out_dt, _p(ws), ws_bytes,
+                                          _s(stream)))
+
+
+def v4a_grouped_out_proj_workspace(T, n_h, c, g, d_g, d) -> int:
+    return lib().v4a_grouped_out_proj_workspace(T, n_h, c, g, d_g, d)
+
+
+def v4a_grouped_out_proj(o, W_A, W_B, T, n_h, c, g, d_g, d, out, ws, ws_bytes, stream=None):
+    _check("v4a_grouped_out_proj", lib().v4a_grouped_out_proj(
+        _p(o), _p(W_A), _p(W_B), T, n_h, c, g, d_g, d, _p(out), _p(ws), ws_bytes, _s(stream)))

@@ -250,3 +250,63 @@ def csa_prefill_chunked(C, Z, B_, CI, ZI, BI, q, qI, wI, local, *, chunk, m, k, 
             q_gamma, kv_gamma, eps, rope_dims, rope_base, 0.0, 1, t0, T, n_h, c, k, w, E,
             out[:, t0:t0 + T], B.BF16, bufs["ws_a"], bufs["ws_a_bytes"], s))
     return dict(kv=kv, KI=KI, idx=idx, cnt=cnt, out=out, bufs=bufs)
+
+
+def linear(X, W, *, out_dt="bf16", out=None, ws=None, stream=None):
+    """Y = X W^T through v4a_linear: X [T][K] bf16, W [N][K] bf16 -> Y [T][N] (bf16 or f32)."""
+    T, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty(T, N, dtype=_TORCH[out_dt], device=X.device)
+    nbytes = B.v4a_linear_workspace(T, K, N)
+    if ws is None or ws.numel() < nbytes:
+        ws = workspace(nbytes, X.device)
+    B.v4a_linear(X, W, T, K, N, out, _NP_DT[out_dt], ws, nbytes, stream)
+    return out
+
+
+def grouped_out_proj(o, W_A, W_B, *, out=None, ws=None, stream=None):
+    """o [T][n_h][c], W_A [g][d_g][c n_h/g], W_B [d][g d_g] (bf16) -> [T][d] bf16."""
+    T, n_h, c = o.shape
+    g, d_g = W_A.shape[0], W_A.shape[1]
+    d = W_B.shape[0]
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=o.device)
+    nbytes = B.v4a_grouped_out_proj_workspace(T, n_h, c, g, d_g, d)
+    if ws is None or ws.numel() < nbytes:
+        ws = workspace(nbytes, o.device)
+    B.v4a_grouped_out_proj(o, W_A, W_B, T, n_h, c, g, d_g, d, out, ws, nbytes, stream)
+    return out
+
+
+def csa_layer_prefill(H, Wt, *, m, k, w, chunk=None, rope_dims=64, gamma=None, gammaI=None,
+                      stream=None, keep=False):
+    """One CSA attention layer over a prefill of n tokens (H [n][d] bf16), "CSA And HCA:
+    Definition, State, And Cost Model": the projections of sections 2.1, 3.1, 3.2 and
+    5.1 (v4a_linear), the hot path (compressors, indexer top-k, sparse attention;
+    chunked when chunk is given) and the grouped output projection of section 5.4.
+    Wt: bf16 weights W_dq [d_c][d], W_uq [n_h c][d_c], W_iuq [n_hI cI][d_c], W_w [n_hI][d],
+    W_loc [c][d], W_kv, W_z [2c][d], W_ikv, W_iz [2cI][d], W_oa [g][d_g][c n_h/g],
+    W_ob [d][g d_g]; float32 B [2m][c], BI [2m][cI].  Returns the [n][d] output (and the
+    intermediates when keep=True)."""
+    n = H.shape[0]
+    c = Wt["W_loc"].shape[0]
+    n_h = Wt["W_uq"].shape[0] // c
+    cI = Wt["W_ikv"].shape[0] // 2
+    n_hI = Wt["W_w"].shape[0]
+    ws = workspace(B.v4a_linear_workspace(n, 8, 8), H.device)
+    lin = lambda X, W_, dt="bf16": linear(X, W_, out_dt=dt, ws=ws, stream=stream)
+    cq = lin(H, Wt["W_dq"])
+    q = lin(cq, Wt["W_uq"]).view(n, n_h, c)
+    qI = lin(cq, Wt["W_iuq"]).view(n, n_hI, cI)
+    wI = lin(H, Wt["W_w"], "f32")
+    local = lin(H, Wt["W_loc"])
+    C, Z = lin(H, Wt["W_kv"]), lin(H, Wt["W_z"])
+    CI, ZI = lin(H, Wt["W_ikv"]), lin(H, Wt["W_iz"])
+    r = csa_prefill_chunked(C, Z, Wt["B"], CI, ZI, Wt["BI"], q, qI, wI, local,
+                            chunk=chunk or n, m=m, k=k, w=w, gamma=gamma, gammaI=gammaI,
+                            q_gamma=gamma, kv_gamma=gamma, rope_dims=rope_dims, stream=stream)
+    out = grouped_out_proj(r["out"][0], Wt["W_oa"], Wt["W_ob"], stream=stream)
+    if keep:
+        return out, dict(cq=cq, q=q, qI=qI, wI=wI, local=local, C=C, Z=Z, CI=CI, ZI=ZI, **r)
+    return out

@@ -310,6 +310,41 @@ V4A_API size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d);
 V4A_API int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * v4a_linear -- a plain projection Y = X W^T of the layer around the attention path
+ * (the query, indexer and compressor projections of [Def] sections 2.1, 3.1, 3.2
+ * and 5.1): Y[t][n] = sum_k X[t][k] W[n][k], bf16 operands, float32 accumulation.
+ *   X   : device bf16 [T][K];  W : device bf16 [N][K] (row n = output feature n).
+ *   Y   : device [T][N] of out_dt (V4A_BF16 or V4A_F32).
+ *   ws  : device workspace of v4a_linear_workspace(T, K, N) bytes, 16-byte aligned.
+ * Errors: V4A_EINVAL for null pointers or sizes < 1; V4A_ENOTSUP if K or N is not a
+ *   multiple of 8 or out_dt is another type; V4A_ENOSPC for a small workspace;
+ *   V4A_EIO if the GEMM library fails.
+ */
+V4A_API size_t v4a_linear_workspace(int T, int K, int N);
+V4A_API int v4a_linear(const void* X, const void* W, int T, int K, int N, void* Y, v4a_dtype out_dt,
+               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * v4a_grouped_out_proj -- the grouped output projection ([Def] section 5.4):
+ *   out[t] = W_B [ W_A[0] o^G[t][0]; ... ; W_A[g-1] o^G[t][g-1] ]
+ * where o^G[t][i] is the concatenation of the c-wide outputs of heads
+ * i n_h/g .. (i+1) n_h/g - 1 of query t (a contiguous block of its output row).
+ *   o    : device bf16 [T][n_h][c], the attention output.
+ *   W_A  : device bf16 [g][d_g][c n_h/g].
+ *   W_B  : device bf16 [d][g d_g].
+ *   out  : device bf16 [T][d].
+ *   ws   : device workspace of v4a_grouped_out_proj_workspace(...) bytes, 256-byte
+ *          aligned; it also holds the intermediate [T][g d_g] (rounded to bf16).
+ * Float32 accumulation.  Errors: V4A_EINVAL for null pointers, sizes < 1 or n_h not
+ *   a multiple of g; V4A_ENOTSUP unless c n_h/g, d_g and d are multiples of 8;
+ *   V4A_ENOSPC; V4A_EIO.
+ */
+V4A_API size_t v4a_grouped_out_proj_workspace(int T, int n_h, int c, int g, int d_g, int d);
+V4A_API int v4a_grouped_out_proj(const void* o, const void* W_A, const void* W_B, int T, int n_h,
+                         int c, int g, int d_g, int d, void* out, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
  * v4a_csa_decode_step_noalloc -- v4a_csa_decode_step for callers that cannot
  * allocate device memory (code under HIP graph capture, serving loops or harnesses
  * that forbid allocation).  Same description `d`, same results bit for bit, same

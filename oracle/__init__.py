@@ -13,6 +13,8 @@ Functions follow "CSA And HCA: Definition, State, And Cost Model" ([Def]):
   attend_csa     -- sections 3.2, 5.1-5.3 (one softmax over top-k entries + window)
   attend_hca     -- sections 4, 5.1-5.3 (all completed entries + window)
   decode_step    -- section 7 (incremental decode order)
+  linear         -- the projections around the path (sections 2.1, 3.1, 3.2, 5.1)
+  grouped_out_proj -- section 5.4 (grouped output projection)
 
 Parity pins for every function live in tests/test_oracle_*.py.
 """
@@ -249,6 +251,27 @@ def attend_decode(q, kv_comp, ring, idx, cnt, *, t, w, sink=None, q_gamma=None, 
                             _pd(sk), _pd(_f64(q_gamma)), _pd(_f64(kv_gamma)), int(q_norm),
                             int(kv_norm), eps, rope_dims, rope_base, scale, n_h, c, w, _pd(out))
     return out
+
+
+def linear(X, W) -> np.ndarray:
+    """A projection of the layer around the path (sections 2.1, 3.1, 3.2, 5.1):
+    Y[t][n] = sum_k X[t][k] W[n][k] in float64."""
+    return _f64(X) @ _f64(W).T
+
+
+def grouped_out_proj(o, W_A, W_B) -> np.ndarray:
+    """Section 5.4: out_t = W^{O,B} [W^{O,A}_1 o^G_{t,1}; ...; W^{O,A}_g o^G_{t,g}] in float64.
+    o [T][n_h][c]; W_A [g][d_g][c n_h/g]; W_B [d][g d_g]; group i is heads
+    i n_h/g .. (i+1) n_h/g - 1, concatenated in head order."""
+    o, W_A, W_B = _f64(o), _f64(W_A), _f64(W_B)
+    T, n_h, c = o.shape
+    g, d_g, Kg = W_A.shape
+    assert n_h % g == 0 and Kg == c * (n_h // g)
+    mid = np.empty((T, g, d_g))
+    for i in range(g):
+        oG = o[:, i * (n_h // g):(i + 1) * (n_h // g), :].reshape(T, Kg)
+        mid[:, i, :] = oG @ W_A[i].T
+    return mid.reshape(T, g * d_g) @ W_B.T
 
 
 def decode_step(state: dict, *, t, c, cI, m, k, w, rope_dims, rope_base=10000.0, eps=1e-6,

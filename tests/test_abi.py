@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 17, names
+    assert len(names) == 21, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (v4a_\w+)", out))
@@ -222,3 +222,28 @@ def test_decode_step_noalloc_validation(lib):
     assert lib.v4a_csa_decode_step_noalloc(None, None) == EINVAL
     hdr = open(HEADER).read()
     assert f"#define V4A_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr
+
+
+def test_projection_validation(lib):
+    """v4a_linear / v4a_grouped_out_proj validate on the host before any device work."""
+    assert lib.v4a_linear_workspace(0, 8, 8) == 0
+    ws = B.v4a_linear_workspace(16, 64, 64)
+    assert ws > 0
+    run = lambda **kw: lib.v4a_linear(*[kw.get(n, d) for n, d in (
+        ("X", P), ("W", P), ("T", 16), ("K", 64), ("N", 64), ("Y", P), ("dt", 1), ("ws", P),
+        ("wsb", ws), ("s", None))])
+    assert run(X=None) == EINVAL
+    assert run(T=0) == EINVAL
+    assert run(K=60) == ENOTSUP
+    assert run(dt=2) == ENOTSUP
+    assert run(wsb=ws - 1) == ENOSPC
+    assert B.v4a_grouped_out_proj_workspace(16, 64, 512, 7, 64, 64) == 0   # n_h % g
+    need = B.v4a_grouped_out_proj_workspace(16, 64, 512, 8, 64, 64)
+    assert need >= 16 * 8 * 64 * 2
+    gp = lambda **kw: lib.v4a_grouped_out_proj(*[kw.get(n, d) for n, d in (
+        ("o", P), ("A", P), ("B", P), ("T", 16), ("n_h", 64), ("c", 512), ("g", 8), ("d_g", 64),
+        ("d", 64), ("out", P), ("ws", P), ("wsb", need), ("s", None))])
+    assert gp(o=None) == EINVAL
+    assert gp(g=7) == EINVAL
+    assert gp(d=60) == ENOTSUP
+    assert gp(wsb=need - 1) == ENOSPC

@@ -911,3 +911,134 @@ def test_csa_prefill_128k_chunked_sampled():
                                   q_norm=True, kv_norm=True, rope_dims=64)
         assert_attn_close(dl(r["out"][0, t:t + 1]), ref_o, atol=ATOL_BF16, rel_rms=REL_RMS_BF16,
                           what=f"128K row {t}")
+
+
+# -------------------------------------------------- projections and the layer wrap --- #
+
+def _bf16_gemm_gate(got, ref, sumabs, K, what):
+    """|got - ref| <= 1 bf16 ulp of ref + K 2^-23 sum_k |x_k w_k|: the float32 sum of bf16
+    products is exact up to its accumulation error, then rounded once to bf16."""
+    err = np.abs(got - ref)
+    bound = _bf16_ulp(ref) + K * 2.0 ** -23 * sumabs
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {err.size} beyond the bound"
+
+
+def _bf16_ulp(x):
+    from _helpers import bf16_ulp
+    return bf16_ulp(x)
+
+
+@pytest.mark.parametrize("T,K,N,out_dt", [(257, 512, 1024, "bf16"), (64, 4096, 64, "f32"),
+                                          (1000, 1024, 136, "bf16")])
+def test_linear_bf16(T, K, N, out_dt):
+    rng = np.random.default_rng(T + K + N)
+    X = synth.formats.bf16_bits(rng.standard_normal((T, K)))
+    W = synth.formats.bf16_bits(rng.standard_normal((N, K)) / math.sqrt(K))
+    log(f"linear T={T} K={K} N={N} out={out_dt}")
+    Y = ops.linear(up(X), up(W), out_dt=out_dt)
+    torch.cuda.synchronize()
+    Xd, Wd = f64(X, "bf16"), f64(W, "bf16")
+    ref = oracle.linear(Xd, Wd)
+    got = decode_stored(Y, out_dt)
+    if out_dt == "f32":
+        bound = K * 2.0 ** -23 * (np.abs(Xd) @ np.abs(Wd).T)
+        assert np.all(np.abs(got - ref) <= bound), "f32 linear"
+    else:
+        _bf16_gemm_gate(got, ref, np.abs(Xd) @ np.abs(Wd).T, K, "linear")
+
+
+@pytest.mark.parametrize("T,n_h,c,g,d_g,d", [(300, 64, 512, 8, 1024, 4096), (77, 128, 512, 16, 256, 1024)])
+def test_grouped_out_proj(T, n_h, c, g, d_g, d):
+    """The grouped output projection against the oracle fed the same attention output.
+    The intermediate [T][g d_g] is rounded to bf16 (a layer activation), so the gate adds
+    2^-7 sum_j |W_B[n][j]| |mid_j| (one bf16 ulp of every intermediate value)."""
+    rng = np.random.default_rng(T + g)
+    Kg = c * n_h // g
+    o = synth.formats.bf16_bits(0.05 * rng.standard_normal((T, n_h, c)))
+    W_A = synth.formats.bf16_bits(rng.standard_normal((g, d_g, Kg)) / math.sqrt(Kg))
+    W_B = synth.formats.bf16_bits(rng.standard_normal((d, g * d_g)) / math.sqrt(g * d_g))
+    log(f"grouped out proj T={T} n_h={n_h} g={g} d_g={d_g} d={d}")
+    out = ops.grouped_out_proj(up(o), up(W_A), up(W_B))
+    torch.cuda.synchronize()
+    od, Ad, Bd = f64(o, "bf16"), f64(W_A, "bf16"), f64(W_B, "bf16")
+    ref = oracle.grouped_out_proj(od, Ad, Bd)
+    mid = np.stack([od[:, i * (n_h // g):(i + 1) * (n_h // g)].reshape(T, Kg) @ Ad[i].T
+                    for i in range(g)], axis=1).reshape(T, g * d_g)
+    mid_abs = np.stack([np.abs(od[:, i * (n_h // g):(i + 1) * (n_h // g)].reshape(T, Kg)) @ np.abs(Ad[i]).T
+                        for i in range(g)], axis=1).reshape(T, g * d_g)
+    bound_mid = 2.0 ** -7 * np.abs(mid) + Kg * 2.0 ** -23 * mid_abs
+    got = decode_stored(out, "bf16")
+    err = np.abs(got - ref)
+    bound = (_bf16_ulp(ref) + bound_mid @ np.abs(Bd).T
+             + g * d_g * 2.0 ** -23 * ((np.abs(mid) + bound_mid) @ np.abs(Bd).T))
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{int(bad.sum())} of {err.size} beyond the bound"
+    # and the grouping is the one the pages define: the RMS error against the oracle is a
+    # fraction of a bf16 step, against the oracle with two heads swapped across groups it
+    # is large
+    rms = lambda a, b: np.sqrt(np.mean((a - b) ** 2)) / np.sqrt(np.mean(b ** 2))
+    o2 = od.copy()
+    o2[:, [0, n_h - 1]] = o2[:, [n_h - 1, 0]]
+    assert rms(got, ref) < 4e-3 and rms(got, oracle.grouped_out_proj(o2, Ad, Bd)) > 4e-2
+
+
+def test_csa_layer_prefill_small():
+    """A whole CSA layer (projections, hot path in two chunks, grouped output projection)
+    at a small size with the V4-Flash head shapes; every stage against the oracle fed the
+    previous stage's GPU output."""
+    n, d, d_c, n_h, c, n_hI, cI, g, d_g, m, k, w = 512, 512, 256, 64, 512, 64, 128, 8, 256, 4, 64, 128
+    rng = np.random.default_rng(2024)
+    wgt = lambda rows, cols: synth.formats.bf16_bits(rng.standard_normal((rows, cols)) / math.sqrt(cols))
+    Wh = dict(W_dq=wgt(d_c, d), W_uq=wgt(n_h * c, d_c), W_iuq=wgt(n_hI * cI, d_c), W_w=wgt(n_hI, d),
+              W_loc=wgt(c, d), W_kv=wgt(2 * c, d), W_z=wgt(2 * c, d), W_ikv=wgt(2 * cI, d),
+              W_iz=wgt(2 * cI, d), W_ob=wgt(d, g * d_g))
+    Wh["W_oa"] = synth.formats.bf16_bits(rng.standard_normal((g, d_g, c * n_h // g)) / math.sqrt(c * n_h // g))
+    Bm = (math.sqrt(0.1) * rng.standard_normal((2 * m, c))).astype(np.float32)
+    BI = (math.sqrt(0.1) * rng.standard_normal((2 * m, cI))).astype(np.float32)
+    H = synth.formats.bf16_bits(rng.standard_normal((n, d)))
+    Wt = {key: up(v) for key, v in Wh.items()}
+    Wt["B"], Wt["BI"] = up(Bm), up(BI)
+    gm, gI = np.ones(c, np.float32), np.ones(cI, np.float32)
+    log("csa layer prefill n=512 (projections + hot path + grouped output)")
+    out, st = ops.csa_layer_prefill(up(H), Wt, m=m, k=k, w=w, chunk=256, rope_dims=64,
+                                    gamma=up(gm), gammaI=up(gI), keep=True)
+    torch.cuda.synchronize()
+    dl = lambda t: decode_stored(t, "bf16")
+    Hd = f64(H, "bf16")
+    # projections
+    for name, src, W_ in (("cq", Hd, "W_dq"), ("local", Hd, "W_loc"), ("C", Hd, "W_kv"),
+                          ("Z", Hd, "W_z"), ("CI", Hd, "W_ikv"), ("ZI", Hd, "W_iz")):
+        Wd = f64(Wh[W_], "bf16")
+        _bf16_gemm_gate(dl(st[name]), oracle.linear(src, Wd), np.abs(src) @ np.abs(Wd).T,
+                        src.shape[1], name)
+    cqd = dl(st["cq"])
+    for name, W_ in (("q", "W_uq"), ("qI", "W_iuq")):
+        Wd = f64(Wh[W_], "bf16")
+        _bf16_gemm_gate(dl(st[name]).reshape(n, -1), oracle.linear(cqd, Wd),
+                        np.abs(cqd) @ np.abs(Wd).T, d_c, name)
+    Ww = f64(Wh["W_w"], "bf16")
+    assert np.all(np.abs(st["wI"].cpu().numpy() - oracle.linear(Hd, Ww))
+                  <= d * 2.0 ** -23 * (np.abs(Hd) @ np.abs(Ww).T)), "wI"
+    # hot path on the GPU's projections
+    kv_ref = oracle.compress(dl(st["C"]), dl(st["Z"]), Bm, tok_base=0, i_begin=0, i_end=n // m, c=c,
+                             m=m, overlap=True, gamma=gm, rope_dims=64)
+    assert_bf16_close(dl(st["kv"][0]), kv_ref, what="layer kv")
+    KI_ref = oracle.compress(dl(st["CI"]), dl(st["ZI"]), BI, tok_base=0, i_begin=0, i_end=n // m,
+                             c=cI, m=m, overlap=True, gamma=gI)
+    assert_bf16_close(dl(st["KI"][0]), KI_ref, what="layer KI")
+    sc_ref = oracle.index_scores(dl(st["qI"]), dl(st["KI"][0]), st["wI"].double().cpu().numpy(), t0=0,
+                                 m=m, ld=n // m)
+    check_topk(st["idx"][0].cpu().numpy(), st["cnt"][0].cpu().numpy(), sc_ref, t0=0, m=m, k=k,
+               what="layer top-k")
+    o_ref = oracle.attend_csa(dl(st["q"]), dl(st["kv"][0]), dl(st["local"]), st["idx"][0].cpu().numpy(),
+                              st["cnt"][0].cpu().numpy(), loc_base=0, t0=0, w=w, q_gamma=gm,
+                              kv_gamma=gm, q_norm=True, kv_norm=True, rope_dims=64)
+    od = dl(st["out"][0])
+    assert_attn_close(od, o_ref, atol=ATOL_BF16, rel_rms=REL_RMS_BF16, what="layer attention")
+    # grouped output projection on the GPU's attention output
+    Ad, Bd = f64(Wh["W_oa"], "bf16"), f64(Wh["W_ob"], "bf16")
+    ref = oracle.grouped_out_proj(od, Ad, Bd)
+    got = dl(out)
+    rel = np.sqrt(np.mean((got - ref) ** 2, axis=1)) / np.sqrt(np.mean(ref ** 2, axis=1))
+    assert np.all(rel < 0.01), f"layer output: worst row relative RMS error {rel.max():.3g}"
