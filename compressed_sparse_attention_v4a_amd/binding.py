@@ -64,6 +64,11 @@ def lib() -> ct.CDLL:
         L.v4a_csa_decode_step_workspace.argtypes = [vp]
         L.v4a_csa_decode_step.argtypes = [vp, vp, sz, vp]
         L.v4a_csa_decode_step_noalloc.argtypes = [vp, vp]
+        L.v4a_hca_decode_step_layout.restype = i32
+        L.v4a_hca_decode_step_layout.argtypes = [vp, i32, vp]
+        L.v4a_hca_decode_step_workspace.restype = sz
+        L.v4a_hca_decode_step_workspace.argtypes = [vp]
+        L.v4a_hca_decode_step.argtypes = [vp, vp, sz, vp]
         L.v4a_linear_workspace.restype = sz
         L.v4a_linear_workspace.argtypes = [i32, i32, i32]
         L.v4a_linear.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, sz, vp]
@@ -87,29 +92,68 @@ class DecodeStep(ct.Structure):
         + [(n, ct.c_void_p) for n in ("C", "Z", "B", "gamma", "CI", "ZI", "BI", "gammaI", "kv_comp",
                                       "KI", "KI_scale", "qI", "qI_scale", "wI", "q", "sink",
                                       "q_gamma", "kv_gamma", "kv_ring", "kv_new", "topk_idx",
-                                      "topk_cnt", "topk_score", "out")])
+                                      "topk_cnt", "topk_score", "out")]
+        + [("t_seq", ct.c_void_p), ("page_table", ct.c_void_p), ("max_pages", ct.c_int64),
+           ("pool_rows", ct.c_int64), ("page_entries", ct.c_int)])
+
+
+class HcaStep(ct.Structure):
+    """Mirror of v4a_hca_step (checked against the library's offsets when it loads)."""
+    _fields_ = (
+        [(n, ct.c_int64) for n in ("t", "E_cap", "n_buf", "tok_base")]
+        + [(n, ct.c_int) for n in ("batch", "n_h", "c", "m_prime", "w", "num_splits", "rope_dims")]
+        + [(n, ct.c_float) for n in ("rope_base", "eps", "scale")]
+        + [(n, ct.c_int) for n in ("tail_dt", "attn_dt")]
+        + [(n, ct.c_void_p) for n in ("C", "Z", "B", "gamma", "kv_comp", "q", "sink", "q_gamma",
+                                      "kv_gamma", "kv_ring", "kv_new", "out", "t_seq",
+                                      "page_table")]
+        + [("max_pages", ct.c_int64), ("pool_rows", ct.c_int64), ("page_entries", ct.c_int)])
+
+
+def _check_layout(fn, cls, name):
+    n = len(cls._fields_)
+    off = (ct.c_size_t * n)()
+    size = ct.c_size_t()
+    nf = fn(ct.cast(off, ct.c_void_p), n, ct.cast(ct.byref(size), ct.c_void_p))
+    mine = [getattr(cls, f).offset for f, _ in cls._fields_]
+    if nf != n or list(off) != mine or size.value != ct.sizeof(cls):
+        raise RuntimeError(f"{name} layout of the library does not match the binding")
 
 
 def _check_step_layout(L):
-    n = len(DecodeStep._fields_)
-    off = (ct.c_size_t * n)()
-    size = ct.c_size_t()
-    nf = L.v4a_decode_step_layout(ct.cast(off, ct.c_void_p), n, ct.cast(ct.byref(size), ct.c_void_p))
-    mine = [getattr(DecodeStep, f).offset for f, _ in DecodeStep._fields_]
-    if nf != n or list(off) != mine or size.value != ct.sizeof(DecodeStep):
-        raise RuntimeError("v4a_decode_step layout of the library does not match the binding")
+    _check_layout(L.v4a_decode_step_layout, DecodeStep, "v4a_decode_step")
+    _check_layout(L.v4a_hca_decode_step_layout, HcaStep, "v4a_hca_step")
+
+
+def _fill(cls, fields, what):
+    d = cls()
+    names = {f for f, _ in cls._fields_}
+    ptrs = {f for f, t in cls._fields_ if t is ct.c_void_p}
+    for key, val in fields.items():
+        if key not in names:
+            raise TypeError(f"unknown {what} field {key!r}")
+        setattr(d, key, (None if val is None else val.data_ptr()) if key in ptrs else val)
+    return d
 
 
 def decode_step(**fields) -> DecodeStep:
     """A DecodeStep from keyword arguments: tensors (or None) for the pointer fields,
     numbers for the rest (unset fields are 0 / NULL)."""
-    d = DecodeStep()
-    ptrs = {f for f, t in DecodeStep._fields_ if t is ct.c_void_p}
-    for key, val in fields.items():
-        if key not in {f for f, _ in DecodeStep._fields_}:
-            raise TypeError(f"unknown decode-step field {key!r}")
-        setattr(d, key, (None if val is None else val.data_ptr()) if key in ptrs else val)
-    return d
+    return _fill(DecodeStep, fields, "decode-step")
+
+
+def hca_step(**fields) -> HcaStep:
+    """An HcaStep from keyword arguments (as decode_step)."""
+    return _fill(HcaStep, fields, "HCA-step")
+
+
+def v4a_hca_decode_step_workspace(step: HcaStep) -> int:
+    return lib().v4a_hca_decode_step_workspace(ct.c_void_p(ct.addressof(step)))
+
+
+def v4a_hca_decode_step(step: HcaStep, ws, ws_bytes, stream=None):
+    _check("v4a_hca_decode_step", lib().v4a_hca_decode_step(
+        ct.c_void_p(ct.addressof(step)), _p(ws), ws_bytes, _s(stream)))
 
 
 def v4a_csa_decode_step_workspace(step: DecodeStep) -> int:

@@ -332,9 +332,11 @@ int v4a_hca_attn(const void* q, const void* kv_comp, const void* kv_local, int64
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+static bool serving(const v4a_decode_step* d) { return d->t_seq || d->page_table; }
+
 static v4a::IndexerPlan step_plan(const v4a_decode_step* d) {
   return v4a::indexer_plan(d->batch, 1, d->t, d->n_hI, d->cI, d->m, d->k, d->index_dt,
-                           g_policy.load());
+                           g_policy.load(), serving(d));
 }
 
 static v4a::AttnArgs step_attn(const v4a_decode_step* d) {
@@ -343,6 +345,41 @@ static v4a::AttnArgs step_attn(const v4a_decode_step* d) {
                    d->batch, d->t, 1, d->n_h, d->c, d->k, d->w, 0, d->E_cap, 0, 0, d->out,
                    d->attn_dt, v4a::kModeDecode,
                    decode_splits(d->batch, d->n_h, d->num_splits, d->k, d->w));
+}
+
+// pool rows of the selected entries (paged steps), after the indexer workspace
+static size_t step_phys_bytes(const v4a_decode_step* d) {
+  return d->page_table ? align256((size_t)d->batch * d->k * sizeof(int32_t)) : 0;
+}
+
+static int log2_exact(int64_t x) {
+  int s = 0;
+  while (((int64_t)1 << s) < x) ++s;
+  return ((int64_t)1 << s) == x ? s : -1;
+}
+
+// Validation of the serving fields shared by the CSA and HCA decode steps.
+static int check_serving(const int64_t* t_seq, const int32_t* page_table, int64_t max_pages,
+                         int64_t pool_rows, int page_entries, int64_t E_cap, bool mfma,
+                         v4a::SeqState& st) {
+  st = v4a::SeqState{};
+  if (!t_seq && !page_table) return V4A_OK;
+  REQUIRE(mfma, V4A_ENOTSUP,
+          "per-sequence positions and paged caches need bf16 rows of 512 channels, heads in "
+          "groups of 64 and RoPE 0 or 64");
+  st.tpos = t_seq;
+  if (page_table) {
+    const int sh = log2_exact(page_entries);
+    REQUIRE(page_entries >= 1 && sh >= 0, V4A_EINVAL, "page_entries must be a power of two");
+    REQUIRE(max_pages >= 1 && E_cap == max_pages * page_entries, V4A_EINVAL,
+            "E_cap must equal max_pages * page_entries");
+    REQUIRE(pool_rows >= page_entries && pool_rows <= INT32_MAX && pool_rows % page_entries == 0,
+            V4A_EINVAL, "pool_rows must be a positive multiple of page_entries below 2^31");
+    st.pages = page_table;
+    st.max_pages = max_pages;
+    st.page_shift = sh;
+  }
+  return V4A_OK;
 }
 
 int v4a_decode_step_layout(size_t* off, int n, size_t* size) {
@@ -356,7 +393,8 @@ int v4a_decode_step_layout(size_t* off, int n, size_t* size) {
       V4A_OFF(gammaI), V4A_OFF(kv_comp), V4A_OFF(KI), V4A_OFF(KI_scale), V4A_OFF(qI),
       V4A_OFF(qI_scale), V4A_OFF(wI), V4A_OFF(q), V4A_OFF(sink), V4A_OFF(q_gamma),
       V4A_OFF(kv_gamma), V4A_OFF(kv_ring), V4A_OFF(kv_new), V4A_OFF(topk_idx), V4A_OFF(topk_cnt),
-      V4A_OFF(topk_score), V4A_OFF(out)};
+      V4A_OFF(topk_score), V4A_OFF(out), V4A_OFF(t_seq), V4A_OFF(page_table), V4A_OFF(max_pages),
+      V4A_OFF(pool_rows), V4A_OFF(page_entries)};
 #undef V4A_OFF
   const int nf = (int)(sizeof(o) / sizeof(o[0]));
   for (int i = 0; i < nf && i < n && off; ++i) off[i] = o[i];
@@ -368,7 +406,8 @@ size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d) {
   if (!d || d->batch < 1 || d->m < 1 || d->k < 1 || d->t < 0 || d->n_h < 1 || d->c < 2 ||
       d->num_splits < 0 || d->num_splits > 64)
     return 0;
-  return align256(step_plan(d).total) + v4a::attn_workspace(step_attn(d), g_policy.load());
+  return align256(step_plan(d).total) + step_phys_bytes(d) +
+         v4a::attn_workspace(step_attn(d), g_policy.load());
 }
 
 int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream) {
@@ -385,13 +424,20 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   REQUIRE(d->num_splits >= 0 && d->num_splits <= 64, V4A_EINVAL, "num_splits must be in [0, 64]");
   REQUIRE(d->attn_dt == V4A_F32 || d->attn_dt == V4A_BF16, V4A_ENOTSUP,
           "attention dtype must be F32 or BF16");
-  // the three stages' own checks, exactly as the separate calls make them
+  const bool ragged = d->t_seq != nullptr;
+  // the stages' own checks, as the separate calls make them (per-sequence tails: the
+  // fixed two-block buffer of every sequence, checked against the bound t)
+  REQUIRE(!ragged || d->n_buf == 2 * (int64_t)d->m, V4A_EINVAL,
+          "with t_seq the tail buffers hold 2m rows per sequence (n_buf = %d)", 2 * d->m);
+  const int64_t tb = ragged ? (int64_t)d->m * (d->t / d->m) - d->m : d->tok_base;
   v4a::CompressArgs cm, ci;
-  int rc = compress_prepare(d->C, d->Z, d->tail_dt, d->B, d->batch, d->n_buf, d->tok_base, d->t, 1,
-                            d->c, d->m, 1, d->gamma, d->eps, d->rope_dims, d->rope_base,
-                            d->kv_comp, nullptr, d->attn_dt, d->E_cap, cm);
+  int rc = compress_prepare(d->C, d->Z, d->tail_dt, d->B, d->batch, d->n_buf,
+                            ragged ? (tb > 0 ? tb : 0) : d->tok_base, ragged ? 0 : d->t,
+                            ragged ? 0 : 1, d->c, d->m, 1, d->gamma, d->eps, d->rope_dims,
+                            d->rope_base, d->kv_comp, nullptr, d->attn_dt, d->E_cap, cm);
   if (rc != V4A_OK) return rc;
-  rc = compress_prepare(d->CI, d->ZI, d->tail_dt, d->BI, d->batch, d->n_buf, d->tok_base, d->t, 1,
+  rc = compress_prepare(d->CI, d->ZI, d->tail_dt, d->BI, d->batch, d->n_buf,
+                        ragged ? (tb > 0 ? tb : 0) : d->tok_base, ragged ? 0 : d->t, ragged ? 0 : 1,
                         d->cI, d->m, 1, d->gammaI, d->eps, d->rope_dims_I, d->rope_base, d->KI,
                         d->KI_scale, d->index_dt, d->E_cap, ci);
   if (rc != V4A_OK) return rc;
@@ -405,16 +451,35 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   const v4a::IndexerPlan p = step_plan(d);
   v4a::AttnArgs aa = step_attn(d);
   const int policy = g_policy.load();
-  const size_t ws_i = align256(p.total), need = ws_i + v4a::attn_workspace(aa, policy);
+  v4a::SeqState st;
+  rc = check_serving(d->t_seq, d->page_table, d->max_pages, d->pool_rows, d->page_entries, d->E_cap,
+                     policy == 0 && v4a::attn_mfma_supported(aa), st);
+  if (rc != V4A_OK) return rc;
+  const size_t ws_i = align256(p.total), ws_p = step_phys_bytes(d);
+  const size_t need = ws_i + ws_p + v4a::attn_workspace(aa, policy);
   REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
   REQUIRE(ws && aligned(ws, 256), V4A_EINVAL, "workspace must be 256-byte aligned");
+  int32_t* phys = d->page_table ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + ws_i) : nullptr;
+  if (ragged) {
+    // one entry slot per sequence: emitted or not by the sequence's own position
+    cm.seq = st;
+    ci.seq = st;
+    cm.n_entries = ci.n_entries = 1;
+  } else if (d->page_table) {
+    cm.seq = st;
+    ci.seq = st;
+  }
   v4a::IndexerArgs ia{};
   ia.qI = d->qI; ia.qI_scale = d->qI_scale; ia.KI = d->KI; ia.KI_scale = d->KI_scale; ia.wI = d->wI;
   ia.topk_idx = d->topk_idx; ia.topk_cnt = d->topk_cnt; ia.topk_score = d->topk_score;
   ia.t0 = d->t; ia.E_cap = d->E_cap; ia.batch = d->batch; ia.T = 1; ia.n_hI = d->n_hI;
   ia.cI = d->cI; ia.m = d->m; ia.k = d->k; ia.dt = d->index_dt;
+  ia.seq = st;
+  ia.phys = phys;
+  aa.seq = st;
+  if (phys) aa.idx = phys;  // the attention gathers pool rows
   hipStream_t s = (hipStream_t)stream;
-  void* ws_a = reinterpret_cast<char*>(ws) + ws_i;
+  void* ws_a = reinterpret_cast<char*>(ws) + ws_i + ws_p;
   hipError_t e;
   if (v4a::decode_front_supported(cm, ci, aa, policy)) {
     // tail compressions, window prep and ring insert in one launch
@@ -428,3 +493,83 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   if (e == hipSuccess) e = v4a::launch_attention(aa, ws_a, policy, s);
   return hip_status(e, "v4a_csa_decode_step");
 }
+
+// ---- HCA decode step ---------------------------------------------------------------
+
+static v4a::AttnArgs hca_step_attn(const v4a_hca_step* d) {
+  // candidate list of the latest position: every completed entry plus the window
+  const int64_t N = (d->t + 1) / (d->m_prime > 0 ? d->m_prime : 1) + d->w;
+  return attn_args(d->q, d->kv_comp, d->kv_ring, d->kv_ring, d->kv_new, nullptr, nullptr, d->sink,
+                   d->q_gamma, d->kv_gamma, d->eps, d->rope_dims, d->rope_base, d->scale, d->batch,
+                   d->t, 1, d->n_h, d->c, 0, d->w, d->m_prime, d->E_cap, 0, 0, d->out, d->attn_dt,
+                   v4a::kModeHCADecode,
+                   decode_splits(d->batch, d->n_h, d->num_splits, (int)(N - d->w), d->w));
+}
+
+extern "C" {
+
+int v4a_hca_decode_step_layout(size_t* off, int n, size_t* size) {
+#define V4A_OFF(f) offsetof(v4a_hca_step, f)
+  const size_t o[] = {
+      V4A_OFF(t), V4A_OFF(E_cap), V4A_OFF(n_buf), V4A_OFF(tok_base), V4A_OFF(batch), V4A_OFF(n_h),
+      V4A_OFF(c), V4A_OFF(m_prime), V4A_OFF(w), V4A_OFF(num_splits), V4A_OFF(rope_dims),
+      V4A_OFF(rope_base), V4A_OFF(eps), V4A_OFF(scale), V4A_OFF(tail_dt), V4A_OFF(attn_dt),
+      V4A_OFF(C), V4A_OFF(Z), V4A_OFF(B), V4A_OFF(gamma), V4A_OFF(kv_comp), V4A_OFF(q),
+      V4A_OFF(sink), V4A_OFF(q_gamma), V4A_OFF(kv_gamma), V4A_OFF(kv_ring), V4A_OFF(kv_new),
+      V4A_OFF(out), V4A_OFF(t_seq), V4A_OFF(page_table), V4A_OFF(max_pages), V4A_OFF(pool_rows),
+      V4A_OFF(page_entries)};
+#undef V4A_OFF
+  const int nf = (int)(sizeof(o) / sizeof(o[0]));
+  for (int i = 0; i < nf && i < n && off; ++i) off[i] = o[i];
+  if (size) *size = sizeof(v4a_hca_step);
+  return nf;
+}
+
+size_t v4a_hca_decode_step_workspace(const v4a_hca_step* d) {
+  if (!d || d->batch < 1 || d->m_prime < 1 || d->t < 0 || d->n_h < 1 || d->c < 2 || d->w < 1 ||
+      d->num_splits < 0 || d->num_splits > 64)
+    return 0;
+  return v4a::attn_workspace(hca_step_attn(d), g_policy.load());
+}
+
+int v4a_hca_decode_step(const v4a_hca_step* d, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(d, V4A_EINVAL, "null step description");
+  REQUIRE(d->t >= 0 && d->t < INT32_MAX, V4A_EINVAL, "t out of range");
+  REQUIRE(d->m_prime >= 1, V4A_EINVAL, "m_prime must be >= 1");
+  REQUIRE(d->num_splits >= 0 && d->num_splits <= 64, V4A_EINVAL, "num_splits must be in [0, 64]");
+  int rc = check_attn_common(d->q, d->kv_comp, d->out, d->n_h, d->c, d->rope_dims, d->w, d->attn_dt,
+                             d->batch, d->eps);
+  if (rc != V4A_OK) return rc;
+  REQUIRE(d->kv_ring, V4A_EINVAL, "null kv_ring");
+  const bool ragged = d->t_seq != nullptr;
+  REQUIRE(!ragged || d->n_buf == d->m_prime, V4A_EINVAL,
+          "with t_seq the tail buffers hold m' rows per sequence (n_buf = %d)", d->m_prime);
+  REQUIRE(d->E_cap >= (d->t + 1) / d->m_prime && d->E_cap >= 1, V4A_EINVAL,
+          "E_cap smaller than the visible entries");
+  v4a::AttnArgs aa = hca_step_attn(d);
+  const int policy = g_policy.load();
+  REQUIRE(policy == 0 && v4a::attn_mfma_supported(aa), V4A_ENOTSUP,
+          "HCA decode needs bf16 rows of 512 channels, heads in groups of 64 and RoPE 0 or 64");
+  v4a::SeqState st;
+  rc = check_serving(d->t_seq, d->page_table, d->max_pages, d->pool_rows, d->page_entries, d->E_cap,
+                     true, st);
+  if (rc != V4A_OK) return rc;
+  const int64_t tb = ragged ? (int64_t)d->m_prime * (d->t / d->m_prime) : d->tok_base;
+  v4a::CompressArgs cm;
+  rc = compress_prepare(d->C, d->Z, d->tail_dt, d->B, d->batch, d->n_buf, ragged ? tb : d->tok_base,
+                        ragged ? 0 : d->t, ragged ? 0 : 1, d->c, d->m_prime, 0, d->gamma, d->eps,
+                        d->rope_dims, d->rope_base, d->kv_comp, nullptr, d->attn_dt, d->E_cap, cm);
+  if (rc != V4A_OK) return rc;
+  const size_t need = v4a::attn_workspace(aa, policy);
+  REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
+  REQUIRE(ws && aligned(ws, 256), V4A_EINVAL, "workspace must be 256-byte aligned");
+  cm.seq = st;
+  if (ragged) cm.n_entries = 1;
+  aa.seq = st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = v4a::launch_compress(cm, s);  // the entry a completed block emits
+  if (e == hipSuccess) e = v4a::launch_attention(aa, ws, policy, s);
+  return hip_status(e, "v4a_hca_decode_step");
+}
+
+}  // extern "C"

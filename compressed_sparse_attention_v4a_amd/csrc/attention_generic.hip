@@ -329,7 +329,7 @@ __global__ __launch_bounds__(64 * kMergeHeads) void attn_merge_kernel(AttnArgs a
       float x0 = acc[e] * inv, x1 = acc[e + 1] * inv;
       if (a.rope_dims > 0 && d >= r0 && d < c) {
         float cs, sn;
-        rope_cs(-(double)a.t0, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
+        rope_cs(-(double)(a.seq.tpos ? a.seq.tpos[b] : a.t0), a.rope.inv_freq[(d - r0) >> 1], cs, sn);
         const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
         x0 = y0;
         x1 = y1;

@@ -146,6 +146,13 @@ struct MqaArgs {
   int batch, T, n_h, k, w, m_prime, rope_dims, mode, splits, split_len;
   float eps, rope_base, qscale;
   RopeTab rope;
+  // decode serving state: per-sequence positions (tpos) and paged compressed rows.  With
+  // pages, kvc is a pool: a CSA list (idx) already holds pool rows, a dense HCA prefix is
+  // translated through the block table here.
+  const int64_t* tpos;
+  const int32_t* pages;
+  int64_t max_pages;
+  int page_shift;
 };
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
@@ -193,7 +200,9 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = wv >> 2, cc = (wv >> 1) & 1, kx = wv & 1;
   const int hl = lane >> 5, l32 = lane & 31;
-  const bool decode = MODE == kModeDecode;
+  constexpr bool kDec = MODE == kModeDecode || MODE == kModeHCADecode;
+  const bool decode = kDec;
+  constexpr bool dense = MODE == kModeHCA || MODE == kModeHCADecode;  // every completed entry
   const int nq = decode ? 1 : a.T;
   const int hgroups = a.n_h / kHG;
   const int64_t n_items = decode ? (int64_t)a.batch * hgroups * a.splits : (int64_t)a.batch * hgroups * a.T;
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       it.hgrp = (int)(r % hgroups);
       it.b = (int)(r / hgroups);
       it.qi = 0;
-      it.t = a.t0;
+      it.t = a.tpos ? a.tpos[it.b] : a.t0;
     } else {
       const int64_t bh = (int64_t)a.batch * hgroups;
       const int64_t u = j / bh, r = j % bh;
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       it.split = 0;
       it.t = a.t0 + it.qi;
     }
-    if (MODE == kModeHCA) {
+    if constexpr (dense) {
       it.ncomp = (it.t + 1) / a.m_prime;
     } else {
       it.ncomp = min(max(a.cnt[(int64_t)it.b * nq + it.qi], 0), a.k);
@@ -269,8 +278,12 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   // candidate r0 (row r0 + 8 wv + j), loaded a chunk ahead into a register.  Clamped to
   // the top-k row; the value is only used for rows inside the compressed part.
   auto load_raw = [&](const Item& it, int64_t r0) -> int {
-    if constexpr (MODE == kModeHCA) {
-      return 0;
+    if constexpr (dense) {
+      // paged: the block-table entry of the row's page (rows inside the compressed prefix)
+      if (!a.pages) return 0;
+      const int64_t u = it.ub + r0 + kRowsPerWave * wv + (lane & 7);
+      const int64_t s = u < it.ncomp ? u : 0;
+      return a.pages[(int64_t)it.b * a.max_pages + (s >> a.page_shift)];
     } else {
       if (a.k <= 0) return 0;
       const int32_t* irow = a.idx + ((int64_t)it.b * nq + it.qi) * a.k;
@@ -284,22 +297,28 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   // Address of row r0 + 8 wv + (lane & 7) of the candidate list (lanes j < 8 matter):
   // each row load of gather_row takes it from lane j into scalar registers (the lane
   // offset stays a 32-bit vector operand of the scalar-base form of the load)
+  // window rows: prefill workspace row = position - lrow_base; decode row r = position lo + r
+  // of the sequence's own window
+  const int64_t kv_bstride = a.pages ? 0 : a.E_cap;  // a pool has no per-sequence stride
+  const int64_t kv_rows = a.pages ? ((int64_t)1 << 31) - 1 : a.E_cap;
   auto row_addr = [&](const Item& it, int64_t r0, int raw) -> uint64_t {
-    const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)it.b * a.E_cap * kC);
+    const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)it.b * kv_bstride * kC);
     const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)it.b * a.n_lrows * kC);
-    int myid = -1 - (int)(it.t - a.lrow_base);  // past the list end: the query's own window row
+    const int64_t wbase = decode ? it.lo : a.lrow_base;
+    int myid = -1 - (int)(it.t - wbase);  // past the list end: the query's own window row
     const int64_t rr = r0 + kRowsPerWave * wv + (lane & 7);
     if (rr < it.nrows) {
       const int64_t u = it.ub + rr;
       if (u < it.ncomp) {
-        if (MODE == kModeHCA) {
-          myid = (int)u;
+        if constexpr (dense) {
+          myid = a.pages ? (int)(((int64_t)raw << a.page_shift) | (u & (((int64_t)1 << a.page_shift) - 1)))
+                         : (int)u;
         } else {
           // out-of-range indices must not fault
-          myid = (int)min(max((int64_t)raw, (int64_t)0), a.E_cap - 1);
+          myid = (int)min(max((int64_t)raw, (int64_t)0), kv_rows - 1);
         }
       } else {
-        myid = -1 - (int)(it.lo + (u - it.ncomp) - a.lrow_base);
+        myid = -1 - (int)(it.lo + (u - it.ncomp) - wbase);
       }
     }
     return myid >= 0 ? (uint64_t)kvc_b + (uint64_t)myid * kRowBytes
@@ -468,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     auto overflowed = [&]() -> bool {
       if (!uni(flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3] | flag_s[4] | flag_s[5] | flag_s[6] | flag_s[7]))
         return false;
-      if constexpr (MODE == kModeDecode) m_ref = fmaxf(m_ref, tile_max());
+      if constexpr (kDec) m_ref = fmaxf(m_ref, tile_max());
       return true;
     };
 
@@ -570,13 +589,13 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax), false, false);
           lmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * qinv;  // qinv > 0: order kept
         }
-        if constexpr (MODE == kModeDecode) mx_run = fmaxf(mx_run, lmax);
+        if constexpr (kDec) mx_run = fmaxf(mx_run, lmax);
         if (c == 0) {
           // reference maximum: this chunk's maximum over the tile's four waves
           if (hl == 0) mx_s[wv][l32] = lmax;
           wait_lgkmcnt<0>();
           block_sync();
-          if constexpr (MODE == kModeDecode) {
+          if constexpr (kDec) {
             m_ref = fmaxf(m_ref, tile_max());  // raised by a restart
           } else {
             m_ref = tile_max();
@@ -644,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       {
         const bool any = __ballot(ovf) != 0;
         if (lane == 0) flag_s[wv] = any ? 1 : 0;
-        if constexpr (MODE == kModeDecode) {
+        if constexpr (kDec) {
           if (hl == 0) mx_s[wv][l32] = mx_run;
         }
       }
@@ -762,7 +781,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     {
       f32x16 O[2][2];
       float l_part;
-      if constexpr (MODE == kModeDecode) {
+      if constexpr (kDec) {
         // decode splits restart instead of leaving the item to the exact kernel (which would
         // cost every decode call a launch): run() has raised the reference; the gather in
         // flight lands, chunk 0 is gathered again and the loop starts over.  Each restart
@@ -826,24 +845,33 @@ __global__ __launch_bounds__(256) void decode_front_kernel(CompressArgs cm, Comp
 
 bool attn_mfma_supported(const AttnArgs& a) {
   return a.dt == kBF16 && a.c == kC && a.n_h % kHG == 0 && (a.rope_dims == 0 || a.rope_dims == 64) &&
-         (a.mode == kModeHCA || (int64_t)a.k + a.w <= kMaxCand);
+         (a.mode == kModeHCA || a.mode == kModeHCADecode || (int64_t)a.k + a.w <= kMaxCand);
 }
 
+static bool is_decode(const AttnArgs& a) { return a.mode == kModeDecode || a.mode == kModeHCADecode; }
+
 static int64_t local_rows(const AttnArgs& a) {
-  if (a.mode == kModeDecode) return a.w;
+  if (is_decode(a)) return a.w;
   const int64_t lo = a.t0 - a.w + 1 > 0 ? a.t0 - a.w + 1 : 0;
   return a.t0 + a.T - lo;
 }
 
+// longest candidate list of a decode call: k + w (CSA), or every completed entry of the
+// latest position plus w (HCA)
+int64_t decode_max_list(const AttnArgs& a) {
+  if (a.mode == kModeHCADecode) return (a.t0 + 1) / a.m_prime + a.w;
+  return (int64_t)a.k + a.w;
+}
+
 static int decode_split_len(const AttnArgs& a) {
-  const int64_t N = (int64_t)a.k + a.w;
+  const int64_t N = decode_max_list(a);
   int64_t per = (N + a.num_splits - 1) / a.num_splits;
   return (int)per;
 }
 
 // Work items of the matrix-core kernel (64 heads of one query, or of one decode split).
 static int64_t mfma_items(const AttnArgs& a) {
-  const int64_t per = a.mode == kModeDecode ? (a.num_splits > 1 ? a.num_splits : 1) : a.T;
+  const int64_t per = is_decode(a) ? (a.num_splits > 1 ? a.num_splits : 1) : a.T;
   return (int64_t)a.batch * (a.n_h / kHG) * per;
 }
 
@@ -851,7 +879,7 @@ static int64_t mfma_items(const AttnArgs& a) {
 size_t attn_mfma_workspace(const AttnArgs& a) {
   size_t loc = ((size_t)a.batch * local_rows(a) * kC * 2 + 255) / 256 * 256;
   size_t part = 0;
-  if (a.mode == kModeDecode && a.num_splits > 1)
+  if (is_decode(a) && a.num_splits > 1)
     part = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
   const size_t redo = (size_t)(1 + mfma_items(a)) * sizeof(int);
   return loc + part + redo;
@@ -874,7 +902,7 @@ static MfmaWs mfma_ws(const AttnArgs& a, void* ws) {
   const size_t loc_bytes = ((size_t)a.batch * nl_rows * kC * 2 + 255) / 256 * 256;
   w.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + loc_bytes);
   size_t part_bytes = 0;
-  if (a.mode == kModeDecode && a.num_splits > 1)
+  if (is_decode(a) && a.num_splits > 1)
     part_bytes = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
   w.redo = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + loc_bytes + part_bytes);
   return w;
@@ -891,7 +919,8 @@ static LocalPrepArgs prep_args(const AttnArgs& a, const MfmaWs& w) {
   lp.rope_base = a.rope_base;
   lp.rope = a.rope;
   lp.w = a.w;
-  if (a.mode == kModeDecode) {
+  lp.tpos = a.seq.tpos;
+  if (is_decode(a)) {
     lp.src = reinterpret_cast<const uint16_t*>(a.kv_local);
     lp.ring = reinterpret_cast<uint16_t*>(a.kv_ring);
     lp.kv_new = reinterpret_cast<const uint16_t*>(a.kv_new);
@@ -988,13 +1017,20 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   m.qscale = a.scale * kLog2e;
   m.rope = a.rope;
   m.batch = a.batch;
+  m.tpos = a.seq.tpos;
+  m.pages = a.seq.pages;
+  m.max_pages = a.seq.max_pages;
+  m.page_shift = a.seq.page_shift;
   // one workgroup per item (64 heads of one query, or of one decode split)
   const int64_t hgroups = a.n_h / kHG;
-  if (a.mode == kModeDecode) {
+  if (is_decode(a)) {
     m.splits = a.num_splits > 1 ? a.num_splits : 1;
-    m.split_len = m.splits > 1 ? decode_split_len(a) : (a.k + a.w);
+    m.split_len = m.splits > 1 ? decode_split_len(a) : (int)decode_max_list(a);
     const int64_t items = (int64_t)a.batch * hgroups * m.splits;
-    hipLaunchKernelGGL(mqa_mfma_kernel<kModeDecode>, dim3((unsigned)items), dim3(kThreads), 0, s, m);
+    if (a.mode == kModeHCADecode)
+      hipLaunchKernelGGL(mqa_mfma_kernel<kModeHCADecode>, dim3((unsigned)items), dim3(kThreads), 0, s, m);
+    else
+      hipLaunchKernelGGL(mqa_mfma_kernel<kModeDecode>, dim3((unsigned)items), dim3(kThreads), 0, s, m);
     err = hipGetLastError();
     // decode splits restart in place on a reference overflow: no recomputation launch
     if (err != hipSuccess || m.splits <= 1) return err;

@@ -35,8 +35,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   const int tid = threadIdx.x;
   const int g = tid % G, p = tid / G;
   const bool active = p < P;
-  const int64_t i = a.i_begin + blockIdx.x;
   const int b = blockIdx.y;
+  const SlotEntry se = slot_entry(a, b, blockIdx.x);
+  if (!se.emit) return;  // uniform over the workgroup
+  const int64_t i = se.i;
   const int width = a.overlap ? 2 * c : c;
   const int npos = (a.overlap && i > 0) ? 2 * m : m;
   const Tin* Cb = reinterpret_cast<const Tin*>(a.C) + (int64_t)b * a.n_buf * width;
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
         if (u < npos) {
           const bool sa = u < m;
           const int64_t pos = sa ? (int64_t)m * i + u : (int64_t)m * (i - 1) + (u - m);
-          const int64_t row = pos - a.tok_base;
+          const int64_t row = pos - se.tok_base;
           const int64_t off = row * width + (sa ? 0 : c) + ch0;
           Vec<Tin>::load(Zb, off, lg[r]);
           Vec<Tin>::load(Cb, off, cv[r]);
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
     }
   }
 
-  const int64_t orow = (int64_t)b * a.E_cap + i;
+  const int64_t orow = cache_row(a.seq, a.E_cap, b, i);
   if (a.out_dt == kF32) {
     if (owner) {
       float* o = reinterpret_cast<float*>(a.out) + orow * c + g * VEC;

@@ -43,6 +43,28 @@ struct Vec<uint16_t> {
 // RMSNorm weights of a call without RMSNorm (read, never applied; VEC <= 8)
 __device__ __attribute__((aligned(16))) const float kOnes[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
 
+// Entry `slot` of the call for sequence b: its index, whether it is emitted, and the
+// position of row 0 of the sequence's C/Z buffer.  With per-sequence positions each
+// sequence emits at most one entry (slot 0), the one its new token completes.
+struct SlotEntry {
+  int64_t i, tok_base;
+  bool emit;
+};
+__device__ __forceinline__ SlotEntry slot_entry(const CompressArgs& a, int b, int64_t slot) {
+  SlotEntry e;
+  if (a.seq.tpos) {
+    const int64_t t = a.seq.tpos[b];
+    e.i = t / a.m;
+    e.emit = slot == 0 && (t + 1) % a.m == 0;
+    e.tok_base = (int64_t)a.m * e.i - (a.overlap ? a.m : 0);
+  } else {
+    e.emit = slot < a.n_entries;
+    e.i = a.i_begin + (e.emit ? slot : 0);
+    e.tok_base = a.tok_base;
+  }
+  return e;
+}
+
 // One wave: entries 64 / G * vblock .. of sequence b; lane = lane of the wave.
 template <typename Tin, int G>
 __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_t vblock, int b, int lane) {
@@ -51,8 +73,9 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
   const int c = a.c, m = a.m;
   const int g = lane % G, ch0 = g * VEC;
   const int64_t slot = vblock * (64 / G) + lane / G;
-  const bool valid = slot < a.n_entries;
-  const int64_t i = a.i_begin + (valid ? slot : 0);
+  const SlotEntry se = slot_entry(a, b, slot);
+  const bool valid = se.emit;
+  const int64_t i = se.i;
   const int width = a.overlap ? 2 * c : c;
   const int npos = (a.overlap && i > 0) ? 2 * m : m;
   const Tin* Cb = reinterpret_cast<const Tin*>(a.C) + (int64_t)b * a.n_buf * width;
@@ -80,7 +103,7 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
     const int uu = u < npos ? u : 0;
     const bool sa = uu < m;
     const int64_t pos = sa ? (int64_t)m * i + uu : (int64_t)m * (i - 1) + (uu - m);
-    const int64_t off = (pos - a.tok_base) * width + (sa ? 0 : c) + ch0;
+    const int64_t off = (pos - se.tok_base) * width + (sa ? 0 : c) + ch0;
     Vec<Tin>::load(Zb, off, lg[u]);
     Vec<Tin>::load(Cb, off, cv[u]);
     const float* brow = a.B + (int64_t)uu * c + ch0;  // B^a rows 0..m-1, B^b rows m..2m-1
@@ -141,7 +164,7 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
     }
   }
 
-  const int64_t orow = (int64_t)b * a.E_cap + i;
+  const int64_t orow = valid ? cache_row(a.seq, a.E_cap, b, i) : 0;
   if (a.out_dt == kF32) {
     if (valid) {
       float* o = reinterpret_cast<float*>(a.out) + orow * c + ch0;

@@ -21,6 +21,13 @@ namespace v4a {
 
 namespace {
 
+// Selected entry e (or -1 padding) into slot pos of query row q, and, for paged caches,
+// its pool row into the parallel list the attention gathers from.
+__device__ __forceinline__ void write_sel(const IndexerArgs& a, int b, int64_t q, int pos, int32_t e) {
+  a.topk_idx[q * a.k + pos] = e;
+  if (a.phys) a.phys[q * a.k + pos] = e >= 0 ? (int32_t)cache_row(a.seq, a.E_cap, b, e) : -1;
+}
+
 constexpr int kScoreThreads = 256;
 constexpr int kHeadChunk = 32;
 
@@ -37,7 +44,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_scores_kernel(IndexerArgs
                                                                       int64_t ld) {
   extern __shared__ float sq[];  // [n_hI][cI] decoded query, then [n_hI] weights
   const int j = blockIdx.x, b = blockIdx.z;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t s = (int64_t)blockIdx.y * kScoreThreads + threadIdx.x;
   const int nh = a.n_hI, cI = a.cI;
@@ -59,7 +66,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_scores_kernel(IndexerArgs
   for (int h = threadIdx.x; h < nh; h += kScoreThreads) sw[h] = a.wI[qrow0 + h];
   __syncthreads();
   if (s >= E) return;
-  const int64_t krow = (int64_t)b * a.E_cap + s;
+  const int64_t krow = cache_row(a.seq, a.E_cap, b, s);
   float ks = 1.0f;
   if (a.dt == kFP8) ks = reinterpret_cast<const float*>(a.KI_scale)[krow];
   float score = 0.0f;
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(256) void topk_tile_kernel(IndexerArgs a, const flo
   __shared__ uint32_t hist[768];
   __shared__ int sh[16];
   const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t s0 = (int64_t)tl * tile;
   const int N = (int)max((int64_t)0, min((int64_t)tile, E - s0));
@@ -104,10 +111,9 @@ __global__ __launch_bounds__(256) void topk_tile_kernel(IndexerArgs a, const flo
   auto get = [&](int i) { return score_key(srow[i]); };
   if (n_tiles == 1) {
     const int k = a.k;
-    int32_t* oidx = a.topk_idx + q * k;
     float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
     auto emit = [&](int pos, int i, uint32_t key) {
-      oidx[pos] = (int32_t)(s0 + i);
+      write_sel(a, b, q, pos, (int32_t)(s0 + i));
       if (osc) osc[pos] = key_score(key);
     };
     const int n = min(N, k);
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(256) void topk_tile_kernel(IndexerArgs a, const flo
       block_select_emit(get, N, k, sel, sh, emit);
     }
     for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
-      oidx[p] = -1;
+      write_sel(a, b, q, p, -1);
       if (osc) osc[p] = 0.0f;
     }
     if (threadIdx.x == 0) a.topk_cnt[q] = n;
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_t
   __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int j = blockIdx.x, b = blockIdx.y;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t q = (int64_t)b * a.T + j;
   const int k = a.k;
@@ -158,11 +164,10 @@ __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_t
   const int N = n_tiles * kc;
   const uint32_t* ck = cand_key + q * N;
   const int32_t* ci = cand_idx + q * N;
-  int32_t* oidx = a.topk_idx + q * k;
   float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
   auto get = [&](int i) { return ck[i]; };
   auto emit = [&](int pos, int i, uint32_t key) {
-    oidx[pos] = ci[i];
+    write_sel(a, b, q, pos, ci[i]);
     if (osc) osc[pos] = key_score(key);
   };
   if (n > 0) {
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(1024) void topk_merge_kernel(IndexerArgs a, int n_t
     block_select_emit(get, N, n, sel, sh, emit);
   }
   for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
-    oidx[p] = -1;
+    write_sel(a, b, q, p, -1);
     if (osc) osc[p] = 0.0f;
   }
   if (threadIdx.x == 0) a.topk_cnt[q] = n;
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(THREADS) void topk_tile_reg_kernel(IndexerArgs a, c
   __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int j = blockIdx.x, tl = blockIdx.y, b = blockIdx.z;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t s0 = (int64_t)tl * kRegTile;
   const int N = (int)max((int64_t)0, min((int64_t)kRegTile, E - s0));
@@ -209,13 +214,12 @@ __global__ __launch_bounds__(THREADS) void topk_tile_reg_kernel(IndexerArgs a, c
   const bool final_out = n_tiles == 1;
   const int want = final_out ? a.k : kc;
   const int n = min(N, want);
-  int32_t* oidx = a.topk_idx + q * a.k;
   float* osc = a.topk_score ? a.topk_score + q * a.k : nullptr;
   uint32_t* ck = cand_key + (q * n_tiles + tl) * kc;
   int32_t* ci = cand_idx + (q * n_tiles + tl) * kc;
   auto emit = [&](int pos, int i, uint32_t kk) {
     if (final_out) {
-      oidx[pos] = (int32_t)(s0 + i);
+      write_sel(a, b, q, pos, (int32_t)(s0 + i));
       if (osc) osc[pos] = key_score(kk);
     } else {
       ck[pos] = kk;
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(THREADS) void topk_tile_reg_kernel(IndexerArgs a, c
   reg_select_emit(key, N, sel, sh, emit);
   for (int p = n + threadIdx.x; p < want; p += blockDim.x) {
     if (final_out) {
-      oidx[p] = -1;
+      write_sel(a, b, q, p, -1);
       if (osc) osc[p] = 0.0f;
     } else {
       ck[p] = 0u;  // below every real score's key
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int
   __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int j = blockIdx.x, b = blockIdx.y;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t q = (int64_t)b * a.T + j;
   const int k = a.k;
@@ -255,7 +259,6 @@ __global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int
   const int N = n_tiles * kc;
   const uint32_t* ck = cand_key + q * N;
   const int32_t* ci = cand_idx + q * N;
-  int32_t* oidx = a.topk_idx + q * k;
   float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
   const int base = threadIdx.x * PER;
   uint32_t key[PER];
@@ -273,13 +276,13 @@ __global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int
     // exactly n real candidates are wanted; padding keys (0) rank below all of them
     const Selection sel = reg_radix_select(key, N, n, hist, sh);
     auto emit = [&](int pos, int i, uint32_t kk) {
-      oidx[pos] = ci[i];
+      write_sel(a, b, q, pos, ci[i]);
       if (osc) osc[pos] = key_score(kk);
     };
     reg_select_emit(key, N, sel, sh, emit);
   }
   for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
-    oidx[p] = -1;
+    write_sel(a, b, q, p, -1);
     if (osc) osc[p] = 0.0f;
   }
   if (threadIdx.x == 0) a.topk_cnt[q] = n;
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(IndexerArgs a, const f
   __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   const int sl = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t q = (int64_t)b * a.T + j;
   // lower bound L from the group maxima (every workgroup of the row computes the same)
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a
   __shared__ int sh[40];
   __shared__ int pre[65];  // candidate offset of every slice (n_slices <= 64)
   const int j = blockIdx.x, b = blockIdx.y;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t q = (int64_t)b * a.T + j;
   const int k = a.k;
@@ -394,7 +397,6 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a
   const int total = pre[n_slices];
   // candidates >= min(k, E) by construction; the minimum keeps the selection in range
   const int n = (int)min(min((int64_t)k, E), (int64_t)total);
-  int32_t* oidx = a.topk_idx + q * k;
   float* osc = a.topk_score ? a.topk_score + q * k : nullptr;
   // candidate p of the row (slice order = index order)
   auto at = [&](int p) -> int64_t {
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a
     Selection sel{0u, kFinalThreads * kFinalPer};  // every candidate (total == n)
     if (total > n) sel = reg_radix_select(key, total, n, hist, sh, 0, per);
     reg_select_emit_slot(key, total, sel, sh, [&](int pos, int v, uint32_t kk) {
-      oidx[pos] = ix[v];
+      write_sel(a, b, q, pos, ix[v]);
       if (osc) osc[pos] = key_score(kk);
     }, per);
   } else {
@@ -457,12 +459,12 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a
     auto get = [&](int p) -> uint32_t { return cand_key[at(p)]; };
     const Selection sel = block_radix_select(get, total, n, hist, sh);
     block_select_emit(get, total, n, sel, sh, [&](int pos, int p, uint32_t kk) {
-      oidx[pos] = cand_idx[at(p)];
+      write_sel(a, b, q, pos, cand_idx[at(p)]);
       if (osc) osc[pos] = key_score(kk);
     });
   }
   for (int p = n + threadIdx.x; p < k; p += blockDim.x) {
-    oidx[p] = -1;
+    write_sel(a, b, q, p, -1);
     if (osc) osc[p] = 0.0f;
   }
   if (threadIdx.x == 0) a.topk_cnt[q] = n;
@@ -478,7 +480,7 @@ hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64
                                       uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s);
 
 IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k, int dt,
-                         int policy) {
+                         int policy, bool serving) {
   IndexerPlan p{};
   const int64_t Emax = (t0 + T) / m;
   p.ld = (Emax + 63) / 64 * 64;
@@ -491,7 +493,7 @@ IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, 
   p.n_tiles = (int)((Emax + p.tile - 1) / p.tile);
   if (p.n_tiles < 1) p.n_tiles = 1;
   p.kc = k < p.tile ? k : p.tile;
-  p.fused = policy == 0 && indexer_fused_supported(Emax, T, n_hI, cI, k, dt);
+  p.fused = policy == 0 && !serving && indexer_fused_supported(Emax, T, n_hI, cI, k, dt);
   p.mfma_scan = policy == 0 && indexer_mfma_supported(T, n_hI, cI, dt);
   if (p.fused) {
     p.score_bytes = p.cand_bytes = p.total = 0;

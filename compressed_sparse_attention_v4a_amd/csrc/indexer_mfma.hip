@@ -535,7 +535,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, jj = lane & 15;
   const int j = blockIdx.y, b = blockIdx.z;
-  const int64_t t = a.t0 + j;
+  const int64_t t = query_pos(a, b, j);
   const int64_t E = (t + 1) / a.m;
   const int64_t e0 = (int64_t)blockIdx.x * kScanEntries + wv * (kScanEntries / 4);
   if (e0 >= E) return;
@@ -591,7 +591,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   float* srow = scores + q * ld;
   const int64_t qg = q * ng_ld;  // this query's group maxima
   uint32_t gacc = 0u;
-  const int64_t kbase = (int64_t)b * a.E_cap;
   // The wave's 16 tiles go in batches: every key load of a batch is issued before its
   // first MFMA, so a wave waits for four (MXFP4: two) memory round trips instead of one per tile (the
   // compiler, left alone, serialises load -> MFMA per tile).  Four FP8 (eight MXFP4) tiles
@@ -610,7 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
     for (int t = 0; t < kB; ++t) {
       int64_t s = e0 + 16 * (b0 + t) + jj;
       if (s >= E) s = E - 1;
-      const int64_t row = kbase + s;
+      const int64_t row = cache_row(a.seq, a.E_cap, b, s);
       if (DT == kFP8) {
         const uint4* p = reinterpret_cast<const uint4*>(kb + row * kCI + 32 * g);
         kx[t][0] = p[0];

@@ -25,6 +25,28 @@ struct RopeTab {
 };
 void rope_table(RopeTab& tab, int rope_dims, float rope_base);
 
+// Serving state shared by the decode kernels (all optional):
+//   tpos   : per-sequence positions of the new token (device [batch]); NULL = the
+//            uniform position of the call.
+//   pages  : block table (device [batch][max_pages]) of paged caches: entry s of
+//            sequence b lives in pool row pages[b][s >> page_shift] << page_shift |
+//            (s & (2^page_shift - 1)); NULL = contiguous [batch][E_cap] caches.
+struct SeqState {
+  const int64_t* tpos;
+  const int32_t* pages;
+  int64_t max_pages;
+  int page_shift;
+};
+
+// Row of entry s of sequence b in a cache of E_cap rows per sequence (or in the pool).
+__host__ __device__ inline int64_t cache_row(const SeqState& st, int64_t E_cap, int b, int64_t s) {
+  if (st.pages) {
+    const int64_t pg = st.pages[(int64_t)b * st.max_pages + (s >> st.page_shift)];
+    return (pg << st.page_shift) | (s & (((int64_t)1 << st.page_shift) - 1));
+  }
+  return (int64_t)b * E_cap + s;
+}
+
 struct CompressArgs {
   const void* C;
   const void* Z;
@@ -37,6 +59,10 @@ struct CompressArgs {
   int in_dt, out_dt;
   float eps, rope_base;
   RopeTab rope;
+  // Per-sequence decode (seq.tpos set): sequence b emits entry tpos[b] / m when
+  // (tpos[b] + 1) % m == 0, from a tail buffer whose row 0 is position
+  // m * (tpos[b] / m) - (overlap ? m : 0) (the preceding block, then the current one).
+  SeqState seq;
 };
 
 // Window-row preparation (attention prep kernel, fused decode front).
@@ -51,6 +77,7 @@ struct LocalPrepArgs {
   int w, rope_dims, decode;
   float eps, rope_base;
   RopeTab rope;
+  const int64_t* tpos;   // decode: per-sequence position of the new token (or NULL: t)
 };
 
 struct IndexerArgs {
@@ -64,6 +91,8 @@ struct IndexerArgs {
   float* topk_score;
   int64_t t0, E_cap;
   int batch, T, n_hI, cI, m, k, dt;
+  SeqState seq;      // decode: per-sequence positions and paged key rows
+  int32_t* phys;     // paged decode: the selected entries' pool rows, aligned with topk_idx
 };
 
 // Workspace plan of the indexer: scores [batch][T][ld] f32 and stage-A candidates.
@@ -98,21 +127,32 @@ struct AttnArgs {
   int prep_done;  // window rows already prepared (fused decode front kernel)
   float eps, rope_base, scale;
   RopeTab rope;
+  SeqState seq;   // decode: per-sequence positions and paged rows (idx then holds pool rows)
 };
 
-enum AttnMode : int { kModeCSA = 0, kModeDecode = 1, kModeHCA = 2 };
+// kModeHCADecode: one new token per sequence, every completed entry (ratio m_prime) and
+// the ring window.
+// Position of query j of sequence b (per-sequence decode positions when given).
+__device__ inline int64_t query_pos(const IndexerArgs& a, int b, int j) {
+  return a.seq.tpos ? a.seq.tpos[b] + j : a.t0 + j;
+}
+
+enum AttnMode : int { kModeCSA = 0, kModeDecode = 1, kModeHCA = 2, kModeHCADecode = 3 };
 
 // launchers (return hipSuccess or the launch error)
 hipError_t launch_visibility(int64_t t0, int T, int m, int k, int w, int32_t* E, int32_t* cnt,
                              int32_t* lo, int32_t* len, hipStream_t s);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
+// serving: per-sequence positions or paged keys (the all-in-LDS fused kernels, which
+// assume neither, are not planned)
 IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k, int dt,
-                         int policy);
+                         int policy, bool serving = false);
 hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void* ws,
                                hipStream_t s);
 
 size_t attn_workspace(const AttnArgs& a, int policy);
+bool attn_mfma_supported(const AttnArgs& a);  // the matrix-core kernels take this shape
 hipError_t launch_attention(const AttnArgs& a, void* ws, int policy, hipStream_t s);
 
 // Fused decode front (one launch: main and index tail compression, window-row prep and

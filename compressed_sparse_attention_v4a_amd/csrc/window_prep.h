@@ -19,12 +19,15 @@ __device__ __forceinline__ void window_prep_block(const LocalPrepArgs& a, int64_
   const int lane = tid & 63;
   const int64_t r = blk * 4 + (tid >> 6);
   if (r >= a.n_lrows) return;
-  const int64_t pos = a.lrow_base + r;
+  // decode: workspace row r holds position lo + r of the sequence's window, lo =
+  // max(0, t - w + 1) with the sequence's own t
+  const int64_t t = (a.decode && a.tpos) ? a.tpos[b] : a.t;
+  const int64_t pos = (a.decode && a.tpos) ? (t - a.w + 1 > 0 ? t - a.w + 1 : 0) + r : a.lrow_base + r;
   const uint16_t* src;
   if (a.decode) {
-    if (pos > a.t) return;
-    src = (pos == a.t && a.kv_new) ? a.kv_new + (int64_t)b * kWinC
-                                   : a.src + ((int64_t)b * a.w + pos % a.w) * kWinC;
+    if (pos > t) return;
+    src = (pos == t && a.kv_new) ? a.kv_new + (int64_t)b * kWinC
+                                 : a.src + ((int64_t)b * a.w + pos % a.w) * kWinC;
   } else {
     src = a.src + ((int64_t)b * a.n_loc + (pos - a.loc_base)) * kWinC;
   }
@@ -35,8 +38,8 @@ __device__ __forceinline__ void window_prep_block(const LocalPrepArgs& a, int64_
     g0 = *reinterpret_cast<const float4*>(a.gamma + 8 * lane);
     g1 = *reinterpret_cast<const float4*>(a.gamma + 8 * lane + 4);
   }
-  if (a.decode && pos == a.t && a.kv_new)
-    *reinterpret_cast<uint4*>(a.ring + ((int64_t)b * a.w + a.t % a.w) * kWinC + 8 * lane) = v;
+  if (a.decode && pos == t && a.kv_new)
+    *reinterpret_cast<uint4*>(a.ring + ((int64_t)b * a.w + t % a.w) * kWinC + 8 * lane) = v;
   const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
   float x[8];
   float ss = 0.0f;

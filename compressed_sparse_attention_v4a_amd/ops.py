@@ -133,12 +133,16 @@ def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI,
                     qI_scale, wI, q, kv_ring, kv_new, index_dt, gamma=None, gammaI=None, sink=None,
                     q_gamma=None, kv_gamma=None, rope_dims=0, rope_dims_I=0, rope_base=10000.0,
                     eps=1e-6, scale=0.0, num_splits=0, out=None, with_scores=True, stream=None,
-                    ws=None, noalloc=False):
+                    ws=None, noalloc=False, t_seq=None, page_table=None, page_entries=0,
+                    pool_rows=0):
     """One CSA decode step (tail compression of both instances, index top-k, ring insert and
     attention) through v4a_csa_decode_step.  C, Z: [batch][n_buf][2c] bf16; CI, ZI likewise
     with cI; qI [batch][n_hI][cI or cI/2]; q [batch][n_h][c].  Caches are updated in place.
     noalloc=True calls v4a_csa_decode_step_noalloc (the library's fixed scratch, no
-    workspace).  Returns (out, idx, cnt, score)."""
+    workspace).  Serving state: t_seq (int64 [batch], per-sequence positions; t is then
+    their maximum and the tails are [batch][2m][2c]), page_table (int32
+    [batch][max_pages]) with page_entries and pool_rows (kv_comp / KI are then pools).
+    Returns (out, idx, cnt, score)."""
     batch, n_h, c = q.shape
     n_hI = qI.shape[1]
     cI = CI.shape[2] // 2
@@ -147,14 +151,18 @@ def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI,
     idx = torch.empty(batch, k, dtype=torch.int32, device=dev)
     cnt = torch.empty(batch, dtype=torch.int32, device=dev)
     sc = torch.empty(batch, k, dtype=torch.float32, device=dev) if with_scores else None
+    paged = page_table is not None
+    E_cap = page_table.shape[1] * page_entries if paged else kv_comp.shape[1]
     step = B.decode_step(
-        t=t, E_cap=kv_comp.shape[1], n_buf=C.shape[1], tok_base=tail_base, batch=batch, n_h=n_h,
+        t=t, E_cap=E_cap, n_buf=C.shape[1], tok_base=tail_base, batch=batch, n_h=n_h,
         c=c, n_hI=n_hI, cI=cI, m=m, k=k, w=w, num_splits=num_splits, rope_dims=rope_dims,
         rope_dims_I=rope_dims_I, rope_base=rope_base, eps=eps, scale=scale, tail_dt=B.BF16,
         index_dt=_NP_DT[index_dt], attn_dt=B.BF16, C=C, Z=Z, B=B_, gamma=gamma, CI=CI, ZI=ZI,
         BI=BI, gammaI=gammaI, kv_comp=kv_comp, KI=KI, KI_scale=KI_scale, qI=qI,
         qI_scale=qI_scale, wI=wI, q=q, sink=sink, q_gamma=q_gamma, kv_gamma=kv_gamma,
-        kv_ring=kv_ring, kv_new=kv_new, topk_idx=idx, topk_cnt=cnt, topk_score=sc, out=out)
+        kv_ring=kv_ring, kv_new=kv_new, topk_idx=idx, topk_cnt=cnt, topk_score=sc, out=out,
+        t_seq=t_seq, page_table=page_table, max_pages=page_table.shape[1] if paged else 0,
+        pool_rows=pool_rows, page_entries=page_entries)
     if noalloc:
         B.v4a_csa_decode_step_noalloc(step, stream)
         return out, idx, cnt, sc
@@ -309,4 +317,29 @@ def csa_layer_prefill(H, Wt, *, m, k, w, chunk=None, rope_dims=64, gamma=None, g
     out = grouped_out_proj(r["out"][0], Wt["W_oa"], Wt["W_ob"], stream=stream)
     if keep:
         return out, dict(cq=cq, q=q, qI=qI, wI=wI, local=local, C=C, Z=Z, CI=CI, ZI=ZI, **r)
+    return out
+
+
+def hca_decode_step(*, t, m_prime, w, tail_base, C, Z, B_, kv_comp, q, kv_ring, kv_new=None,
+                    gamma=None, sink=None, q_gamma=None, kv_gamma=None, rope_dims=0,
+                    rope_base=10000.0, eps=1e-6, scale=0.0, num_splits=0, out=None, stream=None,
+                    t_seq=None, page_table=None, page_entries=0, pool_rows=0):
+    """One HCA decode step (ring insert, tail emission every m' tokens, dense attention over
+    every completed entry and the window) through v4a_hca_decode_step.  C, Z: [batch][n_buf][c]
+    bf16 tails; kv_comp [batch][E_cap][c] (or the pool); q [batch][n_h][c].  Returns out."""
+    batch, n_h, c = q.shape
+    out = torch.empty_like(q) if out is None else out
+    paged = page_table is not None
+    E_cap = page_table.shape[1] * page_entries if paged else kv_comp.shape[1]
+    step = B.hca_step(
+        t=t, E_cap=E_cap, n_buf=C.shape[1], tok_base=tail_base, batch=batch, n_h=n_h, c=c,
+        m_prime=m_prime, w=w, num_splits=num_splits, rope_dims=rope_dims, rope_base=rope_base,
+        eps=eps, scale=scale, tail_dt=B.BF16, attn_dt=B.BF16, C=C, Z=Z, B=B_, gamma=gamma,
+        kv_comp=kv_comp, q=q, sink=sink, q_gamma=q_gamma, kv_gamma=kv_gamma, kv_ring=kv_ring,
+        kv_new=kv_new, out=out, t_seq=t_seq, page_table=page_table,
+        max_pages=page_table.shape[1] if paged else 0, pool_rows=pool_rows,
+        page_entries=page_entries)
+    nbytes = B.v4a_hca_decode_step_workspace(step)
+    ws = workspace(nbytes, q.device)
+    B.v4a_hca_decode_step(step, ws, nbytes, stream)
     return out

@@ -26,7 +26,9 @@
  *     tokens [r*i, r*(i+1)) for ratio r.  Query t sees entries
  *     s < floor((t+1)/r) ([Def] section 1) and the window
  *     j in [max(0, t-w+1), t] ([Def] section 5.1).
- *   - Uniform batches: all sequences of one call share positions (t0, T, t).
+ *   - Batches: the prefill and separate decode calls take one position (t0, T, t) for
+ *     every sequence of the call; the decode steps (v4a_csa_decode_step,
+ *     v4a_hca_decode_step) also take per-sequence positions and paged caches.
  */
 #ifndef V4A_H
 #define V4A_H
@@ -300,6 +302,26 @@ typedef struct v4a_decode_step {
   int32_t* topk_cnt;         /* [batch] */
   float* topk_score;         /* [batch][k] or NULL */
   void* out;                 /* [batch][n_h][c] */
+  /* Serving state ([Def] section 7: every request owns its state), all optional.
+   * t_seq      : device int64 [batch], the position of each sequence's new token
+   *              (ragged batches); t is then an upper bound (t >= every t_seq[b]).  The
+   *              tail buffers C, Z, CI, ZI become [batch][2m][2c] (resp. 2cI): row 0 is
+   *              position m*(t_seq[b]/m) - m (the preceding block, then the current one;
+   *              n_buf must be 2m, tok_base is ignored); sequence b emits an entry exactly
+   *              when (t_seq[b]+1) % m == 0.
+   * page_table : device int32 [batch][max_pages]: paged caches.  Entry s of sequence b is
+   *              row page_table[b][s / page_entries] * page_entries + s % page_entries of
+   *              the pools kv_comp [pool_rows][c], KI [pool_rows][...] and KI_scale
+   *              [pool_rows][...]; E_cap must equal max_pages * page_entries.  With 128-token
+   *              pages (page_entries = 128/m) the CSA and HCA caches of a layer share one
+   *              page granularity (lcm(m, m') = 128 tokens).
+   * Both need the matrix-core attention shapes (bf16 rows of 512 channels, heads in
+   * groups of 64, RoPE 0 or 64); otherwise V4A_ENOTSUP. */
+  const int64_t* t_seq;
+  const int32_t* page_table;
+  int64_t max_pages;
+  int64_t pool_rows;
+  int page_entries;          /* a power of two */
 } v4a_decode_step;
 
 /* Byte offsets of the fields of v4a_decode_step in declaration order, for bindings
@@ -308,6 +330,56 @@ typedef struct v4a_decode_step {
 V4A_API int v4a_decode_step_layout(size_t* off, int n, size_t* size);
 V4A_API size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d);
 V4A_API int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * v4a_hca_decode_step -- one HCA decode step for every sequence of the batch ([Def]
+ * section 7 with the HCA state: ring, main cache appended every m' tokens, no
+ * indexer; section 4 for the attention): the new token at position t goes into ring
+ * slot t % w (from kv_new, when given); if (t+1) % m' == 0 the completed block's
+ * entry (t+1)/m' - 1 is emitted (one-stream compressor of section 2.2, RMSNorm with
+ * gamma, RoPE at m' i) into kv_comp; then one softmax per head over every completed
+ * entry s < (t+1)/m' joined with the window, with sink, RMSNorm and RoPE as for the
+ * CSA calls.  Equivalent to
+ *   v4a_compress(C, Z, tail_dt, B, batch, n_buf, tok_base, t, 1, c, m_prime, 0, gamma,
+ *                eps, rope_dims, rope_base, kv_comp, NULL, attn_dt, E_cap)
+ * followed by the dense attention of v4a_hca_attn for the single query t, with the
+ * window read from the ring.  Needs the matrix-core shapes (bf16 rows of 512
+ * channels, heads in groups of 64, RoPE 0 or 64); V4A_ENOTSUP otherwise.  Serving
+ * state (t_seq, page_table, ...) as in v4a_decode_step; with t_seq the tail buffers
+ * are [batch][m'][c] whose row 0 is position m' * (t_seq[b] / m').
+ */
+typedef struct v4a_hca_step {
+  int64_t t;                 /* position of the new token (upper bound with t_seq) */
+  int64_t E_cap;             /* rows of kv_comp per sequence (logical capacity when paged) */
+  int64_t n_buf, tok_base;   /* tail buffers: n_buf rows, row r = position tok_base + r */
+  int batch, n_h, c, m_prime, w;
+  int num_splits;            /* 0 = automatic */
+  int rope_dims;
+  float rope_base, eps, scale;
+  v4a_dtype tail_dt;         /* C, Z: F32 or BF16 */
+  v4a_dtype attn_dt;         /* q, kv_comp, kv_ring, kv_new, out: BF16 */
+  const void* C;             /* [batch][n_buf][c] */
+  const void* Z;
+  const float* B;            /* [m_prime][c] */
+  const float* gamma;        /* [c] or NULL */
+  void* kv_comp;             /* [batch][E_cap][c] (or the pool when paged) */
+  const void* q;             /* [batch][n_h][c] */
+  const float* sink;         /* [n_h] or NULL */
+  const float* q_gamma;      /* [c] or NULL */
+  const float* kv_gamma;     /* [c] or NULL */
+  void* kv_ring;             /* [batch][w][c], token j in slot j % w */
+  const void* kv_new;        /* [batch][c] or NULL */
+  void* out;                 /* [batch][n_h][c] */
+  const int64_t* t_seq;      /* serving state, as in v4a_decode_step */
+  const int32_t* page_table;
+  int64_t max_pages;
+  int64_t pool_rows;
+  int page_entries;
+} v4a_hca_step;
+
+V4A_API int v4a_hca_decode_step_layout(size_t* off, int n, size_t* size);
+V4A_API size_t v4a_hca_decode_step_workspace(const v4a_hca_step* d);
+V4A_API int v4a_hca_decode_step(const v4a_hca_step* d, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * v4a_linear -- a plain projection Y = X W^T of the layer around the attention path

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 21, names
+    assert len(names) == 24, names
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (v4a_\w+)", out))
@@ -247,3 +247,54 @@ def test_projection_validation(lib):
     assert gp(g=7) == EINVAL
     assert gp(d=60) == ENOTSUP
     assert gp(wsb=need - 1) == ENOSPC
+
+
+def test_serving_state_validation(lib):
+    """Per-sequence positions and paged caches are checked on the host: the tail layout of
+    a ragged step, the page geometry, and the shapes the matrix-core kernels take."""
+    class Fake:
+        def __init__(self, addr=4096):
+            self.addr = addr
+
+        def data_ptr(self):
+            return self.addr
+
+    F = Fake()
+
+    def step(**kw):
+        a = dict(t=131071, E_cap=32768, n_buf=8, tok_base=131064, batch=2, n_h=64, c=512,
+                 n_hI=64, cI=128, m=4, k=512, w=128, rope_dims=64, rope_base=1e4, eps=1e-6,
+                 tail_dt=B.BF16, index_dt=B.FP8_E4M3, attn_dt=B.BF16, C=F, Z=F, B=F, CI=F, ZI=F,
+                 BI=F, kv_comp=F, KI=F, KI_scale=F, qI=F, qI_scale=F, wI=F, q=F, kv_ring=F,
+                 topk_idx=F, topk_cnt=F, out=F)
+        a.update(kw)
+        return B.decode_step(**a)
+
+    def run(d):
+        return lib.v4a_csa_decode_step(ct.c_void_p(ct.addressof(d)), ct.c_void_p(4096), 1 << 34, None)
+
+    assert run(step(t_seq=F, n_buf=16)) == EINVAL                     # ragged tails are 2m rows
+    pg = dict(page_table=F, max_pages=1024, page_entries=32, pool_rows=65536)
+    assert run(step(**dict(pg, page_entries=24))) == EINVAL           # not a power of two
+    assert run(step(**dict(pg, max_pages=512))) == EINVAL             # E_cap != pages * entries
+    assert run(step(**dict(pg, pool_rows=100))) == EINVAL             # not whole pages
+    assert run(step(t_seq=F, c=256, n_buf=8)) == ENOTSUP              # general-kernel shape
+    need = B.v4a_csa_decode_step_workspace(step(**pg))
+    assert need >= B.v4a_csa_decode_step_workspace(step()) + 2 * 512 * 4  # pool rows of the selection
+
+    def hstep(**kw):
+        a = dict(t=65535, E_cap=512, n_buf=128, tok_base=65408, batch=2, n_h=64, c=512,
+                 m_prime=128, w=128, rope_dims=64, rope_base=1e4, eps=1e-6, tail_dt=B.BF16,
+                 attn_dt=B.BF16, C=F, Z=F, B=F, kv_comp=F, q=F, kv_ring=F, out=F)
+        a.update(kw)
+        return B.hca_step(**a)
+
+    def hrun(d):
+        return lib.v4a_hca_decode_step(ct.c_void_p(ct.addressof(d)), ct.c_void_p(4096), 1 << 34, None)
+
+    assert B.v4a_hca_decode_step_workspace(hstep()) > 0
+    assert hrun(hstep(m_prime=0)) == EINVAL
+    assert hrun(hstep(E_cap=511)) == EINVAL
+    assert hrun(hstep(c=256)) == ENOTSUP
+    assert hrun(hstep(t_seq=F, n_buf=64)) == EINVAL
+    assert hrun(hstep(tok_base=65409)) == EINVAL                      # tail misses 65408

@@ -1042,3 +1042,244 @@ def test_csa_layer_prefill_small():
     got = dl(out)
     rel = np.sqrt(np.mean((got - ref) ** 2, axis=1)) / np.sqrt(np.mean(ref ** 2, axis=1))
     assert np.all(rel < 0.01), f"layer output: worst row relative RMS error {rel.max():.3g}"
+
+
+# ------------------------------------ serving state: ragged positions, paged caches --- #
+
+_NAN16 = 0x7FC0
+
+
+def _ragged_csa_state(ts, n_h=64, c=512, n_hI=64, cI=128, m=4, w=128, seed=0, page=32):
+    """Decode state of len(ts) sequences, sequence b at position ts[b]: its own entries,
+    ring and two-block tail (row 0 = position m * (t/m) - m).  Rows and slots that hold no
+    existing entry or token are NaN, so a read of one poisons the output."""
+    rng = np.random.default_rng(seed)
+    bt = len(ts)
+    sc = 1 / math.sqrt(c)
+    E_cap = max((t + 1) // m for t in ts) + 2
+    E_cap = (E_cap + page - 1) // page * page
+    kv = np.full((bt, E_cap, c), np.nan)
+    KI = rng.standard_normal((bt, E_cap, cI))
+    ring = np.full((bt, w, c), np.nan)
+    C = np.zeros((bt, 2 * m, 2 * c))
+    Z = np.zeros((bt, 2 * m, 2 * c))
+    CI = np.zeros((bt, 2 * m, 2 * cI))
+    ZI = np.zeros((bt, 2 * m, 2 * cI))
+    for b, t in enumerate(ts):
+        kv[b, :t // m] = rng.standard_normal((t // m, c))
+        for j in range(max(0, t - w), t):
+            ring[b, j % w] = sc * rng.standard_normal(c)
+        C[b] = sc * rng.standard_normal((2 * m, 2 * c))
+        Z[b] = rng.standard_normal((2 * m, 2 * c))
+        CI[b] = rng.standard_normal((2 * m, 2 * cI))
+        ZI[b] = rng.standard_normal((2 * m, 2 * cI))
+    d = dict(ts=list(ts), E_cap=E_cap)
+    d["kv_comp"] = synth.formats.bf16_bits(kv)
+    d["KI"], d["KI_scale"] = synth.formats.fp8_e4m3_rows(KI)
+    d["qI"], d["qI_scale"] = synth.formats.fp8_e4m3_rows(rng.standard_normal((bt, n_hI, cI)))
+    d["ring"] = synth.formats.bf16_bits(ring)
+    d["kv_new"] = synth.formats.bf16_bits(sc * rng.standard_normal((bt, c)))
+    for nm, x in (("C", C), ("Z", Z), ("CI", CI), ("ZI", ZI)):
+        d[nm] = synth.formats.bf16_bits(x)
+    d["B"] = (math.sqrt(0.1) * rng.standard_normal((2 * m, c))).astype(np.float32)
+    d["BI"] = (math.sqrt(0.1) * rng.standard_normal((2 * m, cI))).astype(np.float32)
+    d["q"] = synth.formats.bf16_bits(sc * rng.standard_normal((bt, n_h, c)))
+    d["wI"] = rng.random((bt, n_hI)).astype(np.float32)
+    d["gamma"], d["gammaI"] = np.ones(c, np.float32), np.ones(cI, np.float32)
+    return d
+
+
+def _paging(bt, E_cap, page, seed):
+    """A block table that scatters every sequence's pages over a pool with spare pages."""
+    max_pages = E_cap // page
+    n_pool = bt * max_pages + 3
+    perm = np.random.default_rng(seed).permutation(n_pool)[:bt * max_pages]
+    return perm.reshape(bt, max_pages).astype(np.int32), n_pool * page
+
+
+def _to_pool(x, table, page, pool_rows):
+    """[batch][E_cap][...] -> [pool_rows][...] through the block table (spare rows zero)."""
+    bt, E_cap = x.shape[:2]
+    pool = np.zeros((pool_rows,) + x.shape[2:], x.dtype)
+    for b in range(bt):
+        for p in range(E_cap // page):
+            pool[table[b, p] * page:(table[b, p] + 1) * page] = x[b, p * page:(p + 1) * page]
+    return pool
+
+
+def _from_pool(pool, table, page):
+    bt, mp = table.shape
+    return torch.stack([torch.cat([pool[int(table[b, p]) * page:(int(table[b, p]) + 1) * page]
+                                   for p in range(mp)]) for b in range(bt)])
+
+
+def _run_ragged_csa(d, m=4, k=512, w=128, paged=None):
+    ts = d["ts"]
+    g, gI = up(d["gamma"]), up(d["gammaI"])
+    kw = {}
+    if paged is None:
+        kv, KI, KIs = up(d["kv_comp"]), up(d["KI"]), up(d["KI_scale"])
+    else:
+        table, page, pool_rows = paged
+        kv = up(_to_pool(d["kv_comp"], table, page, pool_rows))
+        KI = up(_to_pool(d["KI"], table, page, pool_rows))
+        KIs = up(_to_pool(d["KI_scale"], table, page, pool_rows))
+        kw = dict(page_table=up(table), page_entries=page, pool_rows=pool_rows)
+    ring = up(d["ring"])
+    out, idx, cnt, sc = ops.csa_decode_step(
+        t=max(ts), m=m, k=k, w=w, tail_base=0, C=up(d["C"]), Z=up(d["Z"]), B_=up(d["B"]),
+        CI=up(d["CI"]), ZI=up(d["ZI"]), BI=up(d["BI"]), kv_comp=kv, KI=KI, KI_scale=KIs,
+        qI=up(d["qI"]), qI_scale=up(d["qI_scale"]), wI=up(d["wI"]), q=up(d["q"]), kv_ring=ring,
+        kv_new=up(d["kv_new"]), index_dt="fp8", gamma=g, gammaI=gI, q_gamma=g, kv_gamma=g,
+        rope_dims=64, t_seq=up(np.array(ts, np.int64)), **kw)
+    torch.cuda.synchronize()
+    if paged is not None:
+        table, page, _ = paged
+        kv, KI, KIs = _from_pool(kv, table, page), _from_pool(KI, table, page), _from_pool(KIs, table, page)
+    return dict(kv=kv, KI=KI, KIs=KIs, ring=ring, idx=idx, cnt=cnt, sc=sc, out=out)
+
+
+def test_decode_step_ragged_positions():
+    """One CSA decode call over sequences at different positions (128K, mid-block, the
+    first full top-k, the first tokens): each emits, selects and attends by its own
+    position, checked per sequence against the oracle."""
+    ts = [131071, 40002, 2047, 5, 70, 8191]
+    m, k, w, c, cI = 4, 512, 128, 512, 128
+    d = _ragged_csa_state(ts, seed=21)
+    log(f"ragged decode step positions {ts}")
+    r = _run_ragged_csa(d)
+    for b, t in enumerate(ts):
+        E = (t + 1) // m
+        if (t + 1) % m == 0:
+            lo = m * (t // m) - m
+            rows = slice(max(0, -lo), 2 * m)
+            tail = dict(tok_base=max(lo, 0), i_begin=E - 1, i_end=E, m=m, overlap=True)
+            ref_kv = oracle.compress(f64(d["C"][b][rows], "bf16"), f64(d["Z"][b][rows], "bf16"), d["B"],
+                                     c=c, gamma=d["gamma"], rope_dims=64, **tail)[0]
+            assert_bf16_close(decode_stored(r["kv"][b, E - 1], "bf16"), ref_kv, what=f"t={t} entry")
+            ref_ki = oracle.compress(f64(d["CI"][b][rows], "bf16"), f64(d["ZI"][b][rows], "bf16"),
+                                     d["BI"], c=cI, gamma=d["gammaI"], **tail)[0]
+            check_quantised(r["KI"][b, E - 1:E], r["KIs"][b, E - 1:E], ref_ki[None], "fp8")
+        cnt = int(r["cnt"][b])
+        assert cnt == min(k, E), f"t={t}: count {cnt}"
+        if E > 0:
+            KId = decode_stored(r["KI"][b, :E], "fp8", r["KIs"][b, :E])
+            qId = oracle.decode(d["qI"][b], "fp8", d["qI_scale"][b])
+            ref_s = oracle.index_scores(qId[None], KId, d["wI"][b][None].astype(np.float64), t0=t,
+                                        m=m, ld=E)
+            check_topk(r["idx"][b:b + 1].cpu().numpy(), r["cnt"][b:b + 1].cpu().numpy(), ref_s, t0=t,
+                       m=m, k=k, gpu_scores=r["sc"][b:b + 1].cpu().numpy(), what=f"t={t}")
+        ringd = decode_stored(r["ring"][b], "bf16")
+        assert np.array_equal(ringd[t % w], f64(d["kv_new"][b], "bf16")), f"t={t}: ring insert"
+        kvd = decode_stored(r["kv"][b][r["idx"][b, :cnt].long()], "bf16")
+        ref_o = oracle.attend_decode(f64(d["q"][b], "bf16"), kvd, ringd,
+                                     np.arange(cnt, dtype=np.int32), cnt, t=t, w=w,
+                                     q_gamma=d["gamma"], kv_gamma=d["gamma"], q_norm=True,
+                                     kv_norm=True, rope_dims=64)
+        o = decode_stored(r["out"][b], "bf16")
+        assert np.all(np.isfinite(o)), f"t={t}: a nonexistent token or entry was read"
+        assert_attn_close(o, ref_o, atol=ATOL_BF16, rel_rms=REL_RMS_BF16, what=f"ragged t={t}")
+
+
+def test_decode_step_paged_equals_contiguous():
+    """The same ragged step with both caches in a page pool (32 entries = 128 tokens per
+    page, pages scattered through a block table) gives the contiguous result bit for bit,
+    and the emitted entries land in the right pool rows."""
+    ts = [131071, 40002, 2047, 5]
+    d = _ragged_csa_state(ts, seed=22)
+    table, pool_rows = _paging(len(ts), d["E_cap"], 32, 5)
+    log("paged vs contiguous decode step")
+    a = _run_ragged_csa(d)
+    b_ = _run_ragged_csa(d, paged=(table, 32, pool_rows))
+    for key in ("kv", "KI", "KIs", "ring", "idx", "cnt", "sc", "out"):
+        x, y = a[key], b_[key]
+        if key == "kv":  # NaN rows compare by bits
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), key
+
+
+def _hca_state(ts, n_h=64, c=512, mp=128, w=128, seed=0, page=1):
+    rng = np.random.default_rng(seed)
+    bt = len(ts)
+    sc = 1 / math.sqrt(c)
+    E_cap = max((t + 1) // mp for t in ts) + 2
+    E_cap = (E_cap + page - 1) // page * page
+    kv = np.full((bt, E_cap, c), np.nan)
+    ring = np.full((bt, w, c), np.nan)
+    for b, t in enumerate(ts):
+        kv[b, :t // mp] = rng.standard_normal((t // mp, c))
+        for j in range(max(0, t - w), t):
+            ring[b, j % w] = sc * rng.standard_normal(c)
+    d = dict(ts=list(ts), E_cap=E_cap)
+    d["kv_comp"] = synth.formats.bf16_bits(kv)
+    d["ring"] = synth.formats.bf16_bits(ring)
+    d["kv_new"] = synth.formats.bf16_bits(sc * rng.standard_normal((bt, c)))
+    d["C"] = synth.formats.bf16_bits(sc * rng.standard_normal((bt, mp, c)))
+    d["Z"] = synth.formats.bf16_bits(rng.standard_normal((bt, mp, c)))
+    d["B"] = (math.sqrt(0.1) * rng.standard_normal((mp, c))).astype(np.float32)
+    d["q"] = synth.formats.bf16_bits(sc * rng.standard_normal((bt, n_h, c)))
+    d["gamma"] = np.ones(c, np.float32)
+    d["sink"] = rng.standard_normal(n_h).astype(np.float32)
+    return d
+
+
+def _run_hca(d, mp=128, w=128, ragged=True, paged=None):
+    ts = d["ts"]
+    g = up(d["gamma"])
+    kw = {}
+    kv = up(d["kv_comp"])
+    if paged is not None:
+        table, page, pool_rows = paged
+        kv = up(_to_pool(d["kv_comp"], table, page, pool_rows))
+        kw = dict(page_table=up(table), page_entries=page, pool_rows=pool_rows)
+    ring = up(d["ring"])
+    t = max(ts)
+    if ragged:
+        kw["t_seq"] = up(np.array(ts, np.int64))
+    out = ops.hca_decode_step(t=t, m_prime=mp, w=w, tail_base=mp * (t // mp), C=up(d["C"]),
+                              Z=up(d["Z"]), B_=up(d["B"]), kv_comp=kv, q=up(d["q"]), kv_ring=ring,
+                              kv_new=up(d["kv_new"]), gamma=g, sink=up(d["sink"]), q_gamma=g,
+                              kv_gamma=g, rope_dims=64, **kw)
+    torch.cuda.synchronize()
+    if paged is not None:
+        kv = _from_pool(kv, paged[0], paged[1])
+    return dict(kv=kv, ring=ring, out=out)
+
+
+@pytest.mark.parametrize("ragged", [True, False])
+def test_hca_decode_step(ragged):
+    """HCA decode: ring insert, the block entry every m' = 128 tokens, dense attention over
+    every completed entry and the window (with a sink); ragged positions or one shared
+    position, against the oracle per sequence."""
+    ts = [65535, 1000, 127, 300, 8191] if ragged else [4095, 4095, 4095]
+    mp, w, c = 128, 128, 512
+    d = _hca_state(ts, seed=31)
+    log(f"hca decode step positions {ts}")
+    r = _run_hca(d, ragged=ragged)
+    for b, t in enumerate(ts):
+        E = (t + 1) // mp
+        if (t + 1) % mp == 0:
+            ref_kv = oracle.compress(f64(d["C"][b], "bf16"), f64(d["Z"][b], "bf16"), d["B"],
+                                     tok_base=mp * (t // mp), i_begin=E - 1, i_end=E, c=c, m=mp,
+                                     overlap=False, gamma=d["gamma"], rope_dims=64)[0]
+            assert_bf16_close(decode_stored(r["kv"][b, E - 1], "bf16"), ref_kv, what=f"t={t} entry")
+        ringd = decode_stored(r["ring"][b], "bf16")
+        kvd = decode_stored(r["kv"][b, :max(E, 1)], "bf16")
+        ref_o = oracle.attend_decode(f64(d["q"][b], "bf16"), kvd, ringd, np.arange(E, dtype=np.int32),
+                                     E, t=t, w=w, sink=d["sink"], q_gamma=d["gamma"],
+                                     kv_gamma=d["gamma"], q_norm=True, kv_norm=True, rope_dims=64)
+        o = decode_stored(r["out"][b], "bf16")
+        assert np.all(np.isfinite(o)), f"t={t}: a nonexistent token or entry was read"
+        assert_attn_close(o, ref_o, atol=ATOL_BF16, rel_rms=REL_RMS_BF16, what=f"hca t={t}")
+
+
+def test_hca_decode_paged_equals_contiguous():
+    ts = [65535, 1000, 127, 300]
+    d = _hca_state(ts, seed=32)
+    table, pool_rows = _paging(len(ts), d["E_cap"], 1, 6)
+    log("paged vs contiguous HCA decode step")
+    a = _run_hca(d)
+    b_ = _run_hca(d, paged=(table, 1, pool_rows))
+    for key in ("kv", "ring", "out"):
+        assert torch.equal(a[key].view(torch.int16), b_[key].view(torch.int16)), key
