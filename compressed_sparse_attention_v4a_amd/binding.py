@@ -13,8 +13,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libv4a.so")
 
-F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
-DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4}
+F32, BF16, FP8_E4M3, MXFP4, KV576 = 0, 1, 2, 3, 4
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4, "kv576": KV576}
 
 _lib = None
 
@@ -94,7 +94,8 @@ class DecodeStep(ct.Structure):
                                       "q_gamma", "kv_gamma", "kv_ring", "kv_new", "topk_idx",
                                       "topk_cnt", "topk_score", "out")]
         + [("t_seq", ct.c_void_p), ("page_table", ct.c_void_p), ("max_pages", ct.c_int64),
-           ("pool_rows", ct.c_int64), ("page_entries", ct.c_int)])
+           ("pool_rows", ct.c_int64), ("page_entries", ct.c_int), ("kv576", ct.c_int),
+           ("kv_scale", ct.c_void_p)])
 
 
 class HcaStep(ct.Structure):

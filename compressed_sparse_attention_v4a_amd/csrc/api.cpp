@@ -120,11 +120,13 @@ static int compress_prepare(const void* C, const void* Z, v4a_dtype in_dt, const
   REQUIRE(c % vec == 0, V4A_ENOTSUP, "c must be a multiple of %d for this input dtype", vec);
   REQUIRE(c / vec <= 256, V4A_ENOTSUP, "c too large (max %d for this input dtype)", 256 * vec);
   REQUIRE(out_dt == V4A_F32 || out_dt == V4A_BF16 || out_dt == V4A_FP8_E4M3 ||
-              out_dt == V4A_MXFP4,
+              out_dt == V4A_MXFP4 || out_dt == V4A_KV576,
           V4A_ENOTSUP, "unknown out_dt");
   REQUIRE(out_dt != V4A_MXFP4 || c % 32 == 0, V4A_EINVAL, "MXFP4 output needs c %% 32 == 0");
-  REQUIRE((out_dt != V4A_FP8_E4M3 && out_dt != V4A_MXFP4) || out_scale, V4A_EINVAL,
-          "out_scale is required for FP8/MXFP4 output");
+  REQUIRE(out_dt != V4A_KV576 || (rope_dims % vec == 0 && rope_dims < c), V4A_EINVAL,
+          "KV576 output needs rope_dims a multiple of %d and below c", vec);
+  REQUIRE((out_dt != V4A_FP8_E4M3 && out_dt != V4A_MXFP4 && out_dt != V4A_KV576) || out_scale,
+          V4A_EINVAL, "out_scale is required for FP8/MXFP4/KV576 output");
   REQUIRE(aligned(C, 16) && aligned(Z, 16), V4A_EINVAL, "C and Z must be 16-byte aligned");
   const int64_t i_begin = t0 / m, i_end = (t0 + T) / m;
   REQUIRE(E_cap >= i_end, V4A_EINVAL, "E_cap (%lld) < last entry + 1 (%lld)", (long long)E_cap,
@@ -347,9 +349,22 @@ static v4a::AttnArgs step_attn(const v4a_decode_step* d) {
                    decode_splits(d->batch, d->n_h, d->num_splits, d->k, d->w));
 }
 
-// pool rows of the selected entries (paged steps), after the indexer workspace
+// pool rows of the selected entries (paged bf16 steps), or the bf16 staging of the
+// selected production-format rows (kv576 steps), after the indexer workspace
 static size_t step_phys_bytes(const v4a_decode_step* d) {
+  if (d->kv576) return align256((size_t)d->batch * d->k * (size_t)d->c * 2);
   return d->page_table ? align256((size_t)d->batch * d->k * sizeof(int32_t)) : 0;
+}
+
+// attention of a kv576 step: dense over the staged rows (cnt[b] of them), then the window
+static v4a::AttnArgs step_attn_staged(const v4a_decode_step* d, void* staged) {
+  v4a::AttnArgs a = attn_args(d->q, staged, d->kv_ring, d->kv_ring, d->kv_new, nullptr, d->topk_cnt,
+                              d->sink, d->q_gamma, d->kv_gamma, d->eps, d->rope_dims, d->rope_base,
+                              d->scale, d->batch, d->t, 1, d->n_h, d->c, d->k, d->w, 1, d->k, 0, 0,
+                              d->out, d->attn_dt, v4a::kModeHCADecode,
+                              decode_splits(d->batch, d->n_h, d->num_splits, d->k, d->w));
+  a.dense_cnt = d->topk_cnt;
+  return a;
 }
 
 static int log2_exact(int64_t x) {
@@ -394,7 +409,7 @@ int v4a_decode_step_layout(size_t* off, int n, size_t* size) {
       V4A_OFF(qI_scale), V4A_OFF(wI), V4A_OFF(q), V4A_OFF(sink), V4A_OFF(q_gamma),
       V4A_OFF(kv_gamma), V4A_OFF(kv_ring), V4A_OFF(kv_new), V4A_OFF(topk_idx), V4A_OFF(topk_cnt),
       V4A_OFF(topk_score), V4A_OFF(out), V4A_OFF(t_seq), V4A_OFF(page_table), V4A_OFF(max_pages),
-      V4A_OFF(pool_rows), V4A_OFF(page_entries)};
+      V4A_OFF(pool_rows), V4A_OFF(page_entries), V4A_OFF(kv576), V4A_OFF(kv_scale)};
 #undef V4A_OFF
   const int nf = (int)(sizeof(o) / sizeof(o[0]));
   for (int i = 0; i < nf && i < n && off; ++i) off[i] = o[i];
@@ -407,7 +422,7 @@ size_t v4a_csa_decode_step_workspace(const v4a_decode_step* d) {
       d->num_splits < 0 || d->num_splits > 64)
     return 0;
   return align256(step_plan(d).total) + step_phys_bytes(d) +
-         v4a::attn_workspace(step_attn(d), g_policy.load());
+         v4a::attn_workspace(d->kv576 ? step_attn_staged(d, nullptr) : step_attn(d), g_policy.load());
 }
 
 int v4a_csa_decode_step(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* stream) {
@@ -430,11 +445,14 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   REQUIRE(!ragged || d->n_buf == 2 * (int64_t)d->m, V4A_EINVAL,
           "with t_seq the tail buffers hold 2m rows per sequence (n_buf = %d)", 2 * d->m);
   const int64_t tb = ragged ? (int64_t)d->m * (d->t / d->m) - d->m : d->tok_base;
+  const bool kv576 = d->kv576 != 0;
+  REQUIRE(!kv576 || d->kv_scale, V4A_EINVAL, "kv576 needs kv_scale");
   v4a::CompressArgs cm, ci;
   int rc = compress_prepare(d->C, d->Z, d->tail_dt, d->B, d->batch, d->n_buf,
                             ragged ? (tb > 0 ? tb : 0) : d->tok_base, ragged ? 0 : d->t,
                             ragged ? 0 : 1, d->c, d->m, 1, d->gamma, d->eps, d->rope_dims,
-                            d->rope_base, d->kv_comp, nullptr, d->attn_dt, d->E_cap, cm);
+                            d->rope_base, d->kv_comp, kv576 ? d->kv_scale : nullptr,
+                            kv576 ? V4A_KV576 : d->attn_dt, d->E_cap, cm);
   if (rc != V4A_OK) return rc;
   rc = compress_prepare(d->CI, d->ZI, d->tail_dt, d->BI, d->batch, d->n_buf,
                         ragged ? (tb > 0 ? tb : 0) : d->tok_base, ragged ? 0 : d->t, ragged ? 0 : 1,
@@ -455,11 +473,19 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   rc = check_serving(d->t_seq, d->page_table, d->max_pages, d->pool_rows, d->page_entries, d->E_cap,
                      policy == 0 && v4a::attn_mfma_supported(aa), st);
   if (rc != V4A_OK) return rc;
+  REQUIRE(!kv576 || (policy == 0 && v4a::attn_mfma_supported(aa) && d->c == 512), V4A_ENOTSUP,
+          "kv576 caches need bf16 rows of 512 channels, heads in groups of 64, RoPE 0 or 64");
   const size_t ws_i = align256(p.total), ws_p = step_phys_bytes(d);
+  if (kv576) {
+    aa = step_attn_staged(d, reinterpret_cast<char*>(ws) + ws_i);
+    aa.seq = v4a::SeqState{};
+    aa.seq.tpos = st.tpos;  // the staged list is contiguous; positions stay per sequence
+  }
   const size_t need = ws_i + ws_p + v4a::attn_workspace(aa, policy);
   REQUIRE(ws_bytes >= need, V4A_ENOSPC, "workspace too small: %zu < %zu", ws_bytes, need);
   REQUIRE(ws && aligned(ws, 256), V4A_EINVAL, "workspace must be 256-byte aligned");
-  int32_t* phys = d->page_table ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + ws_i) : nullptr;
+  int32_t* phys = (d->page_table && !kv576) ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + ws_i)
+                                             : nullptr;
   if (ragged) {
     // one entry slot per sequence: emitted or not by the sequence's own position
     cm.seq = st;
@@ -476,7 +502,7 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   ia.cI = d->cI; ia.m = d->m; ia.k = d->k; ia.dt = d->index_dt;
   ia.seq = st;
   ia.phys = phys;
-  aa.seq = st;
+  if (!kv576) aa.seq = st;
   if (phys) aa.idx = phys;  // the attention gathers pool rows
   hipStream_t s = (hipStream_t)stream;
   void* ws_a = reinterpret_cast<char*>(ws) + ws_i + ws_p;
@@ -490,6 +516,9 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
     if (e == hipSuccess) e = v4a::launch_compress(ci, s);
   }
   if (e == hipSuccess) e = v4a::launch_indexer_topk(ia, p, ws, s);
+  if (e == hipSuccess && kv576)
+    e = v4a::launch_kv576_gather(d->kv_comp, d->kv_scale, d->topk_idx, d->topk_cnt, st, d->E_cap,
+                                 d->batch, d->k, d->rope_dims, reinterpret_cast<char*>(ws) + ws_i, s);
   if (e == hipSuccess) e = v4a::launch_attention(aa, ws_a, policy, s);
   return hip_status(e, "v4a_csa_decode_step");
 }

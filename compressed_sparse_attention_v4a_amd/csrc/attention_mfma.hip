@@ -153,6 +153,7 @@ struct MqaArgs {
   const int32_t* pages;
   int64_t max_pages;
   int page_shift;
+  int staged;  // dense decode over a staged list: cnt[b] rows per sequence, not (t+1)/m'
 };
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* base, int off) {
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       it.t = a.t0 + it.qi;
     }
     if constexpr (dense) {
-      it.ncomp = (it.t + 1) / a.m_prime;
+      it.ncomp = a.staged ? min(max(a.cnt[(int64_t)it.b * nq + it.qi], 0), a.k) : (it.t + 1) / a.m_prime;
     } else {
       it.ncomp = min(max(a.cnt[(int64_t)it.b * nq + it.qi], 0), a.k);
     }
@@ -839,9 +840,52 @@ __global__ __launch_bounds__(256) void decode_front_kernel(CompressArgs cm, Comp
   if (wv == 1 && vb * (64 / GI) < ci.n_entries) compress_rows_body<uint16_t, GI>(ci, vb, b, lane);
 }
 
+// Selected entries of a decode step in the production row format (kKV576), dequantised
+// to bf16 into a staging list [batch][k][512] (row u = the u-th selected entry), which
+// the attention then reads as a dense prefix of cnt[b] rows.  One wave per row: lane l
+// takes channels 8 l .. 8 l + 7 (eight E4M3 codes times the row scale, or eight bf16).
+__global__ __launch_bounds__(256) void kv576_gather_kernel(const uint8_t* kv, const float* kv_scale,
+                                                           const int32_t* idx, const int32_t* cnt,
+                                                           SeqState seq, int64_t E_cap, int k,
+                                                           int rope_dims, uint16_t* staged) {
+  const int b = blockIdx.y;
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (u >= k || u >= cnt[b]) return;
+  const int64_t row = cache_row(seq, E_cap, b, idx[(int64_t)b * k + u]);
+  const int nq = kC - rope_dims;
+  const uint8_t* src = kv + row * kv576_row_bytes(kC, rope_dims);
+  const int ch0 = 8 * lane;
+  uint4 o;
+  if (ch0 < nq) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src + ch0);
+    const float sc = kv_scale[row];
+    const uint32_t w[2] = {v.x, v.y};
+    uint32_t p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (w[e >> 1] >> (16 * (e & 1))) & 255u, hi = (w[e >> 1] >> (16 * (e & 1) + 8)) & 255u;
+      p[e] = pk_bf16(e4m3_to_f32(lo) * sc, e4m3_to_f32(hi) * sc);
+    }
+    o = make_uint4(p[0], p[1], p[2], p[3]);
+  } else {
+    o = *reinterpret_cast<const uint4*>(src + nq + 2 * (ch0 - nq));
+  }
+  *reinterpret_cast<uint4*>(staged + ((int64_t)b * k + u) * kC + ch0) = o;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- host side --
+
+hipError_t launch_kv576_gather(const void* kv, const float* kv_scale, const int32_t* idx,
+                               const int32_t* cnt, const SeqState& seq, int64_t E_cap, int batch,
+                               int k, int rope_dims, void* staged, hipStream_t s) {
+  hipLaunchKernelGGL(kv576_gather_kernel, dim3((unsigned)((k + 3) / 4), (unsigned)batch), dim3(256), 0,
+                     s, reinterpret_cast<const uint8_t*>(kv), kv_scale, idx, cnt, seq, E_cap, k,
+                     rope_dims, reinterpret_cast<uint16_t*>(staged));
+  return hipGetLastError();
+}
 
 bool attn_mfma_supported(const AttnArgs& a) {
   return a.dt == kBF16 && a.c == kC && a.n_h % kHG == 0 && (a.rope_dims == 0 || a.rope_dims == 64) &&
@@ -859,7 +903,7 @@ static int64_t local_rows(const AttnArgs& a) {
 // longest candidate list of a decode call: k + w (CSA), or every completed entry of the
 // latest position plus w (HCA)
 int64_t decode_max_list(const AttnArgs& a) {
-  if (a.mode == kModeHCADecode) return (a.t0 + 1) / a.m_prime + a.w;
+  if (a.mode == kModeHCADecode && !a.dense_cnt) return (a.t0 + 1) / a.m_prime + a.w;
   return (int64_t)a.k + a.w;
 }
 
@@ -946,7 +990,7 @@ static bool tail_rows_ok(const CompressArgs& a) {
 
 bool decode_front_supported(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
                             int policy) {
-  return a.mode == kModeDecode && policy == 0 && attn_mfma_supported(a) && tail_rows_ok(cm) &&
+  return is_decode(a) && policy == 0 && attn_mfma_supported(a) && tail_rows_ok(cm) &&
          tail_rows_ok(ci) && cm.batch == a.batch && ci.batch == a.batch;
 }
 
@@ -1021,6 +1065,8 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   m.pages = a.seq.pages;
   m.max_pages = a.seq.max_pages;
   m.page_shift = a.seq.page_shift;
+  m.staged = a.dense_cnt != nullptr;
+  if (a.dense_cnt) m.cnt = a.dense_cnt;
   // one workgroup per item (64 heads of one query, or of one decode split)
   const int64_t hgroups = a.n_h / kHG;
   if (is_decode(a)) {

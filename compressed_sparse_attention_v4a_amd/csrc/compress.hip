@@ -161,6 +161,30 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) o[v] = f32_to_bf16(x[v]);
     }
+  } else if (a.out_dt == kKV576) {
+    const int nq = c - a.rope_dims;
+    float am = 0.0f;
+    if (owner) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) am = fmaxf(am, g * VEC + v < nq ? fabsf(x[v]) : 0.0f);
+    }
+    am = block_max(am, red);
+    float scale = am / 448.0f;
+    if (!(scale > 0.0f)) scale = 1.0f;
+    if (owner) {
+      uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow * kv576_row_bytes(c, a.rope_dims);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const int ch = g * VEC + v;
+        if (ch < nq) {
+          const float y = x[v] / scale;
+          o[ch] = (uint8_t)(f32_to_e4m3_abs(fabsf(y)) | (y < 0.0f ? 0x80u : 0u));
+        } else {
+          reinterpret_cast<uint16_t*>(o + nq)[ch - nq] = f32_to_bf16(x[v]);
+        }
+      }
+      if (g == 0) reinterpret_cast<float*>(a.out_scale)[orow] = scale;
+    }
   } else if (a.out_dt == kFP8) {
     float am = 0.0f;
     if (owner) {

@@ -180,6 +180,32 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
       if (VEC == 8) *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2 % (VEC / 2)], w[3 % (VEC / 2)]);
       else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1 % (VEC / 2)]);
     }
+  } else if (a.out_dt == kKV576) {
+    // E4M3 codes for channels below c - rope_dims (one scale per row), bf16 above
+    const int nq = c - a.rope_dims;
+    const bool q8 = ch0 < nq;  // VEC divides rope_dims: a lane is all-codes or all-bf16
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) am = fmaxf(am, q8 ? fabsf(x[v]) : 0.0f);
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    float scale = am / 448.0f;
+    if (!(scale > 0.0f)) scale = 1.0f;
+    if (valid) {
+      uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow * kv576_row_bytes(c, a.rope_dims);
+      if (q8) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float y = x[v] / scale;
+          o[ch0 + v] = (uint8_t)(f32_to_e4m3_abs(fabsf(y)) | (y < 0.0f ? 0x80u : 0u));
+        }
+      } else {
+        uint16_t* ob = reinterpret_cast<uint16_t*>(o + nq);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ob[ch0 - nq + v] = f32_to_bf16(x[v]);
+      }
+      if (g == 0) reinterpret_cast<float*>(a.out_scale)[orow] = scale;
+    }
   } else if (a.out_dt == kFP8) {
     float am = 0.0f;
 #pragma unroll

@@ -16,7 +16,12 @@ int decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, void* s
 // Sets the calling thread's v4a_last_error() message; returns code.
 int report_error(int code, const char* msg);
 
-enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
+enum Dt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3, kKV576 = 4 };
+
+// Production main-cache row (kKV576): the c - rope_dims leading channels as E4M3 codes
+// scaled by one float32 per row, then the rope_dims rotated channels as bf16
+// (c = 512, rope_dims = 64: 448 + 128 = 576 bytes).
+__host__ __device__ inline int kv576_row_bytes(int c, int rope_dims) { return c + rope_dims; }
 
 // RoPE inverse frequencies base^(-2i/rope_dims), i < rope_dims/2 (rope_dims <= 64).
 constexpr int kMaxRopeDims = 64;
@@ -128,6 +133,7 @@ struct AttnArgs {
   float eps, rope_base, scale;
   RopeTab rope;
   SeqState seq;   // decode: per-sequence positions and paged rows (idx then holds pool rows)
+  const int32_t* dense_cnt;  // kModeHCADecode over a staged list: cnt[b] rows per sequence
 };
 
 // kModeHCADecode: one new token per sequence, every completed entry (ratio m_prime) and
@@ -153,6 +159,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
 
 size_t attn_workspace(const AttnArgs& a, int policy);
 bool attn_mfma_supported(const AttnArgs& a);  // the matrix-core kernels take this shape
+// Selected production-format rows (kKV576, c = 512) of a decode step -> bf16 staging
+// [batch][k][512].
+hipError_t launch_kv576_gather(const void* kv, const float* kv_scale, const int32_t* idx,
+                               const int32_t* cnt, const SeqState& seq, int64_t E_cap, int batch,
+                               int k, int rope_dims, void* staged, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, void* ws, int policy, hipStream_t s);
 
 // Fused decode front (one launch: main and index tail compression, window-row prep and

@@ -14,7 +14,7 @@ import torch
 from . import binding as B
 
 _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
-_NP_DT = {"f32": B.F32, "bf16": B.BF16, "fp8": B.FP8_E4M3, "mxfp4": B.MXFP4}
+_NP_DT = {"f32": B.F32, "bf16": B.BF16, "fp8": B.FP8_E4M3, "mxfp4": B.MXFP4, "kv576": B.KV576}
 
 
 def upload(x: np.ndarray, dt: str | None = None, device="cuda") -> torch.Tensor:
@@ -57,6 +57,9 @@ def compress(C, Z, B_, *, c, m, overlap, in_dt, out_dt="bf16", t0=0, T=None, tok
             out = torch.empty(batch, E_cap, c, dtype=_TORCH[out_dt], device=dev)
         elif out_dt == "fp8":
             out = torch.empty(batch, E_cap, c, dtype=torch.uint8, device=dev)
+            out_scale = torch.empty(batch, E_cap, dtype=torch.float32, device=dev)
+        elif out_dt == "kv576":
+            out = torch.empty(batch, E_cap, c + rope_dims, dtype=torch.uint8, device=dev)
             out_scale = torch.empty(batch, E_cap, dtype=torch.float32, device=dev)
         else:
             out = torch.empty(batch, E_cap, c // 2, dtype=torch.uint8, device=dev)
@@ -134,7 +137,7 @@ def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI,
                     q_gamma=None, kv_gamma=None, rope_dims=0, rope_dims_I=0, rope_base=10000.0,
                     eps=1e-6, scale=0.0, num_splits=0, out=None, with_scores=True, stream=None,
                     ws=None, noalloc=False, t_seq=None, page_table=None, page_entries=0,
-                    pool_rows=0):
+                    pool_rows=0, kv576=False, kv_scale=None):
     """One CSA decode step (tail compression of both instances, index top-k, ring insert and
     attention) through v4a_csa_decode_step.  C, Z: [batch][n_buf][2c] bf16; CI, ZI likewise
     with cI; qI [batch][n_hI][cI or cI/2]; q [batch][n_h][c].  Caches are updated in place.
@@ -162,7 +165,7 @@ def csa_decode_step(*, t, m, k, w, tail_base, C, Z, B_, CI, ZI, BI, kv_comp, KI,
         qI_scale=qI_scale, wI=wI, q=q, sink=sink, q_gamma=q_gamma, kv_gamma=kv_gamma,
         kv_ring=kv_ring, kv_new=kv_new, topk_idx=idx, topk_cnt=cnt, topk_score=sc, out=out,
         t_seq=t_seq, page_table=page_table, max_pages=page_table.shape[1] if paged else 0,
-        pool_rows=pool_rows, page_entries=page_entries)
+        pool_rows=pool_rows, page_entries=page_entries, kv576=int(kv576), kv_scale=kv_scale)
     if noalloc:
         B.v4a_csa_decode_step_noalloc(step, stream)
         return out, idx, cnt, sc

@@ -60,8 +60,14 @@ extern "C" {
  *   V4A_MXFP4    : OCP MX v1.0 MXFP4: E2M1 codes packed two per byte (element 2j
  *                  in the low nibble of byte j) with one E8M0 scale byte per 32
  *                  consecutive elements of a row (value = code * 2^(scale-127)).
+ *   V4A_KV576    : the production main-cache row of [Def] section 8: the c - rope_dims
+ *                  leading channels as E4M3 codes (one float32 scale per row, scale =
+ *                  max|x| / 448 over those channels, codes round to nearest even and
+ *                  saturate), then the rope_dims rotated channels as bf16; c + rope_dims
+ *                  bytes per row (576 at c = 512, rope_dims = 64).  Compressor output
+ *                  and decode-step cache format only.
  */
-typedef enum { V4A_F32 = 0, V4A_BF16 = 1, V4A_FP8_E4M3 = 2, V4A_MXFP4 = 3 } v4a_dtype;
+typedef enum { V4A_F32 = 0, V4A_BF16 = 1, V4A_FP8_E4M3 = 2, V4A_MXFP4 = 3, V4A_KV576 = 4 } v4a_dtype;
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 V4A_API const char* v4a_last_error(void);
@@ -322,6 +328,13 @@ typedef struct v4a_decode_step {
   int64_t max_pages;
   int64_t pool_rows;
   int page_entries;          /* a power of two */
+  /* Production cache rows ([Def] section 8): kv576 != 0 stores kv_comp as V4A_KV576 rows
+   * ([batch][E_cap][c + rope_dims] bytes, or the pool) with kv_scale float32 [batch][E_cap]
+   * (or [pool_rows]); the emitted entry is written in that format and the selected rows
+   * are dequantised to bf16 when gathered.  q, the ring and out stay bf16.  Needs the
+   * matrix-core shapes with c = 512. */
+  int kv576;
+  float* kv_scale;
 } v4a_decode_step;
 
 /* Byte offsets of the fields of v4a_decode_step in declaration order, for bindings

@@ -116,6 +116,18 @@ def decode_mxfp4_rows(packed, e8m0) -> np.ndarray:
     return out
 
 
+def decode_kv576_rows(rows, scale, c=512, rope_dims=64) -> np.ndarray:
+    """Production main-cache rows ("CSA And HCA: Definition, State, And Cost Model",
+    section 8: FP8 for the c - rope_dims leading channels, BF16 for the RoPE channels):
+    bytes [..][c + rope_dims] = E4M3 codes times the row's float32 scale, then the
+    little-endian bf16 channels."""
+    r = np.ascontiguousarray(rows, dtype=np.uint8)
+    nq = c - rope_dims
+    lead = decode_fp8_rows(r[..., :nq].reshape(-1, nq), np.asarray(scale, np.float32).reshape(-1))
+    tail = decode_bf16(np.ascontiguousarray(r[..., nq:]).view(np.uint16).reshape(-1, rope_dims))
+    return np.concatenate([lead, tail], axis=1).reshape(r.shape[:-1] + (c,))
+
+
 def decode(x, dt: str, scale=None) -> np.ndarray:
     """Stored array -> float64 for dt in {'f32', 'bf16', 'fp8', 'mxfp4'}."""
     if dt == "f32":
@@ -126,6 +138,8 @@ def decode(x, dt: str, scale=None) -> np.ndarray:
         return decode_fp8_rows(x, scale)
     if dt == "mxfp4":
         return decode_mxfp4_rows(x, scale)
+    if dt == "kv576":
+        return decode_kv576_rows(x, scale)
     raise ValueError(dt)
 
 

@@ -108,3 +108,15 @@ def mxfp4_rows(x) -> tuple[np.ndarray, np.ndarray]:
     code = code.reshape(x.shape[:-1] + (cols,))
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
     return packed, e8m0
+
+
+def kv576_rows(x, rope_dims=64) -> tuple[np.ndarray, np.ndarray]:
+    """Rows [..][c] -> production cache rows [..][c + rope_dims] bytes (E4M3 codes of the
+    c - rope_dims leading channels with one float32 scale per row, then the rope_dims
+    channels as little-endian bf16) and the scales [..]."""
+    x = np.asarray(x, dtype=np.float64)
+    c = x.shape[-1]
+    nq = c - rope_dims
+    codes, scale = fp8_e4m3_rows(x[..., :nq])
+    tail = bf16_bits(x[..., nq:]).view(np.uint8)
+    return np.concatenate([codes, tail], axis=-1), scale

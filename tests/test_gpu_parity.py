@@ -1283,3 +1283,116 @@ def test_hca_decode_paged_equals_contiguous():
     b_ = _run_hca(d, paged=(table, 1, pool_rows))
     for key in ("kv", "ring", "out"):
         assert torch.equal(a[key].view(torch.int16), b_[key].view(torch.int16)), key
+
+
+# ---------------------------------------------- production cache rows (576 bytes) --- #
+
+def check_kv576(rows, scale, ref, rope_dims=64, what=""):
+    """Production rows against float64 entries: the row scale follows max|x|/448 over the
+    E4M3 channels, every code is within half an E4M3 step, the rotated channels within one
+    bf16 ulp (plus the float32 pooling allowance)."""
+    c = ref.shape[-1]
+    nq = c - rope_dims
+    s = scale.detach().cpu().numpy().astype(np.float64).reshape(-1)
+    assert_close(s, np.abs(ref[:, :nq]).max(axis=1) / 448.0, rtol=1e-5, what=f"{what} row scale")
+    got = oracle.decode_kv576_rows(rows.detach().cpu().numpy(), s.astype(np.float32), c=c,
+                                   rope_dims=rope_dims)
+    v = ref[:, :nq] / s[:, None]
+    assert np.all(np.abs(got[:, :nq] - ref[:, :nq]) <= 0.5001 * fp8_step(v) * s[:, None] + 1e-7), \
+        f"{what}: E4M3 channels"
+    assert_bf16_close(got[:, nq:], ref[:, nq:], what=f"{what}: bf16 channels")
+
+
+def test_compress_kv576_emission():
+    """Main entries emitted straight into production rows ([Def] section 8)."""
+    rng = np.random.default_rng(12)
+    c, m, n = 512, 4, 256
+    C = synth.formats.bf16_bits(rng.standard_normal((n, 2 * c)) / math.sqrt(c))
+    Z = synth.formats.bf16_bits(rng.standard_normal((n, 2 * c)))
+    B_ = (0.3 * rng.standard_normal((2 * m, c))).astype(np.float32)
+    g = np.ones(c, np.float32)
+    log("compress emission kv576")
+    out, osc = _run_compress(C, Z, B_, c=c, m=m, overlap=True, in_dt="bf16", out_dt="kv576",
+                             gamma=g, rope_dims=64)
+    ref = _ref_compress(C, Z, B_, "bf16", tok_base=0, i_begin=0, i_end=n // m, c=c, m=m,
+                        overlap=True, gamma=g, rope_dims=64)
+    check_kv576(out[0], osc[0], ref, what="emission")
+
+
+def _kv576_state(ts, seed):
+    d = _ragged_csa_state(ts, seed=seed)
+    kvf = f64(d["kv_comp"], "bf16")
+    kvf = np.where(np.isnan(kvf), 0.0, kvf)  # the production rows hold finite codes
+    d["kv_rows"], d["kv_scale"] = synth.formats.kv576_rows(kvf)
+    return d
+
+
+def _run_kv576(d, m=4, k=512, w=128, paged=None):
+    ts = d["ts"]
+    g, gI = up(d["gamma"]), up(d["gammaI"])
+    kw = {}
+    if paged is None:
+        kv, kvs = up(d["kv_rows"]), up(d["kv_scale"])
+        KI, KIs = up(d["KI"]), up(d["KI_scale"])
+    else:
+        table, page, pool_rows = paged
+        kv = up(_to_pool(d["kv_rows"], table, page, pool_rows))
+        kvs = up(_to_pool(d["kv_scale"], table, page, pool_rows))
+        KI = up(_to_pool(d["KI"], table, page, pool_rows))
+        KIs = up(_to_pool(d["KI_scale"], table, page, pool_rows))
+        kw = dict(page_table=up(table), page_entries=page, pool_rows=pool_rows)
+    ring = up(d["ring"])
+    out, idx, cnt, sc = ops.csa_decode_step(
+        t=max(ts), m=m, k=k, w=w, tail_base=0, C=up(d["C"]), Z=up(d["Z"]), B_=up(d["B"]),
+        CI=up(d["CI"]), ZI=up(d["ZI"]), BI=up(d["BI"]), kv_comp=kv, KI=KI, KI_scale=KIs,
+        qI=up(d["qI"]), qI_scale=up(d["qI_scale"]), wI=up(d["wI"]), q=up(d["q"]), kv_ring=ring,
+        kv_new=up(d["kv_new"]), index_dt="fp8", gamma=g, gammaI=gI, q_gamma=g, kv_gamma=g,
+        rope_dims=64, t_seq=up(np.array(ts, np.int64)), kv576=True, kv_scale=kvs, **kw)
+    torch.cuda.synchronize()
+    if paged is not None:
+        table, page, _ = paged
+        kv, kvs = _from_pool(kv, table, page), _from_pool(kvs, table, page)
+    return dict(kv=kv, kvs=kvs, ring=ring, idx=idx, cnt=cnt, sc=sc, out=out)
+
+
+def test_decode_step_kv576():
+    """Decode with the main cache in production rows: the emitted entry is written in that
+    format, the selected rows are dequantised on gather, and the output matches the oracle
+    fed the stored rows (decoded exactly) and the step's own selection."""
+    ts = [131071, 40002, 2047, 5]
+    m, k, w, c = 4, 512, 128, 512
+    d = _kv576_state(ts, seed=23)
+    log(f"kv576 decode step positions {ts}")
+    r = _run_kv576(d)
+    for b, t in enumerate(ts):
+        E = (t + 1) // m
+        if (t + 1) % m == 0:
+            lo = m * (t // m) - m
+            rows = slice(max(0, -lo), 2 * m)
+            ref_kv = oracle.compress(f64(d["C"][b][rows], "bf16"), f64(d["Z"][b][rows], "bf16"),
+                                     d["B"], tok_base=max(lo, 0), i_begin=E - 1, i_end=E, c=c, m=m,
+                                     overlap=True, gamma=d["gamma"], rope_dims=64)
+            check_kv576(r["kv"][b, E - 1:E], r["kvs"][b, E - 1:E], ref_kv, what=f"t={t} entry")
+        cnt = int(r["cnt"][b])
+        assert cnt == min(k, E)
+        sel = r["idx"][b, :cnt].long()
+        kvd = oracle.decode_kv576_rows(r["kv"][b][sel].cpu().numpy(), r["kvs"][b][sel].cpu().numpy())
+        ringd = decode_stored(r["ring"][b], "bf16")
+        ref_o = oracle.attend_decode(f64(d["q"][b], "bf16"), kvd, ringd,
+                                     np.arange(cnt, dtype=np.int32), cnt, t=t, w=w,
+                                     q_gamma=d["gamma"], kv_gamma=d["gamma"], q_norm=True,
+                                     kv_norm=True, rope_dims=64)
+        assert_attn_close(decode_stored(r["out"][b], "bf16"), ref_o, atol=ATOL_BF16,
+                          rel_rms=REL_RMS_BF16, what=f"kv576 t={t}")
+
+
+def test_decode_step_kv576_paged_equals_contiguous():
+    ts = [131071, 40002, 2047, 5]
+    d = _kv576_state(ts, seed=24)
+    table, pool_rows = _paging(len(ts), d["E_cap"], 32, 7)
+    log("kv576 paged vs contiguous")
+    a, b_ = _run_kv576(d), _run_kv576(d, paged=(table, 32, pool_rows))
+    for key in ("kv", "kvs", "ring", "idx", "cnt", "sc", "out"):
+        x, y = a[key], b_[key]
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), key

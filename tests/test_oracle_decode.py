@@ -106,3 +106,20 @@ def test_mxfp4_decoder_code_points():
     # one scale per 32 elements
     two = oracle.decode_mxfp4_rows(np.full((1, 32), 0x22, np.uint8), np.array([[127, 130]], np.uint8))
     assert np.all(two[0, :32] == 1.0) and np.all(two[0, 32:] == 8.0)
+
+
+def test_kv576_row_decoder():
+    """A production cache row: E4M3 codes (times the row scale) for the leading channels,
+    bf16 for the rotated ones; code points from the OCP FP8 and bfloat16 definitions."""
+    c, rd = 16, 4
+    row = np.zeros(c + rd, np.uint8)
+    row[0] = 0x7E        # E4M3 448 (exponent 15, mantissa 6)
+    row[1] = 0x38        # 1.0
+    row[2] = 0xB8        # -1.0
+    row[3] = 0x01        # smallest subnormal 2^-9
+    bf = np.array([0x3F80, 0xC000, 0x3E80, 0x0000], np.uint16)  # 1, -2, 0.25, 0
+    row[c - rd:] = bf.view(np.uint8)
+    got = oracle.decode_kv576_rows(row[None], np.array([0.5], np.float32), c=c, rope_dims=rd)[0]
+    assert got[0] == 224.0 and got[1] == 0.5 and got[2] == -0.5 and got[3] == 2.0 ** -10
+    assert np.all(got[4:c - rd] == 0.0)
+    assert list(got[c - rd:]) == [1.0, -2.0, 0.25, 0.0]
