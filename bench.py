@@ -143,7 +143,9 @@ def main():
         import torch
         from compressed_sparse_attention_v4a_amd import binding as B
         B.lib()  # fail loudly if the HIP library is missing
-        res = decode_timing(args.decode_only, torch.cuda.current_stream(), rounds=5, warmup=2)
+        name = args.decode_only.replace("_kv576", "")
+        res = decode_timing(name, torch.cuda.current_stream(), rounds=5, warmup=2,
+                            kv576=args.decode_only.endswith("_kv576"))
         print(json.dumps({args.decode_only: res}))
         return
 
@@ -272,6 +274,8 @@ def main():
         torch.cuda.empty_cache()
         line["decode"] = {name: decode_timing(name, stream) for name in
                           ("csa_decode_flash_128k", "csa_decode_pro_1m")}
+        line["decode"]["csa_decode_flash_128k_kv576"] = decode_timing("csa_decode_flash_128k", stream,
+                                                                      kv576=True)
     if extra is not None:
         if args.no_decode:
             del T, kv, KI, idx, cnt, out, ws_i, ws_a, q4, qI4, wI3, loc3
@@ -477,14 +481,15 @@ def _quant_rows(x, dt):
     return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
 
 
-def decode_timing(name, stream, rounds=20, warmup=3):
+def decode_timing(name, stream, rounds=20, warmup=3, kv576=False):
     """One decode call = tail compression (main and index entry E - 1), index scan and
     top-k over the E entries, ring insert and sparse attention, for every sequence of the
     batch at t = L - 1, through v4a_csa_decode_step (the four separate calls are timed as
     well).  Inputs come from seeded device generators with the workload's shapes and
     distributions (the parity tests run the same path on host-generated ones).
     Reported: median over rounds with the 256 MB last-level cache flushed before each call
-    (cold, the headline) and back to back (warm)."""
+    (cold, the headline) and back to back (warm).  kv576: the main cache in the production
+    rows of 448 E4M3 + 64 bf16 channels (dequantised on gather)."""
     import torch
     from compressed_sparse_attention_v4a_amd import binding as B, costmodel, ops
     import synth
@@ -500,7 +505,16 @@ def decode_timing(name, stream, rounds=20, warmup=3):
     E = L // m
     sc = 1.0 / math.sqrt(c)
     rn = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device=dev) * std)
-    kv = rn(bsz, E, c).to(torch.bfloat16)
+
+    def make_kv():
+        x = rn(bsz, E, c).to(torch.bfloat16)
+        if not kv576:
+            return x, None
+        codes, sc_ = _quant_rows(x[..., :c - 64].float(), "fp8")
+        tail = x[..., c - 64:].contiguous().view(torch.uint8)
+        return torch.cat([codes, tail], dim=-1).contiguous(), sc_.contiguous()
+
+    kv, kvs = make_kv()
     KI, KIs = _quant_rows(rn(bsz, E, cI), idt)
     qI, qIs = _quant_rows(rn(bsz, 1, n_hI, cI), idt)
     wI = torch.rand(bsz, 1, n_hI, generator=gen, device=dev)
@@ -543,7 +557,7 @@ def decode_timing(name, stream, rounds=20, warmup=3):
         scale=0.0, tail_dt=B.BF16, index_dt=dt_code, attn_dt=B.BF16, C=C, Z=Z, B=Bm, gamma=g,
         CI=CI, ZI=ZI, BI=BI, gammaI=gI, kv_comp=kv, KI=KI, KI_scale=KIs, qI=qI, qI_scale=qIs,
         wI=wI, q=q, sink=None, q_gamma=g, kv_gamma=g, kv_ring=ring, kv_new=kv_new, topk_idx=idx,
-        topk_cnt=cnt, topk_score=None, out=out)
+        topk_cnt=cnt, topk_score=None, out=out, kv576=int(kv576), kv_scale=kvs)
     ws_s_bytes = B.v4a_csa_decode_step_workspace(step)
     ws_s = ops.workspace(ws_s_bytes, dev)
 
@@ -569,7 +583,8 @@ def decode_timing(name, stream, rounds=20, warmup=3):
         ms = [a.elapsed_time(b) for a, b in ev]
         return sorted(ms[:rounds])[rounds // 2], sorted(ms[rounds:])[rounds // 2]
 
-    cold_sep, warm_sep = timed(separate)
+    # the separate calls have no production-row path (the one-call step does)
+    cold_sep, warm_sep = timed(separate) if not kv576 else (float("nan"), float("nan"))
     cold, warm = timed(fused)
 
     # Second cold state: NCOPY disjoint copies of the whole decode state (caches, ring,
@@ -582,7 +597,8 @@ def decode_timing(name, stream, rounds=20, warmup=3):
     for i in range(ncopy):
         # every tensor the step reads or writes, per copy (kept alive here: the step
         # description holds raw device pointers)
-        tens = dict(kv_comp=rn(bsz, E, c).to(torch.bfloat16), C=C.clone(), Z=Z.clone(),
+        kv_i, kvs_i = make_kv()
+        tens = dict(kv_comp=kv_i, kv_scale=kvs_i, C=C.clone(), Z=Z.clone(),
                     CI=CI.clone(), ZI=ZI.clone(), qI=qI.clone(), qI_scale=qIs.clone(),
                     wI=wI.clone(), q=q.clone(), kv_ring=ring.clone(), kv_new=kv_new.clone())
         tens["KI"], tens["KI_scale"] = _quant_rows(rn(bsz, E, cI), idt)
@@ -592,7 +608,7 @@ def decode_timing(name, stream, rounds=20, warmup=3):
             m=m, k=k, w=w, num_splits=0, rope_dims=64, rope_dims_I=0, rope_base=10000.0, eps=1e-6,
             scale=0.0, tail_dt=B.BF16, index_dt=dt_code, attn_dt=B.BF16, B=Bm, gamma=g, BI=BI,
             gammaI=gI, sink=None, q_gamma=g, kv_gamma=g, topk_idx=idx, topk_cnt=cnt,
-            topk_score=None, out=out, **tens)
+            topk_score=None, out=out, kv576=int(kv576), **tens)
         copies.append((st, tens, ws_i_copy))
 
     def rot_call(i, s_=None):
@@ -624,23 +640,25 @@ def decode_timing(name, stream, rounds=20, warmup=3):
     torch.cuda.synchronize()
     cold_rot_graph = rot_timed(lambda i: graphs[i % ncopy].replay())
     warm_graph = rot_timed(lambda i: graphs[0].replay())
-    counts = costmodel.csa_decode_counts(bsz, L, m, k, w, n_h, c, n_hI, cI, idt)
+    counts = costmodel.csa_decode_counts(bsz, L, m, k, w, n_h, c, n_hI, cI, idt,
+                                         main_row_bytes=(c + 64 + 4) if kv576 else None)
     gbs = counts["total_bytes"] / (cold * 1e-3) / 1e9
     res = {"batch": bsz, "L": L, "n_h": n_h, "k": k, "index_keys": idt,
+           "main_rows": "kv576" if kv576 else "bf16",
            "entry": "v4a_csa_decode_step",
            "us_per_call": round(cold * 1e3, 2), "us_per_call_warm": round(warm * 1e3, 2),
            "us_per_call_cold_rotating": round(cold_rot * 1e3, 2),
            "us_per_call_cold_rotating_graph": round(cold_rot_graph * 1e3, 2),
            "us_per_call_warm_graph": round(warm_graph * 1e3, 2),
-           "us_per_call_separate_calls": round(cold_sep * 1e3, 2),
-           "us_per_call_separate_calls_warm": round(warm_sep * 1e3, 2),
+           "us_per_call_separate_calls": round(cold_sep * 1e3, 2) if not kv576 else None,
+           "us_per_call_separate_calls_warm": round(warm_sep * 1e3, 2) if not kv576 else None,
            "tokens_per_s": round(bsz / (cold * 1e-3), 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "algorithmic_bytes": counts["total_bytes"],
                         "frac_cold_rotating": round(counts["total_bytes"] / (cold_rot * 1e-3) / 1e9
                                                     / PEAK_HBM_GBS, 4)}}
-    del kv, KI, KIs, ws_s, copies, graphs
+    del kv, kvs, KI, KIs, ws_s, copies, graphs
     torch.cuda.empty_cache()
     return res
 

@@ -137,7 +137,11 @@ def hca_prefill_counts(n, m_prime=128, w=128, n_h=64, c=512, t0=0, elem=2) -> di
 
 
 def csa_decode_counts(batch, L, m=4, k=512, w=128, n_h=64, c=512, n_hI=64, cI=128,
-                      idt="fp8", elem=2) -> dict:
+                      idt="fp8", elem=2, main_row_bytes=None) -> dict:
+    """Bytes and FLOPs one decode call must move and do (batch sequences at L - 1).
+    main_row_bytes: bytes of one stored compressed entry (default c * elem; the production
+    row of section 8 is 576 + a 4-byte scale); window rows are read as bf16."""
+    mrb = c * elem if main_row_bytes is None else main_row_bytes
     t = L - 1
     E = (t + 1) // m
     cnt = min(k, E)
@@ -153,7 +157,7 @@ def csa_decode_counts(batch, L, m=4, k=512, w=128, n_h=64, c=512, n_hI=64, cI=12
         q_b = n_hI * cI * elem
     per_seq = {
         "index_read": E * key_b + q_b + n_hI * 4,
-        "gather_read": (cnt + nl) * c * elem,
+        "gather_read": cnt * mrb + nl * c * elem,
         "q_out": 2 * n_h * c * elem,
         "tail": 2 * m * (2 * c + 2 * cI) * elem * 2,
     }
