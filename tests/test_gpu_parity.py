@@ -1396,3 +1396,37 @@ def test_decode_step_kv576_paged_equals_contiguous():
         x, y = a[key], b_[key]
         assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), key
+
+
+def test_general_policy_at_matrix_core_shapes():
+    """v4a_set_kernel_policy(1) sends the V4-Flash shapes to the general kernels (SIMT
+    scores and attention); they meet the same gates as the matrix-core path."""
+    from compressed_sparse_attention_v4a_amd import binding as B
+    prev = B.v4a_set_kernel_policy(1)
+    try:
+        rng = np.random.default_rng(99)
+        T, t0, n_hI, cI, m, k = 120, 900, 64, 128, 4, 128
+        E = (t0 + T) // m
+        qI = synth.formats.bf16_bits(rng.standard_normal((T, n_hI, cI)))
+        KI = synth.formats.bf16_bits(rng.standard_normal((E, cI)))
+        wI = rng.random((T, n_hI)).astype(np.float32)
+        log("general policy: indexer and attention at the matrix-core shapes")
+        idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
+        torch.cuda.synchronize()
+        ref = _oracle_scores(f64(qI, "bf16"), f64(KI, "bf16"), wI.astype(np.float64), t0, m, E)
+        check_topk(idx[0].cpu().numpy(), cnt[0].cpu().numpy(), ref, t0=t0, m=m, k=k,
+                   gpu_scores=sc[0].cpu().numpy(), what="general indexer")
+        P = _small_prefill(7, 96, 64, 512, 512, 128, 896, True, 64)
+        g = up(P["g"])
+        out = ops.sparse_mqa_prefill(up(P["q"]), up(P["kv"]), up(P["local"]), up(P["idx"]),
+                                     up(P["cnt"]), t0=896, w=128, dt="bf16", loc_base=P["lb"],
+                                     sink=up(P["sink"]), q_gamma=g, kv_gamma=g, rope_dims=64)
+        torch.cuda.synchronize()
+        ref = oracle.attend_csa(f64(P["q"], "bf16"), f64(P["kv"], "bf16"), f64(P["local"], "bf16"),
+                                P["idx"], P["cnt"], loc_base=P["lb"], t0=896, w=128, sink=P["sink"],
+                                q_gamma=P["g"], kv_gamma=P["g"], q_norm=True, kv_norm=True,
+                                rope_dims=64)
+        assert_attn_close(decode_stored(out[0], "bf16"), ref, atol=ATOL_BF16, rel_rms=REL_RMS_BF16,
+                          what="general attention")
+    finally:
+        B.v4a_set_kernel_policy(prev)
