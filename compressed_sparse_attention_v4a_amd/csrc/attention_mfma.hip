@@ -74,11 +74,13 @@ constexpr int kMaxCand = 2048; // longest candidate list (k + w) served here; lo
 // exact general kernel, so O is never rescaled.
 constexpr float kLazy = 64.0f;
 
-// XOR applied to the low three bits of the 16-byte chunk index of row r.  Eight
-// consecutive rows get eight different values (score reads: eight lanes, eight
-// rows, one chunk column), and rows 4h..4h+3 get values in four different chunk
-// pairs (transposing V reads: four rows x two adjacent chunks per 16 lanes).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// XOR applied to the low four bits of the 16-byte chunk index of row r.  The LDS has
+// 64 four-byte banks: a 16-byte read serves 16 lanes per cycle, which must cover the 16
+// chunk positions of a 256-byte span, and a transposing 8-byte read 32 lanes.  Sixteen
+// consecutive rows get sixteen different values (score reads: 16 lanes, 16 rows, one
+// chunk column), and rows 4h..4h+3 differ in bits 2-3 (transposing V reads: four rows x
+// four adjacent chunks per 32 lanes, each row in its own 64-byte quarter).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const int h = kRowsPerWave * wv + r;
-      const uint32_t voff = (uint32_t)(lane ^ swz(r)) << 4;  // swz(h) = swz(r)
+      const uint32_t voff = (uint32_t)(lane ^ swz(h)) << 4;
       dma_b128(qrows + (int64_t)h * kRowBytes, voff, dst + h * kRowBytes);
     }
   };
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
                      : (uint64_t)kvl_b + (uint64_t)(-1 - myid) * kRowBytes;
   };
   // row 8 wv + r of a chunk into chunk buffer dst; lane i carries chunk i of the global
-  // row into LDS chunk i ^ swz(r) (row 8 wv + r has swz(r))
+  // row into LDS chunk i ^ swz(8 wv + r)
   auto gather_row = [&](uint64_t addr, char* dst, int r) {
     // readlane returns int: go through uint32_t so the low half is not sign-extended
     const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(addr >> 32), r) << 32) |
@@ -335,7 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     // per-row offsets would hold eight registers across the loop
     uint32_t lb = (uint32_t)lane << 4;
     asm volatile("" : "+v"(lb));
-    dma_b128(reinterpret_cast<const char*>(ra), lb ^ ((uint32_t)swz(r) << 4), dst + (kRowsPerWave * wv + r) * kRowBytes);
+    dma_b128(reinterpret_cast<const char*>(ra), lb ^ ((uint32_t)swz(kRowsPerWave * wv + r) << 4),
+             dst + (kRowsPerWave * wv + r) * kRowBytes);
   };
   auto fill = [&](const Item& it, char* dst, int64_t r0, int raw) {
     const uint64_t addr = row_addr(it, r0, raw);
@@ -345,23 +348,26 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 
   // ---- per-lane LDS byte offsets (everything step-dependent is an immediate) --
   // score reads: row 32 cc + l32, channels 256 kx + 16 s + 8 hl .. + 7, i.e. chunk
-  // 8 (4 kx + (s >> 2)) + (2 (s & 3) + hl), swizzled within its 128-byte group
+  // 32 kx + 16 (s >> 3) + (2 (s & 7) + hl), swizzled within its 256-byte group
   const int srow = 32 * cc + l32;
-  int sb[4];
+  int sb[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4) + 512 * kx;
+  for (int u = 0; u < 8; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4) + 512 * kx;
   // transposing V reads, 16-lane group G = lane >> 4, J = lane & 15 = 4 i + q:
   //   row 16 p + 8 e + 4 (G >> 1) + i, channels 32 T + 16 (G & 1) + 4 q .. +3, T = 2 wv + nt
   //   (wave wv owns the 64 contiguous channels 64 wv ..); chunk 8 wv + 4 nt + x lies at
-  //   byte 128 wv + 16 ((4 nt + x) ^ swz(row)) of its row
-  int vbase[2];
+  //   byte 16 ((8 wv + 4 nt + x) ^ swz(row)) of its row, swz(row) = 4 i + 2 e + (G >> 1)
+  int vbase[2][2];  // [nt][e]; step p adds 16 rows (16 KiB)
   {
     const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
     const int x = 2 * (G & 1) + (q >> 1);
-    const int y = (i << 1) | (G >> 1);  // swz of the row
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-      vbase[nt] = (4 * (G >> 1) + i) * kRowBytes + 128 * wv + (((4 * nt + x) ^ y) << 4) + 8 * (q & 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * e + 4 * (G >> 1) + i;
+        vbase[nt][e] = row * kRowBytes + (((8 * wv + 4 * nt + x) ^ swz(row)) << 4) + 8 * (q & 1);
+      }
   }
   const int pbase = lane * 16;
 
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int j = g8 + 8 * (u0 + u);
-          v[u] = __builtin_bit_cast(u32x4, lds_read_b128(qbufp, hq * kRowBytes + ((j ^ swz(l8)) << 4)));
+          v[u] = __builtin_bit_cast(u32x4, lds_read_b128(qbufp, hq * kRowBytes + ((j ^ swz(hq)) << 4)));
           gm[u][0] = *reinterpret_cast<const float4*>(qg_s + 8 * j);
           gm[u][1] = *reinterpret_cast<const float4*>(qg_s + 8 * j + 4);
         }
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
             }
           }
           const u32x4 pk = {pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]), pk_bf16(y[4], y[5]), pk_bf16(y[6], y[7])};
-          *reinterpret_cast<u32x4*>(qbufp + hq * kRowBytes + ((j ^ swz(l8)) << 4)) = pk;
+          *reinterpret_cast<u32x4*>(qbufp + hq * kRowBytes + ((j ^ swz(hq)) << 4)) = pk;
         }
       }
       ss += __shfl_xor(ss, 8, 64);
@@ -463,8 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     bf16x8 qb[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s)
-      qb[s] = lds_read_b128(qbufp, (32 * hh + l32) * kRowBytes + (((2 * (s & 3) + hl) ^ swz(l32)) << 4) +
-                                       128 * (4 * kx + (s >> 2)));
+      qb[s] = lds_read_b128(qbufp, (32 * hh + l32) * kRowBytes + (((32 * kx + 2 * s + hl) ^ swz(l32)) << 4));
     const float qinv = qinv_s[32 * hh + l32];
     // the next chunk's gather overwrites the query rows: every fragment read has returned
     // before the first loop barrier
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-          if (s + 2 < 16) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 3] + 128 * ((s + 2) >> 2));
+          if (s + 2 < 16) ka[(s + 2) % 3] = lds_read_b128(buf, sb[(s + 2) & 7] + 256 * ((s + 2) >> 3));
           __builtin_amdgcn_sched_barrier(0);
           S = mfma32(ka[s % 3], qb[s], S);
           if ((s & 3) == 1 && more) gather_row(naddr, nbuf, s >> 2);
@@ -627,9 +632,8 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         auto vread = [&](int it) -> bf16x8 {
           // it = 2 p + nt
-          const int off = vbase[it & 1] + 16384 * (it >> 1);
-          const u32x2 v1 = lds_read_tr(buf, off);
-          const u32x2 v2 = lds_read_tr(buf, off + 8 * kRowBytes);
+          const u32x2 v1 = lds_read_tr(buf, vbase[it & 1][0] + 16384 * (it >> 1));
+          const u32x2 v2 = lds_read_tr(buf, vbase[it & 1][1] + 16384 * (it >> 1));
           const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
           return __builtin_bit_cast(bf16x8, cat);
         };

@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
       const int e = 4 * ins + (lane >> 4);
       int64_t se = s0 + e;
       if (se >= Ewg) se = Ewg - 1;         // padding rows: any visible entry (masked later)
-      const int ch = (lane & 15) ^ (e & 7);
+      const int ch = (lane & 15) ^ (e & 15);  // chunk position ^ entry within its 16-entry tile
       const char* src = kb + se * kRowB + ch * 16;
       const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void)(buf + ins * 1024);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -393,8 +393,14 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
 #pragma unroll
       for (int i = 0; i < 4; ++i) wgt[mt][i] = a.wI[qrow + 16 * mt + 4 * g + i];
   }
-  const int bb0 = jj * kRowB + (((2 * g) ^ (jj & 7)) << 4);
-  const int bb1 = jj * kRowB + (((2 * g + 1) ^ (jj & 7)) << 4);
+  // K fragment of k-step ks: chunk kchunk(ks, g) of entry jj, stored at chunk position
+  // kchunk ^ jj.  A 16-byte LDS read serves 16 lanes per cycle (64 four-byte banks; lanes
+  // grouped by bit 5 and the parity of bits 2-4 of the lane index), and with rows of 256
+  // bytes the XOR with the whole entry index gives the 16 lanes of a group 16 different
+  // chunk positions.
+  int bb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) bb[ks] = jj * kRowB + ((kchunk(ks, g) ^ jj) << 4);
   float* scw = sc[wv];
   uint32_t* ckw = ckey[wv];
   int32_t* ciw = cidx[wv];
@@ -452,7 +458,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     // K fragments of entry tile et + 1 are read while tile et is multiplied; the four head
     // tiles are independent accumulation chains, interleaved k-step by k-step
     auto kread = [&](int et, int ks) {
-      return *reinterpret_cast<const bf16x8*>(buf + ((ks & 1) ? bb1 : bb0) + et * 16 * kRowB + 128 * (ks >> 1));
+      return *reinterpret_cast<const bf16x8*>(buf + bb[ks] + et * 16 * kRowB);
     };
     bf16x8 kv[2][4];
 #pragma unroll
