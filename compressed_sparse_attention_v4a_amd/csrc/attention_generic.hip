@@ -257,35 +257,6 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(AttnArgs a, floa
   attend_item(a, part, b, j, split, blockIdx.y * kHG, 0, blockIdx.y == 0 && split == 0);
 }
 
-// Items listed by the matrix-core kernel for exact recomputation (a softmax reference
-// it could not use).  redo[0] = count, redo[1 + r] = item; items are numbered as in
-// that kernel: decode (sequence, 64-head group, split) with the split fastest,
-// prefill/HCA (position from the last, sequence, 64-head group) with the group fastest.
-// grid: x = list stride, y = 8-head group within the 64-head group.
-__global__ __launch_bounds__(kThreads) void attn_redo_kernel(AttnArgs a, float* part, const int* redo,
-                                                             int split_len) {
-  const int n = redo[0];
-  const int hgroups = a.n_h / 64;
-  for (int r = blockIdx.x; r < n; r += gridDim.x) {
-    const int64_t item = redo[1 + r];
-    int b, j = 0, split = 0, hgrp;
-    if (a.mode == kModeDecode) {
-      split = (int)(item % a.num_splits);
-      const int64_t q = item / a.num_splits;
-      hgrp = (int)(q % hgroups);
-      b = (int)(q / hgroups);
-    } else {
-      const int64_t bh = (int64_t)a.batch * hgroups;
-      const int64_t u = item / bh, q = item % bh;
-      b = (int)(q / hgroups);
-      hgrp = (int)(q % hgroups);
-      j = a.T - 1 - (int)u;
-    }
-    attend_item(a, part, b, j, split, hgrp * 64 + blockIdx.y * kHG, split_len, false);
-    __syncthreads();
-  }
-}
-
 // Merge of decode partial states (online-softmax combination over the splits, then the
 // sink, normalisation and inverse RoPE at t).  One wave per (head, sequence), four heads
 // per block; lane l holds channels 8 l + 512 i .. + 7.  Every split's state is loaded in
@@ -400,15 +371,6 @@ hipError_t launch_attention_generic(const AttnArgs& a, void* ws, hipStream_t s) 
   if (a.mode == kModeDecode && a.num_splits > 1)
     err = launch_attention_merge(a, reinterpret_cast<const float*>(ws), s);
   return err;
-}
-
-hipError_t launch_attention_redo(const AttnArgs& a, float* part, const int* redo, int split_len,
-                                 hipStream_t s) {
-  const size_t shmem = generic_smem(a.c);
-  // listed items are rare (never for normalised queries and rows): a few workgroups walk
-  // the list, so the launch costs little when it is empty
-  hipLaunchKernelGGL(attn_redo_kernel, dim3(2, 64 / kHG), dim3(kThreads), shmem, s, a, part, redo, split_len);
-  return hipGetLastError();
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s) {

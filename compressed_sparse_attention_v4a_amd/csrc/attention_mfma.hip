@@ -24,10 +24,8 @@
 //   * Softmax with a fixed reference maximum per head (the first chunk's
 //     maximum): probabilities are exp2(s - m_ref) < 2^64, so O is never rescaled.
 //     A chunk maximum past the reference by more than that is noted and acted on
-//     after the pass: the workgroup lists the item for the exact general kernel,
-//     which recomputes it in float32 afterwards; a decode split instead restarts
-//     with the pass maximum as reference (neither is triggered for normalised
-//     queries and rows).  The score accumulator layout of the 32x32 tile is
+//     after the pass: the item restarts with the pass maximum as reference, which
+//     no chunk can exceed (never triggered for normalised queries and rows).  The score accumulator layout of the 32x32 tile is
 //     already the A-operand layout of P V (candidate k-slots permuted identically
 //     on both sides), so each wave packs its P to bf16 and stores it to LDS as a
 //     ready-made fragment.
@@ -70,8 +68,8 @@ constexpr int kRowsPerWave = kNC / kWaves;  // rows of a chunk gathered by each 
 constexpr int kMaxCand = 2048; // longest candidate list (k + w) served here; longer lists take the general kernel
 // Probabilities are exp2(s - m_ref) with m_ref fixed after the first chunk.  They
 // stay below 2^kLazy; O (|v| < 2^6, at most 2^11 candidates) stays below 2^81, far
-// from float32 overflow.  A chunk maximum that grows further sends the item to the
-// exact general kernel, so O is never rescaled.
+// from float32 overflow.  A chunk maximum that grows further makes the item restart
+// with a larger reference, so O is never rescaled.
 constexpr float kLazy = 64.0f;
 
 // XOR applied to the low four bits of the 16-byte chunk index of row r.  The LDS has
@@ -143,7 +141,6 @@ struct MqaArgs {
   const float* q_gamma;   // [512] or null
   uint16_t* out;          // [batch][T or 1][n_h][512]
   float* part;            // decode partials [batch][splits][n_h][514]
-  int* redo;              // [1 + items]: count, then items for the exact general kernel
   int64_t t0, E_cap, lrow_base, n_lrows;
   int batch, T, n_h, k, w, m_prime, rope_dims, mode, splits, split_len;
   float eps, rope_base, qscale;
@@ -487,13 +484,13 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     };
 
     // Whether a wave saw a chunk maximum past the reference (read after the barrier that
-    // follows the flags, once per pass over the list); a decode split then takes the
-    // largest chunk maximum of the tile as its new reference, so that the next pass
-    // cannot overflow.
+    // follows the flags, once per pass over the list); the item then takes the largest
+    // chunk maximum of the tile as its new reference, so that the next pass cannot
+    // overflow.
     auto overflowed = [&]() -> bool {
       if (!uni(flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3] | flag_s[4] | flag_s[5] | flag_s[6] | flag_s[7]))
         return false;
-      if constexpr (kDec) m_ref = fmaxf(m_ref, tile_max());
+      m_ref = fmaxf(m_ref, tile_max());
       return true;
     };
 
@@ -512,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       }
       l_part = 0.0f;
       bool ovf = false;          // a chunk maximum past the reference (this lane's head)
-      float mx_run = -INFINITY;  // largest chunk maximum so far (decode restarts)
+      float mx_run = -INFINITY;  // largest chunk maximum so far (the reference of a restart)
       // one chunk; MORE: a next chunk exists (compile time, so that the gathers interleaved
       // below need no branches; the last chunk is a copy without them)
       auto chunk = [&](int64_t c, auto more_t) -> bool {
@@ -595,17 +592,13 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax), false, false);
           lmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * qinv;  // qinv > 0: order kept
         }
-        if constexpr (kDec) mx_run = fmaxf(mx_run, lmax);
+        mx_run = fmaxf(mx_run, lmax);
         if (c == 0) {
           // reference maximum: this chunk's maximum over the tile's four waves
           if (hl == 0) mx_s[wv][l32] = lmax;
           wait_lgkmcnt<0>();
           block_sync();
-          if constexpr (kDec) {
-            m_ref = fmaxf(m_ref, tile_max());  // raised by a restart
-          } else {
-            m_ref = tile_max();
-          }
+          m_ref = fmaxf(m_ref, tile_max());  // raised by a restart
           if (m_ref == -INFINITY) m_ref = 0.0f;
         } else {
           ovf = ovf || lmax > m_ref + kLazy;
@@ -662,15 +655,12 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
       for (int64_t c = 0; c + 1 < nchunks; ++c)
         if (!chunk(c, std::true_type{})) return false;
       if (nchunks > 0 && !chunk(nchunks - 1, std::false_type{})) return false;
-      // an overflow is acted on once the pass is over: the item is abandoned (prefill) or
-      // the pass restarts with a larger reference (decode); the values computed meanwhile
-      // are discarded
+      // an overflow is acted on once the pass is over: the pass restarts with a larger
+      // reference; the values computed meanwhile are discarded
       {
         const bool any = __ballot(ovf) != 0;
         if (lane == 0) flag_s[wv] = any ? 1 : 0;
-        if constexpr (kDec) {
-          if (hl == 0) mx_s[wv][l32] = mx_run;
-        }
+        if (hl == 0) mx_s[wv][l32] = mx_run;
       }
       wait_lgkmcnt<0>();
       block_sync();  // flags visible
@@ -786,32 +776,19 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
     {
       f32x16 O[2][2];
       float l_part;
-      if constexpr (kDec) {
-        // decode splits restart instead of leaving the item to the exact kernel (which would
-        // cost every decode call a launch): run() has raised the reference; the gather in
-        // flight lands, chunk 0 is gathered again and the loop starts over.  Each restart
-        // raises some head's reference to one of its own chunk maxima, so restarts are
-        // finite.
-        if (__builtin_expect(!run(O, l_part, raw1), 0)) {
-          do {
-            wait_vmcnt<0>();
-            block_sync();
-            fill(cur, kvbuf + par * kChunkBytes, 0, raw0);
-          } while (!run(O, l_part, raw1));
-        }
-        finish(O, l_part);
-      } else if (run(O, l_part, raw1)) {
-        finish(O, l_part);
-      } else {
-        // a chunk maximum ran past the reference: list the item for the exact general
-        // kernel, which recomputes it after this one, and move on (after the gather in
-        // flight has landed)
-        wait_vmcnt<0>();
-        if (tid == 0) {
-          const int slot = atomicAdd(a.redo, 1);
-          a.redo[1 + slot] = (int)item;
-        }
+      // A chunk maximum past the reference by more than kLazy: run() has raised the
+      // reference to the pass maximum; the gather in flight lands, chunk 0 is gathered
+      // again and the pass starts over (no rescaling of O inside the loop, and no second
+      // launch for such items).  The raised reference is at least every chunk maximum of
+      // the list, so the second pass always completes.
+      if (__builtin_expect(!run(O, l_part, raw1), 0)) {
+        do {
+          wait_vmcnt<0>();
+          block_sync();
+          fill(cur, kvbuf + par * kChunkBytes, 0, raw0);
+        } while (!run(O, l_part, raw1));
       }
+      finish(O, l_part);
     }
   }
 }
@@ -917,31 +894,21 @@ static int decode_split_len(const AttnArgs& a) {
   return (int)per;
 }
 
-// Work items of the matrix-core kernel (64 heads of one query, or of one decode split).
-static int64_t mfma_items(const AttnArgs& a) {
-  const int64_t per = is_decode(a) ? (a.num_splits > 1 ? a.num_splits : 1) : a.T;
-  return (int64_t)a.batch * (a.n_h / kHG) * per;
-}
-
-// workspace: [window rows bf16][decode partials f32][recomputation list int32]
+// workspace: [window rows bf16][decode partials f32]
 size_t attn_mfma_workspace(const AttnArgs& a) {
   size_t loc = ((size_t)a.batch * local_rows(a) * kC * 2 + 255) / 256 * 256;
   size_t part = 0;
   if (is_decode(a) && a.num_splits > 1)
     part = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
-  const size_t redo = (size_t)(1 + mfma_items(a)) * sizeof(int);
-  return loc + part + redo;
+  return loc + part;
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, const float* part, hipStream_t s);
-hipError_t launch_attention_redo(const AttnArgs& a, float* part, const int* redo, int split_len,
-                                 hipStream_t s);
 
-// workspace pieces: [window rows bf16][decode partials f32][recomputation list int32]
+// workspace pieces: [window rows bf16][decode partials f32]
 struct MfmaWs {
   uint16_t* lws;
   float* part;
-  int* redo;
 };
 static MfmaWs mfma_ws(const AttnArgs& a, void* ws) {
   const int64_t nl_rows = local_rows(a);
@@ -949,16 +916,11 @@ static MfmaWs mfma_ws(const AttnArgs& a, void* ws) {
   w.lws = reinterpret_cast<uint16_t*>(ws);
   const size_t loc_bytes = ((size_t)a.batch * nl_rows * kC * 2 + 255) / 256 * 256;
   w.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + loc_bytes);
-  size_t part_bytes = 0;
-  if (is_decode(a) && a.num_splits > 1)
-    part_bytes = ((size_t)a.batch * a.num_splits * a.n_h * (kC + 2) * sizeof(float) + 255) / 256 * 256;
-  w.redo = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + loc_bytes + part_bytes);
   return w;
 }
 
 static LocalPrepArgs prep_args(const AttnArgs& a, const MfmaWs& w) {
   LocalPrepArgs lp{};
-  lp.redo = w.redo;
   lp.gamma = a.kv_gamma;
   lp.ws = w.lws;
   lp.n_lrows = local_rows(a);
@@ -1028,7 +990,6 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   const MfmaWs wsp = mfma_ws(a, ws);
   uint16_t* lws = wsp.lws;
   float* part = wsp.part;
-  int* redo = wsp.redo;
   const LocalPrepArgs lp = prep_args(a, wsp);
   hipError_t err = hipSuccess;
   if (!a.prep_done) {
@@ -1048,7 +1009,6 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
   m.q_gamma = a.q_gamma;
   m.out = reinterpret_cast<uint16_t*>(a.out);
   m.part = part;
-  m.redo = redo;
   m.t0 = a.t0;
   m.E_cap = a.E_cap;
   m.lrow_base = lp.lrow_base;
@@ -1092,9 +1052,7 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(mqa_mfma_kernel<kModeHCA>, dim3(grid), dim3(kThreads), 0, s, m);
   else
     hipLaunchKernelGGL(mqa_mfma_kernel<kModeCSA>, dim3(grid), dim3(kThreads), 0, s, m);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_attention_redo(a, part, redo, 0, s);
+  return hipGetLastError();
 }
 
 }  // namespace v4a

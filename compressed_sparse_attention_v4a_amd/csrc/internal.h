@@ -77,7 +77,6 @@ struct LocalPrepArgs {
   const uint16_t* kv_new;
   const float* gamma;
   uint16_t* ws;          // [batch][n_lrows][512]
-  int* redo;             // count of the recomputation list, cleared here
   int64_t lrow_base, loc_base, n_loc, n_lrows, t;
   int w, rope_dims, decode;
   float eps, rope_base;

@@ -15,7 +15,6 @@ constexpr int kWinC = 512;  // channels of a window row (64 lanes x 8)
 
 // Block blk of sequence b (256 threads, tid = thread index): rows 4 blk .. 4 blk + 3, one per wave.
 __device__ __forceinline__ void window_prep_block(const LocalPrepArgs& a, int64_t blk, int b, int tid) {
-  if (blk == 0 && b == 0 && tid == 0) a.redo[0] = 0;
   const int lane = tid & 63;
   const int64_t r = blk * 4 + (tid >> 6);
   if (r >= a.n_lrows) return;

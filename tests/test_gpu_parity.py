@@ -372,8 +372,11 @@ def _aligned_late_rows(rng, kv, c, frac=0.5):
 @pytest.mark.parametrize("mode", ["csa", "hca"])
 def test_attention_reference_overflow_path(mode):
     """Logit spreads beyond the kernels' fixed-reference range (query RMSNorm weight 4,
-    late candidates aligned with the query) go through the exact recomputation.  The
-    candidate rows keep unit weight so the outputs stay O(1) for the absolute gate."""
+    late candidates aligned with the query) restart with the raised reference.  The
+    candidate rows keep unit weight so the outputs stay O(1) for the absolute gate.  The
+    kernel rounds the prepared query (q * gamma / rms(q)) to bf16, so its logit error, and
+    with a peaked softmax the output error, grows with gamma: the element gate is the unit-
+    weight gate times gamma; the per-row RMS gate is unchanged."""
     n, n_h, c, k, w, t0 = 300, 64, 512, 256, 64, 700
     P = _small_prefill(4242, n, n_h, c, k, w, t0, sink=False, rd=64)
     rng = np.random.default_rng(77)
@@ -405,7 +408,7 @@ def test_attention_reference_overflow_path(mode):
         ref = oracle.attend_hca(f64(P["q"], "bf16"), f64(P["kv"], "bf16"), f64(P["local"], "bf16"),
                                 loc_base=P["lb"], t0=t0, m_prime=4, w=w, q_gamma=g, kv_gamma=gk,
                                 q_norm=True, kv_norm=True, rope_dims=64, rows=rows)
-    assert_attn_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16,
+    assert_attn_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16 * float(g[0]),
                       rel_rms=REL_RMS_BF16, what=f"{mode} overflow")
 
 
@@ -767,7 +770,7 @@ def _bits(x):
 def test_prefill_chain_bitwise_reproducible(csa8k):
     """The 8K CSA prefill chain (both compressors, indexer top-k, attention) gives the same
     bits when run twice; so does the attention with query RMSNorm weights of 4, whose
-    overflowing items are listed in arbitrary order for the exact recomputation."""
+    items overflow the fixed reference and restart."""
     cfg, d = csa8k
     log("determinism: csa prefill n=8192 twice")
     g, gI = up(d["gamma"]), up(d["gammaI"])
