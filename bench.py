@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "c728f240ce24368ab2572eca6d0227cfe23b626d5b82a0ddc7c3a0b544717283",
-           "fetch_bytes": 857262624, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "b247781649266bd790f137a4f9fe98e4b7d7fab2215b780106a215bac7c2d95f",
+           "fetch_bytes": 857210055, "write_bytes": 536870912}
 
 
 def parse():
