@@ -506,16 +506,27 @@ int v4a::decode_step_run(const v4a_decode_step* d, void* ws, size_t ws_bytes, vo
   if (phys) aa.idx = phys;  // the attention gathers pool rows
   hipStream_t s = (hipStream_t)stream;
   void* ws_a = reinterpret_cast<char*>(ws) + ws_i + ws_p;
-  hipError_t e;
-  if (v4a::decode_front_supported(cm, ci, aa, policy)) {
-    // tail compressions, window prep and ring insert in one launch
-    e = v4a::launch_decode_front(cm, ci, aa, ws_a, s);
+  hipError_t e = hipSuccess;
+  const bool front = v4a::decode_front_supported(cm, ci, aa, policy);
+  if (front && p.filter && v4a::indexer_fuses_compress(p, ci)) {
+    // the scan compresses the index entry itself; the main entry, the window prep and the
+    // ring insert ride in the top-k final launch (a few workgroups, latency-bound), so no
+    // launch of their own precedes the scan
+    v4a::FrontArgs fa;
+    e = v4a::decode_front_args(cm, aa, ws_a, fa);
+    if (e == hipSuccess) e = v4a::launch_indexer_topk(ia, p, ws, s, &ci, &fa);
     aa.prep_done = 1;
   } else {
-    e = v4a::launch_compress(cm, s);
-    if (e == hipSuccess) e = v4a::launch_compress(ci, s);
+    if (front) {
+      // tail compressions, window prep and ring insert in one launch
+      e = v4a::launch_decode_front(cm, ci, aa, ws_a, s);
+      aa.prep_done = 1;
+    } else {
+      e = v4a::launch_compress(cm, s);
+      if (e == hipSuccess) e = v4a::launch_compress(ci, s);
+    }
+    if (e == hipSuccess) e = v4a::launch_indexer_topk(ia, p, ws, s);
   }
-  if (e == hipSuccess) e = v4a::launch_indexer_topk(ia, p, ws, s);
   if (e == hipSuccess && kv576)
     e = v4a::launch_kv576_gather(d->kv_comp, d->kv_scale, d->topk_idx, d->topk_cnt, st, d->E_cap,
                                  d->batch, d->k, d->rope_dims, reinterpret_cast<char*>(ws) + ws_i, s);

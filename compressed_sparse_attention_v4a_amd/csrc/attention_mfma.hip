@@ -805,14 +805,15 @@ __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
 // they overlap instead of paying a launch and a memory round trip each.  Row b of the
 // grid: block v < n_comp runs compressor group v of the main instance in wave 0 and of
 // the index instance in wave 1 (first, as they have the longest dependency chain);
-// blocks n_comp .. prepare the window rows and insert the new token into the ring.
-// GM, GI: lanes per entry (c / 8) of the main and index instance (bf16 tails).
+// blocks n_comp .. prepare the window rows (kFrontRows per block) and insert the new
+// token into the ring.  GM, GI: lanes per entry (c / 8) of the main and index instance
+// (bf16 tails).
 template <int GM, int GI>
 __global__ __launch_bounds__(256) void decode_front_kernel(CompressArgs cm, CompressArgs ci,
                                                            LocalPrepArgs lp, int n_comp) {
   const int b = blockIdx.y;
   if ((int)blockIdx.x >= n_comp) {
-    window_prep_block(lp, (int)blockIdx.x - n_comp, b, threadIdx.x);
+    window_prep_block<kFrontRows / 4>(lp, (int)blockIdx.x - n_comp, b, threadIdx.x);
     return;
   }
   const int64_t vb = blockIdx.x;
@@ -960,10 +961,21 @@ bool decode_front_supported(const CompressArgs& cm, const CompressArgs& ci, cons
          tail_rows_ok(ci) && cm.batch == a.batch && ci.batch == a.batch;
 }
 
+hipError_t decode_front_args(const CompressArgs& cm, const AttnArgs& a, void* attn_ws,
+                             FrontArgs& out) {
+  out.cm = cm;
+  out.lp = prep_args(a, mfma_ws(a, attn_ws));
+  out.n_prep = (int)((out.lp.n_lrows + kFrontRows - 1) / kFrontRows);
+  out.gm = cm.n_entries > 0 ? cm.c / 8 : 64;
+  out.n_comp = cm.n_entries > 0 ? (int)(((int64_t)cm.n_entries + 64 / out.gm - 1) / (64 / out.gm)) : 0;
+  if (out.gm != 16 && out.gm != 32 && out.gm != 64) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
 hipError_t launch_decode_front(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
                                void* attn_ws, hipStream_t s) {
   const LocalPrepArgs lp = prep_args(a, mfma_ws(a, attn_ws));
-  const int n_prep = (int)((lp.n_lrows + 3) / 4);
+  const int n_prep = (int)((lp.n_lrows + kFrontRows - 1) / kFrontRows);
   auto groups = [](const CompressArgs& x) -> int64_t {
     return x.n_entries > 0 ? ((int64_t)x.n_entries + 64 / (x.c / 8) - 1) / (64 / (x.c / 8)) : 0;
   };

@@ -5,6 +5,8 @@
 // emitted entry).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,10 +38,70 @@ struct Vec<uint16_t> {
   }
 };
 
+// N consecutive float32 (N = 2, 4 or 8), in 16-byte loads where N allows
+template <int N>
+__device__ __forceinline__ void load_f32(const float* p, float* dst) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < N; v += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(p + v);
+      dst[v] = x.x; dst[v + 1] = x.y; dst[v + 2] = x.z; dst[v + 3] = x.w;
+    }
+  } else {
+    const float2 x = *reinterpret_cast<const float2*>(p);
+    dst[0] = x.x; dst[1] = x.y;
+  }
+}
+
+// N consecutive elements (N = 2, 4 or 8) of a row, as float
+template <typename T, int N>
+__device__ __forceinline__ void load_n(const void* base, int64_t off, float* dst) {
+  if constexpr (std::is_same<T, float>::value) {
+    load_f32<N>(reinterpret_cast<const float*>(base) + off, dst);
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + off;
+    uint32_t w[N / 2];
+    if constexpr (N == 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    } else if constexpr (N == 4) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x; w[1] = x.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      dst[2 * i] = __uint_as_float(w[i] << 16);
+      dst[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+// Sum of squares of the c = G VEC channels of an entry whose lane g of the group holds
+// channels g VEC .. g VEC + VEC - 1: a perfect binary tree over the channel index (pairs of
+// neighbouring channels, then pairs of pairs, ...), so the rounded result is the same for
+// every VEC, i.e. for every lane layout of the entry.  No contraction into FMAs.
+template <int VEC, int G>
+__device__ __forceinline__ float tree_sum_sq(const float (&x)[VEC]) {
+  float sq[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) sq[v] = __fmul_rn(x[v], x[v]);
+#pragma unroll
+  for (int w = 1; w < VEC; w <<= 1)
+#pragma unroll
+    for (int v = 0; v < VEC; v += 2 * w) sq[v] = __fadd_rn(sq[v], sq[v + w]);
+  float ss = sq[0];
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) ss = __fadd_rn(ss, __shfl_xor(ss, o, 64));
+  return ss;
+}
+
 // Entries pooling at most 8 positions (CSA, m <= 4 with overlap): one group of G = c / VEC
 // lanes per entry holds every pooled position in registers, so the softmax needs no merge
 // across lanes and the RMSNorm / quantisation maxima are shuffle reductions within the
-// group.  Each wave covers 64 / G entries; no LDS, no barriers.
+// group.  Each wave covers 64 / G entries; no LDS, no barriers.  VEC (channels per lane)
+// changes only the layout: results are bit-identical for every VEC.
 // RMSNorm weights of a call without RMSNorm (read, never applied; VEC <= 8)
 __device__ __attribute__((aligned(16))) const float kOnes[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
 
@@ -66,9 +128,9 @@ __device__ __forceinline__ SlotEntry slot_entry(const CompressArgs& a, int b, in
 }
 
 // One wave: entries 64 / G * vblock .. of sequence b; lane = lane of the wave.
-template <typename Tin, int G>
+template <typename Tin, int G, int VEC = Vec<Tin>::N>
 __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_t vblock, int b, int lane) {
-  constexpr int VEC = Vec<Tin>::N;
+  static_assert(VEC == 2 || VEC == 4 || VEC == 8, "2, 4 or 8 channels per lane");
   constexpr int kMaxPos = 8;
   const int c = a.c, m = a.m;
   const int g = lane % G, ch0 = g * VEC;
@@ -85,11 +147,7 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
   float gw[VEC];
   {
     const float* gp = a.gamma ? a.gamma + ch0 : kOnes;
-#pragma unroll
-    for (int v = 0; v < VEC; v += 4) {
-      const float4 g4 = *reinterpret_cast<const float4*>(gp + v);
-      gw[v] = g4.x; gw[v + 1] = g4.y; gw[v + 2] = g4.z; gw[v + 3] = g4.w;
-    }
+    load_f32<VEC>(gp, gw);
   }
   // every load first, with no branch between them (a branch per position would make
   // each position's loads wait for the previous ones): logits and values of the pooled
@@ -104,15 +162,11 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
     const bool sa = uu < m;
     const int64_t pos = sa ? (int64_t)m * i + uu : (int64_t)m * (i - 1) + (uu - m);
     const int64_t off = (pos - se.tok_base) * width + (sa ? 0 : c) + ch0;
-    Vec<Tin>::load(Zb, off, lg[u]);
-    Vec<Tin>::load(Cb, off, cv[u]);
+    load_n<Tin, VEC>(Zb, off, lg[u]);
+    load_n<Tin, VEC>(Cb, off, cv[u]);
     const float* brow = a.B + (int64_t)uu * c + ch0;  // B^a rows 0..m-1, B^b rows m..2m-1
     float bv[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; v += 4) {
-      const float4 b4 = *reinterpret_cast<const float4*>(brow + v);
-      bv[v] = b4.x; bv[v + 1] = b4.y; bv[v + 2] = b4.z; bv[v + 3] = b4.w;
-    }
+    load_f32<VEC>(brow, bv);
     // arithmetic masking (the loaded values are finite), so no load sits under a branch
     const float lmask = use ? 0.0f : -INFINITY, cmask = use ? 1.0f : 0.0f;
 #pragma unroll
@@ -122,7 +176,6 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
     }
   }
   float x[VEC];
-  float ss = 0.0f;
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
     float mx = lg[0][v];
@@ -137,11 +190,9 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
       ac = fmaf(e, cv[u][v], ac);
     }
     x[v] = valid ? ac / sm : 0.0f;
-    ss = fmaf(x[v], x[v], ss);
   }
   if (a.gamma) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float ss = tree_sum_sq<VEC, G>(x);
     const float inv = 1.0f / sqrtf(ss / (float)c + a.eps);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) x[v] = x[v] * inv * gw[v];
@@ -168,8 +219,12 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
   if (a.out_dt == kF32) {
     if (valid) {
       float* o = reinterpret_cast<float*>(a.out) + orow * c + ch0;
+      if constexpr (VEC % 4 == 0) {
 #pragma unroll
-      for (int v = 0; v < VEC; v += 4) *reinterpret_cast<float4*>(o + v) = make_float4(x[v], x[v + 1], x[v + 2], x[v + 3]);
+        for (int v = 0; v < VEC; v += 4) *reinterpret_cast<float4*>(o + v) = make_float4(x[v], x[v + 1], x[v + 2], x[v + 3]);
+      } else {
+        *reinterpret_cast<float2*>(o) = make_float2(x[0], x[1]);
+      }
     }
   } else if (a.out_dt == kBF16) {
     if (valid) {
@@ -177,8 +232,9 @@ __device__ __forceinline__ void compress_rows_body(const CompressArgs& a, int64_
 #pragma unroll
       for (int v = 0; v < VEC; v += 2) w[v / 2] = (uint32_t)f32_to_bf16(x[v]) | ((uint32_t)f32_to_bf16(x[v + 1]) << 16);
       uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + orow * c + ch0;
-      if (VEC == 8) *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2 % (VEC / 2)], w[3 % (VEC / 2)]);
-      else *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1 % (VEC / 2)]);
+      if constexpr (VEC == 8) *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+      else if constexpr (VEC == 4) *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+      else *reinterpret_cast<uint32_t*>(o) = w[0];
     }
   } else if (a.out_dt == kKV576) {
     // E4M3 codes for channels below c - rope_dims (one scale per row), bf16 above

@@ -13,9 +13,11 @@
 //   3. topk_merge_kernel: per query, the same select over the tiles' candidates.
 // The MFMA paths for the production shapes live in indexer_mfma.hip and reuse
 // the two top-k kernels.
+#include "compress_rows.h"
 #include "device_common.h"
 #include "internal.h"
 #include "topk.h"
+#include "window_prep.h"
 
 namespace v4a {
 
@@ -299,7 +301,11 @@ __global__ __launch_bounds__(1024) void topk_merge_reg_kernel(IndexerArgs a, int
 //           4096 entries with key >= L, in index order, into the slice's own region.
 //   final : one workgroup per query selects the k largest candidates exactly (ties to
 //           the lower index) and writes them in ascending index order: from registers
-//           up to 4096 candidates, else streaming them from the workspace.
+//           up to 4096 candidates, else streaming them from the workspace.  In a decode
+//           step (GM > 0) the launch also carries the step's front work in workgroups
+//           1.. of each sequence's row (FrontArgs): the final selection is a few
+//           latency-bound workgroups, so the front runs beside it instead of in a launch
+//           of its own ahead of the scan.
 constexpr int kFiltSlice = 4096;      // entries per filter workgroup (256 threads x 16)
 constexpr int kFiltGroups = 4096;     // group maxima per query at most (256 threads x 16)
 constexpr int kFinalThreads = 256;    // final kernel: few waves keep its barriers and scans short
@@ -368,10 +374,24 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(IndexerArgs a, const f
   if (threadIdx.x == 0) counts[q * n_slices + sl] = tot;
 }
 
+template <int GM>
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(IndexerArgs a, int n_slices,
                                                           const int* counts,
                                                           const uint32_t* cand_key,
-                                                          const int32_t* cand_idx) {
+                                                          const int32_t* cand_idx, FrontArgs f) {
+  if constexpr (GM > 0) {
+    if (blockIdx.x > 0) {  // front work of sequence blockIdx.y (T == 1: block 0 selects)
+      const int blk = (int)blockIdx.x - 1, b = blockIdx.y;
+      if (blk >= f.n_comp) {
+        window_prep_block<kFrontRows / 4>(f.lp, blk - f.n_comp, b, threadIdx.x);
+        return;
+      }
+      const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+      if (wv == 0 && (int64_t)blk * (64 / GM) < f.cm.n_entries)
+        compress_rows_body<uint16_t, GM>(f.cm, blk, b, lane);
+      return;
+    }
+  }
   __shared__ uint32_t hist[768];
   __shared__ int sh[40];
   __shared__ int pre[65];  // candidate offset of every slice (n_slices <= 64)
@@ -477,7 +497,15 @@ bool indexer_fused_supported(int64_t Emax, int T, int n_hI, int cI, int k, int d
 hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s);
 bool indexer_mfma_supported(int T, int n_hI, int cI, int dt);
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
-                                      uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s);
+                                      uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s,
+                                      const CompressArgs* ci);
+
+bool indexer_fuses_compress(const IndexerPlan& p, const CompressArgs& ci) {
+  // the scan runs (matrix-core scan, not the all-in-LDS prefill kernel) and the entry is a
+  // short-window bf16 entry of 128 channels: 2 channels per lane of one wave
+  const int npos = ci.overlap ? 2 * ci.m : ci.m;
+  return p.mfma_scan && !p.fused && ci.in_dt == kBF16 && ci.c == 128 && npos <= 8;
+}
 
 IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k, int dt,
                          int policy, bool serving) {
@@ -527,7 +555,7 @@ IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, 
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void* ws,
-                               hipStream_t s) {
+                               hipStream_t s, const CompressArgs* cfuse, const FrontArgs* front) {
   float* scores = reinterpret_cast<float*>(ws);
   uint32_t* ck = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + p.score_bytes);
   int32_t* ci = reinterpret_cast<int32_t*>(ck + (size_t)a.batch * a.T * p.n_tiles * p.kc);
@@ -544,19 +572,35 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void*
     w += (rows * p.n_slices * 4 + 255) / 256 * 256;
     uint32_t* fkey = reinterpret_cast<uint32_t*>(w);
     int32_t* fidx = reinterpret_cast<int32_t*>(fkey + rows * p.n_slices * kFiltSlice);
-    err = launch_indexer_scores_mfma(a, scores, p.ld, gmax, p.ng_ld, p.gshift, s);
+    err = launch_indexer_scores_mfma(a, scores, p.ld, gmax, p.ng_ld, p.gshift, s, cfuse);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)p.n_slices, (unsigned)a.T, (unsigned)a.batch),
                        dim3(256), 0, s, a, scores, p.ld, gmax, p.ng_ld, p.gshift, p.n_slices, counts,
                        fkey, fidx);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)a.T, (unsigned)a.batch), dim3(kFinalThreads), 0,
-                       s, a, p.n_slices, counts, fkey, fidx);
+    if (!front) {
+      hipLaunchKernelGGL(topk_final_kernel<0>, dim3((unsigned)a.T, (unsigned)a.batch), dim3(kFinalThreads),
+                         0, s, a, p.n_slices, counts, fkey, fidx, FrontArgs{});
+      return hipGetLastError();
+    }
+    if (a.T != 1) return hipErrorInvalidValue;
+    const dim3 fgrid((unsigned)(1 + front->n_comp + front->n_prep), (unsigned)a.batch);
+    if (front->gm == 64)
+      hipLaunchKernelGGL(topk_final_kernel<64>, fgrid, dim3(kFinalThreads), 0, s, a, p.n_slices, counts,
+                         fkey, fidx, *front);
+    else if (front->gm == 32)
+      hipLaunchKernelGGL(topk_final_kernel<32>, fgrid, dim3(kFinalThreads), 0, s, a, p.n_slices, counts,
+                         fkey, fidx, *front);
+    else if (front->gm == 16)
+      hipLaunchKernelGGL(topk_final_kernel<16>, fgrid, dim3(kFinalThreads), 0, s, a, p.n_slices, counts,
+                         fkey, fidx, *front);
+    else
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   if (Emax > 0) {
     if (p.mfma_scan) {
-      err = launch_indexer_scores_mfma(a, scores, p.ld, nullptr, 0, 0, s);
+      err = launch_indexer_scores_mfma(a, scores, p.ld, nullptr, 0, 0, s, cfuse);
     } else {
       dim3 grid((unsigned)a.T, (unsigned)((Emax + kScoreThreads - 1) / kScoreThreads),
                 (unsigned)a.batch);

@@ -14,6 +14,7 @@
 //     (4 x 8-bit passes, LDS histograms, ballot-based order-preserving compaction)
 //     for its query and writes the selected entry indices in ascending order.
 // Workgroups are issued longest-first (late queries see the most entries).
+#include "compress_rows.h"
 #include "device_common.h"
 #include "internal.h"
 #include "topk.h"
@@ -534,9 +535,14 @@ constexpr int kScanTiles = kScanEntries / 4 / 16;  // 16-entry tiles per wave
 
 // GS >= 0: also writes gmax, per query the maximum order key (score_key) of every group of
 // 16 << GS consecutive entries, for the threshold filter of the decode top-k.
+// ci.out set (decode step, bf16 tails, c^I = 128): the index entry that sequence b's new
+// token completes, entry E - 1, is compressed here by the wave whose entries include it,
+// before that wave's first key load (its own store, then its own load of the row: program
+// order on one wave), instead of by a launch the scan would wait for.  The layout of 2
+// channels per lane gives the same bits as the compressor's (see compress_rows_body).
 template <int DT, int GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(
-    IndexerArgs a, float* scores, int64_t ld, uint32_t* gmax, int64_t ng_ld) {
+    IndexerArgs a, float* scores, int64_t ld, uint32_t* gmax, int64_t ng_ld, CompressArgs ci) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, jj = lane & 15;
@@ -545,6 +551,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   const int64_t E = (t + 1) / a.m;
   const int64_t e0 = (int64_t)blockIdx.x * kScanEntries + wv * (kScanEntries / 4);
   if (e0 >= E) return;
+  if (ci.out) {
+    const SlotEntry se = slot_entry(ci, b, 0);
+    if (se.emit && se.i >= e0 && se.i < e0 + kScanEntries / 4) {
+      compress_rows_body<uint16_t, 64, 2>(ci, 0, b, lane);
+      wait_vmcnt<0>();  // the entry (and its scale) written before any key load below
+    }
+  }
   const int64_t q = (int64_t)b * a.T + j;
   const int64_t qrow = q * kHeads;
   float wq[4][4];  // w_h (times the FP8 row scale of q): head 16 mt + 4 g + i
@@ -739,7 +752,10 @@ bool indexer_mfma_supported(int T, int n_hI, int cI, int dt) {
 }
 
 hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64_t ld,
-                                      uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s) {
+                                      uint32_t* gmax, int64_t ng_ld, int gshift, hipStream_t s,
+                                      const CompressArgs* ci) {
+  CompressArgs cz{};
+  if (ci) cz = *ci;  // cz.out == nullptr: no fused compression
   const int64_t Emax = (a.t0 + a.T) / a.m;
   dim3 grid((unsigned)((Emax + kScanEntries - 1) / kScanEntries), (unsigned)a.T, (unsigned)a.batch);
   // GS template: the group size of the optional group maxima (-1: none)
@@ -747,13 +763,13 @@ hipError_t launch_indexer_scores_mfma(const IndexerArgs& a, float* scores, int64
   do {                                                                                           \
     if (a.dt == kFP8)                                                                            \
       hipLaunchKernelGGL((indexer_scan_kernel<kFP8, gs>), grid, dim3(256), 0, s, a, scores, ld,  \
-                         gmax, ng_ld);                                                           \
+                         gmax, ng_ld, cz);                                                       \
     else if (a.dt == kMXFP4)                                                                     \
       hipLaunchKernelGGL((indexer_scan_kernel<kMXFP4, gs>), grid, dim3(256), 0, s, a, scores, ld, \
-                         gmax, ng_ld);                                                           \
+                         gmax, ng_ld, cz);                                                       \
     else                                                                                         \
       hipLaunchKernelGGL((indexer_scan_kernel<kBF16, gs>), grid, dim3(256), 0, s, a, scores, ld, \
-                         gmax, ng_ld);                                                           \
+                         gmax, ng_ld, cz);                                                       \
   } while (0)
   if (!gmax) V4A_SCAN(-1);
   else if (gshift == 0) V4A_SCAN(0);

@@ -153,8 +153,23 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 // assume neither, are not planned)
 IndexerPlan indexer_plan(int batch, int T, int64_t t0, int n_hI, int cI, int m, int k, int dt,
                          int policy, bool serving = false);
+// Decode-step work that rides in the top-k final launch of the threshold-filter path
+// (extra workgroups per sequence): the main-cache tail compression, the window-row prep
+// and the ring insert, which the attention needs but the index scan does not.
+struct FrontArgs {
+  CompressArgs cm;     // main instance (n_entries 0: nothing to emit)
+  LocalPrepArgs lp;    // window rows into the attention workspace, new token into the ring
+  int n_comp, n_prep;  // workgroups per sequence of each role
+  int gm;              // lanes per main entry, c / 8 (16, 32 or 64)
+};
+
+// ci (decode step, or NULL): the index-cache entry that the step's new token completes is
+// compressed inside the scan (indexer_fuses_compress(p, *ci) must hold).  front (or NULL,
+// threshold-filter plans only): run with the final selection.
 hipError_t launch_indexer_topk(const IndexerArgs& a, const IndexerPlan& p, void* ws,
-                               hipStream_t s);
+                               hipStream_t s, const CompressArgs* ci = nullptr,
+                               const FrontArgs* front = nullptr);
+bool indexer_fuses_compress(const IndexerPlan& p, const CompressArgs& ci);
 
 size_t attn_workspace(const AttnArgs& a, int policy);
 bool attn_mfma_supported(const AttnArgs& a);  // the matrix-core kernels take this shape
@@ -172,5 +187,8 @@ bool decode_front_supported(const CompressArgs& cm, const CompressArgs& ci, cons
                             int policy);
 hipError_t launch_decode_front(const CompressArgs& cm, const CompressArgs& ci, const AttnArgs& a,
                                void* attn_ws, hipStream_t s);
+// The same front work minus the index instance, described for the top-k final launch.
+hipError_t decode_front_args(const CompressArgs& cm, const AttnArgs& a, void* attn_ws,
+                             FrontArgs& out);
 
 }  // namespace v4a
