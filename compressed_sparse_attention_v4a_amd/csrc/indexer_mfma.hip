@@ -537,9 +537,9 @@ constexpr int kScanTiles = kScanEntries / 4 / 16;  // 16-entry tiles per wave
 // 16 << GS consecutive entries, for the threshold filter of the decode top-k.
 // ci.out set (decode step, bf16 tails, c^I = 128): the index entry that sequence b's new
 // token completes, entry E - 1, is compressed here by the wave whose entries include it,
-// before that wave's first key load (its own store, then its own load of the row: program
-// order on one wave), instead of by a launch the scan would wait for.  The layout of 2
-// channels per lane gives the same bits as the compressor's (see compress_rows_body).
+// before that wave's first key load, instead of by a launch the scan would wait for.  The
+// layout of 2 channels per lane gives the same bits as the compressor's (see
+// compress_rows_body).
 template <int DT, int GS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void indexer_scan_kernel(
     IndexerArgs a, float* scores, int64_t ld, uint32_t* gmax, int64_t ng_ld, CompressArgs ci) {
@@ -553,10 +553,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
   if (e0 >= E) return;
   if (ci.out) {
     const SlotEntry se = slot_entry(ci, b, 0);
-    if (se.emit && se.i >= e0 && se.i < e0 + kScanEntries / 4) {
-      compress_rows_body<uint16_t, 64, 2>(ci, 0, b, lane);
-      wait_vmcnt<0>();  // the entry (and its scale) written before any key load below
-    }
+    // no wait for the stores: this wave's later load of the row follows them in program
+    // order to the same addresses, which one wave's memory operations keep
+    if (se.emit && se.i >= e0 && se.i < e0 + kScanEntries / 4) compress_rows_body<uint16_t, 64, 2>(ci, 0, b, lane);
   }
   const int64_t q = (int64_t)b * a.T + j;
   const int64_t qrow = q * kHeads;
@@ -686,7 +685,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
       // consecutive scores
 #pragma unroll
       for (int u = 0; u < kB / 4; ++u) {
-        const float v = g == 0 ? res[4 * u] : g == 1 ? res[4 * u + 1] : g == 2 ? res[4 * u + 2] : res[4 * u + 3];
+        // a bit-mask select: written as a conditional chain, the compiler indexed res[] by g
+        // through scratch memory (a store and a dependent load per batch)
+        uint32_t v_bits = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v_bits |= __float_as_uint(res[4 * u + i]) & (0u - (uint32_t)(g == i));
+        const float v = __uint_as_float(v_bits);
         const int64_t s = e0 + 16 * (b0 + 4 * u + g) + jj;
         if (s < E) srow[s] = v;
       }

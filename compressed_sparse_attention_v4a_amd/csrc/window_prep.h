@@ -12,8 +12,7 @@ namespace v4a {
 namespace {
 
 constexpr int kWinC = 512;  // channels of a window row (64 lanes x 8)
-constexpr int kFrontRows = 4;  // window rows per decode-front workgroup (one per wave: the
-                                // accurate RoPE of several rows in one wave runs serially)
+constexpr int kFrontRows = 16;  // window rows per decode-front workgroup (4 per wave)
 
 // Block blk of sequence b (256 threads, tid = thread index): rows 4 RPW blk .. 4 RPW blk +
 // 4 RPW - 1, RPW per wave (wave wv takes rows wv, wv + 4, ...), every row's load issued
@@ -79,7 +78,8 @@ __device__ __forceinline__ void window_prep_block(const LocalPrepArgs& a, int64_
       float y0 = x[e], y1 = x[e + 1];
       if (a.rope_dims > 0 && d >= r0) {
         float cs, sn;
-        rope_cs((double)pos, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
+        // the row is stored as bf16: the hardware sine after the float64 reduction
+        rope_cs_fast((double)pos, a.rope.inv_freq[(d - r0) >> 1], cs, sn);
         const float z0 = y0 * cs - y1 * sn, z1 = y0 * sn + y1 * cs;
         y0 = z0;
         y1 = z1;
