@@ -27,7 +27,7 @@ ATOL_F32 = 1e-4
 
 
 def up(x, dt=None):
-    return ops.upload(x, dt, DEV)
+    return None if x is None else ops.upload(x, dt, DEV)
 
 
 def f64(x, dt):
@@ -529,7 +529,8 @@ def _run_decode(cfg, d, num_splits=0):
     ops.compress(up(d["CI"]), up(d["ZI"]), up(d["BI"]), c=cI, m=m, overlap=True, in_dt="bf16",
                  out_dt=idt, t0=t, T=1, tok_base=base, gamma=gI, out=KI, out_scale=KIs)
     qI = up(d["qI"]).unsqueeze(1)
-    qIs = up(d["qI_scale"]).unsqueeze(1)
+    qIs = up(d["qI_scale"])
+    qIs = qIs.unsqueeze(1) if qIs is not None else None  # bf16 keys carry no scales
     idx, cnt, sc = ops.indexer_topk(qI, KI, up(d["wI"]).unsqueeze(1), dt=idt, m=m, k=k, t0=t,
                                     qI_scale=qIs, KI_scale=KIs)
     qg = up(d["q_gamma"]) if "q_gamma" in d else g
@@ -559,8 +560,8 @@ def _check_decode(cfg, d, r, check_seqs, sink=None):
         else:
             assert_bf16_close(decode_stored(r["KI"][b, E - 1], idt), ref_ki, what="index key")
         # scores over the GPU's cache state, then the top-k gate
-        KId = decode_stored(r["KI"][b, :E], idt, r["KIs"][b, :E])
-        qId = oracle.decode(d["qI"][b], idt, d["qI_scale"][b])
+        KId = decode_stored(r["KI"][b, :E], idt, r["KIs"][b, :E] if r["KIs"] is not None else None)
+        qId = oracle.decode(d["qI"][b], idt, d["qI_scale"][b] if d["qI_scale"] is not None else None)
         ref_s = oracle.index_scores(qId[None], KId, d["wI"][b][None].astype(np.float64), t0=t, m=m,
                                     ld=E)
         check_topk(r["idx"][b:b + 1].cpu().numpy(), r["cnt"][b:b + 1].cpu().numpy(), ref_s, t0=t,
@@ -596,23 +597,33 @@ def _run_decode_step(cfg, d, num_splits=0):
     return dict(kv=kv, KI=KI, KIs=KIs, ring=ring, idx=idx, cnt=cnt, sc=sc, out=out)
 
 
-@pytest.mark.parametrize("name,batch,L", [("csa_decode_flash_128k", 4, 8192),
-                                          ("csa_decode_pro_1m", 2, 16384),
-                                          ("csa_decode_flash_128k", 3, 8190),
-                                          ("csa_decode_flash_128k", 2, 131072)])
-def test_decode_step_matches_separate_calls(name, batch, L):
-    """v4a_csa_decode_step (one call, fused front launch) equals the four separate calls bit
-    for bit -- caches, ring, selection, scores and output -- and passes the oracle checks.
-    L = 8190 puts the new token mid-block: nothing is emitted.  L = 131072 (E = 32768) is the
-    128K workload's shape, where the selection takes the threshold-filter path that the
-    timed decode call uses."""
-    cfg = synth.configs.workload(name, batch=batch, L=L)
+@pytest.mark.parametrize("name,batch,L,idt", [("csa_decode_flash_128k", 4, 8192, None),
+                                              ("csa_decode_pro_1m", 2, 16384, None),
+                                              ("csa_decode_flash_128k", 3, 8190, None),
+                                              ("csa_decode_flash_128k", 2, 131072, None),
+                                              ("csa_decode_flash_128k", 2, 131072, "bf16"),
+                                              ("csa_decode_pro_1m", 2, 262144, None)])
+def test_decode_step_matches_separate_calls(name, batch, L, idt):
+    """v4a_csa_decode_step (one call) equals the four separate calls bit for bit -- caches,
+    ring, selection, scores and output -- and passes the oracle checks.  L = 8190 puts the
+    new token mid-block: nothing is emitted.  L = 131072 (E = 32768, fp8 or bf16 index keys)
+    and L = 262144 (E = 65536, MXFP4) take the threshold-filter selection that the timed
+    decode calls use: there the index scan compresses the new index entry itself (2
+    channels per lane against the compressor kernel's 8) and the main entry, window prep
+    and ring insert run inside the final selection's launch."""
+    over = dict(batch=batch, L=L)
+    if idt:
+        over["idt"] = idt
+    cfg = synth.configs.workload(name, **over)
     cfg["id"] = 11
     d = synth.configs.gen_csa_decode(cfg)
     log(f"decode step vs separate calls {name} batch={batch} L={L}")
     ref = _run_decode(cfg, d)
     got = _run_decode_step(cfg, d)
     for key in ("kv", "KI", "KIs", "ring", "idx", "cnt", "sc", "out"):
+        if ref[key] is None:
+            assert got[key] is None, key
+            continue
         a, b = ref[key].reshape(-1), got[key].reshape(-1)
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), key
