@@ -179,7 +179,7 @@ __device__ __forceinline__ void radix_emit(const uint32_t (&key)[PER], int E, ui
 // Register form of the one-wave top-k for E <= 64 PER: lane l holds the contiguous keys
 // [l per, l per + per), per = ceil(E / 64); radix_kth finds the k-th key and radix_emit
 // places each lane's selected keys with one packed prefix sum of (keys > kth, keys ==
-// kth).  Same result as wave_topk.
+// kth).
 template <int PER>
 __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int32_t* oidx,
                               float* osc, int32_t* ocnt) {
@@ -243,88 +243,6 @@ __device__ uint32_t wave_shrink_pairs(uint32_t* ckey, int32_t* cidx, int n, int 
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
   return kmin;
-}
-
-// Exact top-k of one query over its scores sc[0..E) by one wave; writes the
-// selected indices in ascending order, -1 padding, the count and the scores.
-__device__ void wave_topk(const float* sc, int E, int k, uint32_t* hist, int* sh, int32_t* oidx,
-                          float* osc, int32_t* ocnt) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  const int n = E < k ? E : k;
-  if (E <= k) {
-    for (int i = lane; i < E; i += 64) {
-      oidx[i] = i;
-      if (osc) osc[i] = sc[i];
-    }
-  } else {
-    uint32_t prefix = 0, pmask = 0;
-    int rem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = lane; i < 256; i += 64) hist[i] = 0u;
-      __builtin_amdgcn_wave_barrier();
-      for (int i = lane; i < E; i += 64) {
-        const uint32_t key = score_key(sc[i]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __builtin_amdgcn_wave_barrier();
-      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                     c3 = hist[4 * lane + 3];
-      const uint32_t mine = c0 + c1 + c2 + c3;
-      uint32_t suf = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += v;
-      }
-      uint32_t above = suf - mine;
-      const uint32_t cs[4] = {c0, c1, c2, c3};
-      int found_d = -1, found_above = 0;
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (above < (uint32_t)rem && above + cs[q] >= (uint32_t)rem) {
-          found_d = 4 * lane + q;
-          found_above = (int)above;
-        }
-        above += cs[q];
-      }
-      const uint64_t who = __ballot(found_d >= 0);
-      const int src = __ffsll((unsigned long long)who) - 1;
-      const int d = __shfl(found_d, src, 64);
-      const int ab = __shfl(found_above, src, 64);
-      prefix |= (uint32_t)d << shift;
-      pmask |= 255u << shift;
-      rem -= ab;
-    }
-    const uint32_t kth = prefix;
-    const int need_eq = rem;
-    int base_sel = 0, base_eq = 0;
-    for (int i0 = 0; i0 < E && base_sel < k; i0 += 64) {
-      const int i = i0 + lane;
-      const bool valid = i < E;
-      const float s = valid ? sc[i] : 0.0f;
-      const uint32_t key = valid ? score_key(s) : 0u;
-      const bool gt = valid && key > kth;
-      const bool eq = valid && key == kth;
-      const uint64_t beq = __ballot(eq);
-      const int eq_pre = __popcll(beq & lt);
-      const bool take = gt || (eq && base_eq + eq_pre < need_eq);
-      const uint64_t bt = __ballot(take);
-      if (take) {
-        const int pos = base_sel + __popcll(bt & lt);
-        oidx[pos] = i;
-        if (osc) osc[pos] = s;
-      }
-      base_eq += __popcll(beq);
-      base_sel += __popcll(bt);
-    }
-  }
-  for (int p = n + lane; p < k; p += 64) {
-    oidx[p] = -1;
-    if (osc) osc[p] = 0.0f;
-  }
-  if (lane == 0) *ocnt = n;
-  (void)sh;
 }
 
 // CAPC == 0: every score of a query stays in LDS (CAP of them) and one register top-k
