@@ -802,7 +802,9 @@ __global__ __launch_bounds__(256) void local_prep_kernel(LocalPrepArgs a) {
 }
 
 // Decode front: the independent first steps of a decode step in one launch, so that
-// they overlap instead of paying a launch and a memory round trip each.  Row b of the
+// they overlap instead of paying a launch and a memory round trip each (steps whose top-k
+// is the threshold filter run them inside the scan and the final top-k launch instead,
+// see decode_front_args).  Row b of the
 // grid: block v < n_comp runs compressor group v of the main instance in wave 0 and of
 // the index instance in wave 1 (first, as they have the longest dependency chain);
 // blocks n_comp .. prepare the window rows (kFrontRows per block) and insert the new

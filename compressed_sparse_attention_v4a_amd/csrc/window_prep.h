@@ -1,5 +1,5 @@
-// Window-row preparation shared by the attention prep kernel and the fused decode front
-// kernel: each local (window) row is RMS-normalised with the key weights and rotated at
+// Window-row preparation shared by the attention prep kernel, the decode front kernel and
+// the front workgroups of the decode step's final top-k launch: each local (window) row is RMS-normalised with the key weights and rotated at
 // its own position once ("CSA And HCA: Definition, State, And Cost Model", section 5.2),
 // then stored as bf16 in the attention workspace, so the attention kernels gather every
 // candidate as a plain row.  Decode also inserts the new token's row into the ring.

@@ -266,9 +266,12 @@ V4A_API int v4a_hca_attn(const void* q, const void* kv_comp, const void* kv_loca
  *                         batch, n_h, c, k, w, E_cap, num_splits, out, attn_dt)
  * (bit for bit), with the same arguments, layouts and errors; workspaces are
  * replaced by one.  Where the shapes allow (bf16 tails and attention rows of 512
- * channels, heads in groups of 64), the two tail compressions and the window-row
- * preparation run as one launch.  When (t+1) % m != 0 no entry is emitted and
- * the compressor inputs are not read.
+ * channels, heads in groups of 64), the step needs fewer launches: the two tail
+ * compressions and the window-row preparation run as one launch ahead of the index
+ * scan, or, when the top-k takes its threshold filter (one query over E >= 32 k
+ * entries), the index scan emits the new index entry itself and the main entry,
+ * window rows and ring insert run inside the final top-k launch.  When
+ * (t+1) % m != 0 no entry is emitted and the compressor inputs are not read.
  *   d        : host pointer to the description below (read during the call only).
  *   ws       : device workspace of v4a_csa_decode_step_workspace(d) bytes,
  *              256-byte aligned.
