@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "cb173e9406eb35385c426e1bfe45cb3d6f51cdd6147c66a4119f50f11d33a65d",
-           "fetch_bytes": 857244333, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "565fabe4596555ca1ea93d50e244dfb6a392e4fd1d69407b89fa07d4de14b89f",
+           "fetch_bytes": 857273100, "write_bytes": 536870912}
 
 
 def parse():
