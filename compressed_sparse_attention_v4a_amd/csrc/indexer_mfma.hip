@@ -275,21 +275,23 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
   const char* kb = reinterpret_cast<const char*>(a.KI) + (int64_t)b * a.E_cap * kRowB;
 
   // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them.  The loads
-  // are written out (M0 = LDS destination, per-lane 64-bit source address) so that the
-  // compiler does not wait for them before every later LDS read; the loop waits for them
-  // explicitly before the barrier that publishes the tile.
-  auto fill = [&](char* buf, int64_t s0) {
+  // are written out (M0 = LDS destination, a 32-bit per-lane offset from the sequence's
+  // key base in scalar registers) so that the compiler does not wait for them before
+  // every later LDS read; the loop waits for them explicitly before the barrier that
+  // publishes the tile.  The offsets stay below 2^31: the launcher takes this kernel only
+  // for fewer than 2^23 visible entries.
+  const int ewg = (int)Ewg;
+  auto fill = [&](char* buf, int s0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ins = 4 * wv + r;          // entries 4 ins .. 4 ins + 3
       const int e = 4 * ins + (lane >> 4);
-      int64_t se = s0 + e;
-      if (se >= Ewg) se = Ewg - 1;         // padding rows: any visible entry (masked later)
+      const int se = min(s0 + e, ewg - 1);  // padding rows: any visible entry (masked later)
       const int ch = (lane & 15) ^ (e & 15);  // chunk position ^ entry within its 16-entry tile
-      const char* src = kb + se * kRowB + ch * 16;
+      const uint32_t voff = ((uint32_t)se << 8) | ((uint32_t)ch << 4);
       const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void)(buf + ins * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :: "s"(m0), "v"(src) : "memory");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(m0), "v"(voff), "s"(kb) : "memory");
     }
   };
   const int nchunks = (int)((Ewg + kNE - 1) / kNE);
@@ -328,27 +330,50 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
   bool have_tau = false;    // ... once the buffer has been cut at least once
 
   // The ReLU-weighted head sum of each 16-entry tile runs on the vector unit while the
-  // matrix unit multiplies the next tile (three vector instructions per MFMA), so the
-  // accumulators of one tile wait in Sp; the first tile's predecessor is a dummy with no
-  // entry to store.
+  // matrix unit multiplies the next tile, so the accumulators of one tile wait in Sp (the
+  // first tile's predecessor is a dummy).  A tile's in-lane part is 16 ReLU, 16 FMA and 3
+  // adds; the four 16-lane rows are then combined for two tiles at once (one row swap
+  // exchanges the halves of both: the first tile of the pair ends in lanes 0..31, the
+  // second in lanes 32..63), and the pair's 32 scores are stored or compacted by one set
+  // of instructions.  At 64 vector instructions per tile the vector unit would take as
+  // long as the tile's 16 MFMAs.
   f32x4 Sp[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) Sp[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  int64_t sp = -1;  // entry of this lane's previous tile (-1: none)
-  auto reduce_prev = [&]() {
-    const float acc = relu_weighted_sum(Sp, wgt);
+  float acc_a = 0.0f;  // in-lane head sum of the first tile of the pending pair
+  // this lane's entry within a pair: lanes 0..15 the first tile, 32..47 the second
+  // (lanes 16..31 and 48..63 hold copies and never store)
+  const int eoff = jj + 16 * (lane >> 5);
+  const uint32_t elim = (lane & 16) ? 0u : (uint32_t)Eq;
+  auto inlane = [&]() -> float {
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[i] = fmaf(wgt[mt][i], __int_as_float(max(__float_as_int(Sp[mt][i]), 0)), p[i]);
+    return (p[0] + p[1]) + (p[2] + p[3]);
+  };
+  // the pair whose first entry is e0 (negative for the dummy pair before entry 0, which
+  // the unsigned comparison with elim rejects)
+  auto flush_pair = [&](float acc_b, int e0) {
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc_a), __float_as_uint(acc_b), false, false);
+    const float t = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);  // rows r and r ^ 2
+    const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    const float u = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);  // rows r and r ^ 1
+    const uint32_t e = (uint32_t)(e0 + eoff);
     if constexpr (CAPC == 0) {
-      if (g == 0 && sp >= 0 && sp < Eq) scw[sp] = acc;
+      if (e < elim) scw[e] = u;
     } else {
-      // lanes 0..15 hold the 16 entries of the tile in ascending order: ballot compaction
-      const uint32_t key = score_key(acc);
-      const bool pass = g == 0 && sp >= 0 && sp < Eq && (!have_tau || key > tau);
+      // the pair's entries lie in ascending order over the ballot's lanes: compaction
+      const uint32_t key = score_key(u);
+      const bool pass = e < elim && (!have_tau || key > tau);
       const uint64_t bm = __ballot(pass);
       if (pass) {
         const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
         ckw[pos] = key;
-        ciw[pos] = (int32_t)sp;
+        ciw[pos] = (int32_t)e;
       }
       ncand += __popcll(bm);
     }
@@ -372,7 +397,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     const char* buf = kbuf + cur;
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (c + 1 < nchunks) fill(kbuf + (kNE * kRowB - cur), (int64_t)(c + 1) * kNE);
+    if (c + 1 < nchunks) fill(kbuf + (kNE * kRowB - cur), (c + 1) * kNE);
     __builtin_amdgcn_sched_barrier(0);
     // K fragments of entry tile et + 1 are read while tile et is multiplied; the four head
     // tiles are independent accumulation chains, interleaved k-step by k-step
@@ -398,19 +423,29 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
         for (int mt = 0; mt < 4; ++mt)
           S[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], kv[et & 1][ks], S[mt], 0, 0, 0);
       }
-      reduce_prev();
+      // tile 4 c + et - 1 waits in Sp: the first of a pair (et odd) keeps its in-lane
+      // sum, the second (et even) completes the pair
+      if (et & 1) {
+        acc_a = inlane();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector ALU instructions
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector ALU instructions
+        }
+      } else {
+        flush_pair(inlane(), kNE * c + 16 * et - 32);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector ALU instructions
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) Sp[mt] = S[mt];
-      sp = (int64_t)c * kNE + 16 * et + jj;
     }
   }
-  reduce_prev();  // the last tile
+  flush_pair(inlane(), kNE * nchunks - 32);  // the last pair (a chunk holds two)
 
   // per-query top-k by its own wave (no workgroup barrier needed from here on)
   if (qvalid) {
@@ -648,9 +683,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void i
 
 // The fused prefill kernel covers bf16 keys of 128 channels and 64 heads: with all
 // scores in LDS up to 4096 visible entries per query, with the streaming candidate
-// buffer beyond that (k <= 1024; multi-query chunks, T > 1).
+// buffer beyond that (k <= 1024; multi-query chunks, T > 1), for fewer than 2^23 visible
+// entries (32-bit key offsets).
 bool indexer_fused_supported(int64_t Emax, int T, int n_hI, int cI, int k, int dt) {
-  if (dt != kBF16 || cI != kCI || n_hI != kHeads) return false;
+  if (dt != kBF16 || cI != kCI || n_hI != kHeads || Emax >= ((int64_t)1 << 23)) return false;
   return Emax <= 4096 || (T > 1 && k <= 1024);
 }
 
