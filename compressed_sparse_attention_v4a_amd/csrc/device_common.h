@@ -81,8 +81,10 @@ __device__ __forceinline__ uint32_t f32_to_e2m1_abs(float a) {
 // Order-preserving map of a float score to uint32 (larger score -> larger key).
 // -0 is folded into +0 so that equal values compare equal.
 __device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; otherwise the sign bit set (an arithmetic shift of the
+  // sign gives the mask in two instructions, without a compare and select)
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);

@@ -331,8 +331,8 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
 
   // The ReLU-weighted head sum of each 16-entry tile runs on the vector unit while the
   // matrix unit multiplies the next tile, so the accumulators of one tile wait in Sp (the
-  // first tile's predecessor is a dummy).  A tile's in-lane part is 16 ReLU, 16 FMA and 3
-  // adds; the four 16-lane rows are then combined for two tiles at once (one row swap
+  // first tile's predecessor is a dummy).  A tile's in-lane part is 16 ReLU, 16 FMA and 1
+  // add; the four 16-lane rows are then combined for two tiles at once (one row swap
   // exchanges the halves of both: the first tile of the pair ends in lanes 0..31, the
   // second in lanes 32..63), and the pair's 32 scores are stored or compacted by one set
   // of instructions.  At 64 vector instructions per tile the vector unit would take as
@@ -346,13 +346,13 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
   const int eoff = jj + 16 * (lane >> 5);
   const uint32_t elim = (lane & 16) ? 0u : (uint32_t)Eq;
   auto inlane = [&]() -> float {
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float p[2] = {0.0f, 0.0f};  // two chains of 8: one add to combine
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        p[i] = fmaf(wgt[mt][i], __int_as_float(max(__float_as_int(Sp[mt][i]), 0)), p[i]);
-    return (p[0] + p[1]) + (p[2] + p[3]);
+        p[i & 1] = fmaf(wgt[mt][i], __int_as_float(max(__float_as_int(Sp[mt][i]), 0)), p[i & 1]);
+    return p[0] + p[1];
   };
   // the pair whose first entry is e0 (negative for the dummy pair before entry 0, which
   // the unsigned comparison with elim rejects)
