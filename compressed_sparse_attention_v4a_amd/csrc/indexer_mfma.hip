@@ -274,28 +274,55 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
   const int64_t Eq = qvalid ? (a.t0 + j + 1) / a.m : 0;
   const char* kb = reinterpret_cast<const char*>(a.KI) + (int64_t)b * a.E_cap * kRowB;
 
-  // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them.  The loads
-  // are written out (M0 = LDS destination, a 32-bit per-lane offset from the sequence's
-  // key base in scalar registers) so that the compiler does not wait for them before
-  // every later LDS read; the loop waits for them explicitly before the barrier that
-  // publishes the tile.  The offsets stay below 2^31: the launcher takes this kernel only
-  // for fewer than 2^23 visible entries.
+  // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them (entries
+  // 4 (4 wv + r) .. + 3).  The loads are written out (M0 = LDS destination, formed from this
+  // wave's part of the tile buffers plus an immediate; a 32-bit per-lane offset from the
+  // sequence's key base in scalar registers) so that the compiler does not wait for them
+  // before every later LDS read; the loop waits for them explicitly before the barrier
+  // that publishes the tile.  The offsets stay below 2^31: the launcher takes this kernel
+  // only for fewer than 2^23 visible entries.  Lanes of a load hold chunk position
+  // (lane & 15) ^ (entry & 15) of entry 4 (4 wv + r) + (lane >> 4).
   const int ewg = (int)Ewg;
-  auto fill = [&](char* buf, int s0) {
+  const uint32_t lds_wave = (uint32_t)(uintptr_t)(lds_void)kbuf + (uint32_t)wv * 4096u;
+  uint32_t lofs[4];  // per-lane offset of load r from the tile's first entry
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ins = 4 * wv + r;          // entries 4 ins .. 4 ins + 3
-      const int e = 4 * ins + (lane >> 4);
-      const int se = min(s0 + e, ewg - 1);  // padding rows: any visible entry (masked later)
-      const int ch = (lane & 15) ^ (e & 15);  // chunk position ^ entry within its 16-entry tile
-      const uint32_t voff = ((uint32_t)se << 8) | ((uint32_t)ch << 4);
-      const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void)(buf + ins * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(m0), "v"(voff), "s"(kb) : "memory");
+  for (int r = 0; r < 4; ++r) {
+    const int e = 16 * wv + 4 * r + (lane >> 4);
+    lofs[r] = ((uint32_t)e << 8) | ((uint32_t)((lane & 15) ^ (e & 15)) << 4);
+  }
+  // load r of this wave into buffer NB (M0 = its LDS address), from byte voff of the keys
+  auto load = [lw = lds_wave, kp = kb](auto nb_t, auto r_t, uint32_t voff) {
+    constexpr int OFF = decltype(nb_t)::value * kNE * kRowB + decltype(r_t)::value * 1024;
+    asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
+                 :: "s"(lw), "i"(OFF), "v"(voff), "s"(kp) : "memory");
+  };
+  auto fill = [&](auto nb_t, int s0) {
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
+    using R2 = std::integral_constant<int, 2>;
+    using R3 = std::integral_constant<int, 3>;
+    if (s0 + kNE <= ewg) {
+      const uint32_t sb = (uint32_t)s0 << 8;
+      load(nb_t, R0{}, sb + lofs[0]);
+      load(nb_t, R1{}, sb + lofs[1]);
+      load(nb_t, R2{}, sb + lofs[2]);
+      load(nb_t, R3{}, sb + lofs[3]);
+    } else {
+      // the last tile: rows past the visible entries load entry ewg - 1 (masked later)
+      uint32_t v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int se = min(s0 + 16 * wv + 4 * r + (lane >> 4), ewg - 1);
+        v[r] = ((uint32_t)se << 8) | (lofs[r] & 0xF0u);
+      }
+      load(nb_t, R0{}, v[0]);
+      load(nb_t, R1{}, v[1]);
+      load(nb_t, R2{}, v[2]);
+      load(nb_t, R3{}, v[3]);
     }
   };
   const int nchunks = (int)((Ewg + kNE - 1) / kNE);
-  if (nchunks > 0) fill(kbuf, 0);
+  if (nchunks > 0) fill(std::integral_constant<int, 0>{}, 0);
 
   // resident query rows (A operand, heads as rows) and head weights
   bf16x8 qa[4][4];  // [mt][ks]
@@ -378,8 +405,8 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
       ncand += __popcll(bm);
     }
   };
-  // cut the buffer back to the k best when the next chunk (at most kNE entries) could
-  // overflow it
+  // cut the buffer back to the k best (the loop cuts whenever the next two chunks could
+  // overflow it)
   auto cut = [&]() {
     if constexpr (CAPC > 0) {
       if (ncand > a.k) {
@@ -389,15 +416,14 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
       }
     }
   };
-  for (int c = 0; c < nchunks; ++c) {
-    if constexpr (CAPC > 0) {
-      if (ncand > CAPC - kNE) cut();
-    }
-    const int cur = (c & 1) * (kNE * kRowB);
-    const char* buf = kbuf + cur;
+  // chunk c lives in buffer c & 1; BUF is a compile-time copy of it, so that buffer
+  // offsets are immediates of the LDS instructions
+  auto chunk = [&](int c, auto buf_t) {
+    constexpr int BUF = decltype(buf_t)::value;
+    const char* buf = kbuf + BUF * (kNE * kRowB);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (c + 1 < nchunks) fill(kbuf + (kNE * kRowB - cur), (c + 1) * kNE);
+    if (c + 1 < nchunks) fill(std::integral_constant<int, 1 - BUF>{}, (c + 1) * kNE);
     __builtin_amdgcn_sched_barrier(0);
     // K fragments of entry tile et + 1 are read while tile et is multiplied; the four head
     // tiles are independent accumulation chains, interleaved k-step by k-step
@@ -444,6 +470,14 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) Sp[mt] = S[mt];
     }
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    // the next two chunks (at most 2 kNE entries) must fit in the candidate buffer
+    if constexpr (CAPC > 0) {
+      if (ncand > CAPC - 2 * kNE) cut();
+    }
+    chunk(c, std::integral_constant<int, 0>{});
+    if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>{});
   }
   flush_pair(inlane(), kNE * nchunks - 32);  // the last pair (a chunk holds two)
 
