@@ -25,6 +25,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) void* lds_void;
 
 constexpr int kCI = 128;             // indexer key width
@@ -32,6 +33,7 @@ constexpr int kRowB = kCI * 2;       // 256 bytes per bf16 key
 constexpr int kNE = 64;              // entries per K tile
 constexpr int kQ = 4;                // queries per workgroup (one per wave)
 constexpr int kHeads = 64;
+constexpr int kCutSlack = 64;        // extra candidates a cut inside the stream may keep
 
 // 16-byte chunk (of 16 per key) read by lane group g in k-step s (s < 4); the step
 // index sits above the swizzle bits so per-step addresses are immediates.
@@ -61,19 +63,20 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x4 (&S)[4], const fl
 }
 
 // Radix select of the k-th largest of the keys held in registers by one wave: lane l
-// holds the contiguous keys [l per, l per + per) of E (slots past per or E hold key 0,
-// "absent", below every real key except the one NaN pattern whose key is 0).  Passes over
-// digits shared by every key (wave AND / OR) are skipped; the others count runs of equal
-// digits before touching the histogram (the wave's own, ordered by the wave's in-order LDS
-// operations) and find the bin with a DPP prefix sum.  The passes stop once the k-th key's
-// bin holds exactly the keys still needed.  On return the selection is: keys whose
-// resolved digits (key & pmask) exceed kth, then the first need_eq keys equal to it in
-// position order.  Needs E > k.
+// holds the contiguous keys [l per, l per + per) of E (per <= PER; slots past per or E
+// hold key 0, "absent", below every real key except the one NaN pattern whose key is 0).
+// Passes over digits shared by every key (wave AND / OR) are skipped; the others count
+// runs of equal digits before touching the histogram (the wave's own, ordered by the
+// wave's in-order LDS operations) and find the bin with a DPP prefix sum.  The passes stop
+// once the k-th key's bin holds at most slack keys more than are still needed; the whole
+// bin is then taken.  On return the selection is: keys whose resolved digits
+// (key & pmask) exceed kth, then the first need_eq keys equal to it in position order;
+// kept = its size (k when slack = 0, at most k + slack otherwise).  Needs E > k.
 template <int PER>
-__device__ __forceinline__ void radix_kth(const uint32_t (&key)[PER], int E, int k, uint32_t* hist,
-                                          uint32_t& kth, uint32_t& pmask_out, int& need_eq) {
+__device__ __forceinline__ void radix_kth(const uint32_t (&key)[PER], int E, int per, int k,
+                                          int slack, uint32_t* hist, uint32_t& kth,
+                                          uint32_t& pmask_out, int& need_eq, int& kept) {
   const int lane = threadIdx.x & 63;
-  const int per = (E + 63) / 64;
   const int base = lane * per;
   uint32_t kand = 0xFFFFFFFFu, kor = 0u;
 #pragma unroll
@@ -87,7 +90,7 @@ __device__ __forceinline__ void radix_kth(const uint32_t (&key)[PER], int E, int
   const uint32_t n_absent = 64u * PER - (uint32_t)E;
   for (int i = lane; i < 256; i += 64) hist[i] = 0u;
   uint32_t prefix = 0, pmask = 0;
-  int rem = k;
+  int rem = k, take = -1;  // take >= 0: the whole bin of the k-th key is selected
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (common >= 32 - shift) {
       prefix |= kand & (255u << shift);
@@ -131,26 +134,30 @@ __device__ __forceinline__ void radix_kth(const uint32_t (&key)[PER], int E, int
     prefix |= (uint32_t)__builtin_amdgcn_readlane(hit_bin, src) << shift;
     pmask |= 255u << shift;
     rem -= __builtin_amdgcn_readlane((int)hit_above, src);
-    const bool whole = (uint32_t)__builtin_amdgcn_readlane((int)hit_count, src) == (uint32_t)rem;
+    const int hc = __builtin_amdgcn_readlane((int)hit_count, src);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < 4; ++j) hist[255 - 4 * lane - j] = 0u;  // the bins this lane read
-    // the bin holds exactly the keys still needed: all of them are selected, whatever
-    // their lower digits (the same set the remaining passes would find)
-    if (whole) break;
+    // the bin holds the keys still needed and at most slack more: all of them are
+    // selected, whatever their lower digits (with slack = 0, the same set the remaining
+    // passes would find)
+    if (hc <= rem + slack) {
+      take = hc;
+      break;
+    }
   }
   kth = prefix;
   pmask_out = pmask;
-  need_eq = rem;
+  need_eq = take >= 0 ? take : rem;
+  kept = k - rem + need_eq;
 }
 
 // Output slot of each selected key of a lane (position order, ties to the lower
 // position): calls emit(j, slot) for every selected register j.
 template <int PER, typename F>
-__device__ __forceinline__ void radix_emit(const uint32_t (&key)[PER], int E, uint32_t kth,
+__device__ __forceinline__ void radix_emit(const uint32_t (&key)[PER], int E, int per, uint32_t kth,
                                            uint32_t pmask, int need_eq, F&& emit) {
   const int lane = threadIdx.x & 63;
-  const int per = (E + 63) / 64;
   const int base = lane * per;
   int ngt = 0, neq = 0;
 #pragma unroll
@@ -198,8 +205,9 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
     for (int j = 0; j < PER; ++j) key[j] = (j < per && base + j < E) ? score_key(sc[base + j]) : 0u;
     uint32_t kth, pmask;
     int need_eq;
-    radix_kth<PER>(key, E, k, hist, kth, pmask, need_eq);
-    radix_emit<PER>(key, E, kth, pmask, need_eq, [&](int j, int pos) {
+    int kept;
+    radix_kth<PER>(key, E, per, k, 0, hist, kth, pmask, need_eq, kept);
+    radix_emit<PER>(key, E, per, kth, pmask, need_eq, [&](int j, int pos) {
       oidx[pos] = base + j;
       if (osc) osc[pos] = key_score(key[j]);
     });
@@ -212,30 +220,39 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
 }
 
 // Candidate buffer of one wave for long key lists: the n > k (key, entry) pairs in
-// ckey/cidx[0..n), in ascending entry order, are cut to the k best (larger key first,
-// ties to the lower entry), kept in ascending entry order in [0, k).  Returns the
-// smallest key kept: a later entry (higher index) can only displace a kept one with a
-// strictly larger key.  One wave; n <= 64 PER.
+// ckey/cidx[0..n), in ascending entry order, are cut to the best ones (larger key first,
+// ties to the lower entry), kept in ascending entry order in [0, kept).  slack = 0: the k
+// best (kept = k).  slack > 0: the k best and at most slack more keys of the k-th key's
+// radix bin (the passes stop once that bin is small enough).  Returns the smallest key
+// kept: a later entry (higher index) whose key does not exceed it finds at least k kept
+// keys as large with lower indices, so it can never be selected.  One wave; n <= 64 PER;
+// ckey and cidx 16-byte aligned.
 template <int PER>
-__device__ uint32_t wave_shrink_pairs(uint32_t* ckey, int32_t* cidx, int n, int k, uint32_t* hist) {
+__device__ uint32_t wave_shrink_pairs(uint32_t* ckey, int32_t* cidx, int n, int k, int slack,
+                                      uint32_t* hist, int& kept) {
+  static_assert(PER % 4 == 0, "pairs are read four at a time");
   const int lane = threadIdx.x & 63;
-  const int per = (n + 63) / 64;
-  const int base = lane * per;
+  const int base = lane * PER;  // lane l holds pairs [l PER, l PER + PER): 16-byte reads
   uint32_t key[PER];
   int32_t ent[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool v = j < per && base + j < n;
-    key[j] = v ? ckey[base + j] : 0u;
-    ent[j] = v ? cidx[base + j] : 0;
+  for (int j = 0; j < PER; j += 4) {
+    const u32x4 k4 = *reinterpret_cast<const u32x4*>(ckey + base + j);
+    const u32x4 e4 = *reinterpret_cast<const u32x4*>(cidx + base + j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool v = base + j + i < n;
+      key[j + i] = v ? k4[i] : 0u;
+      ent[j + i] = (int32_t)e4[i];
+    }
   }
   uint32_t kth, pmask;
   int need_eq;
-  radix_kth<PER>(key, n, k, hist, kth, pmask, need_eq);
+  radix_kth<PER>(key, n, PER, k, slack, hist, kth, pmask, need_eq, kept);
   uint32_t kmin = 0xFFFFFFFFu;
   // every lane has loaded its pairs before any slot is rewritten (slot <= position)
   __builtin_amdgcn_wave_barrier();
-  radix_emit<PER>(key, n, kth, pmask, need_eq, [&](int j, int pos) {
+  radix_emit<PER>(key, n, PER, kth, pmask, need_eq, [&](int j, int pos) {
     ckey[pos] = key[j];
     cidx[pos] = ent[j];
     kmin = min(kmin, key[j]);
@@ -257,8 +274,8 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     IndexerArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * kNE * kRowB];
   __shared__ float sc[kQ][CAPC > 0 ? 1 : CAP];
-  __shared__ uint32_t ckey[kQ][CAPC > 0 ? CAPC : 1];
-  __shared__ int32_t cidx[kQ][CAPC > 0 ? CAPC : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t ckey[kQ][CAPC > 0 ? CAPC : 1];
+  __shared__ __attribute__((aligned(16))) int32_t cidx[kQ][CAPC > 0 ? CAPC : 1];
   __shared__ uint32_t hist[kQ][256];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -405,14 +422,16 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
       ncand += __popcll(bm);
     }
   };
-  // cut the buffer back to the k best (the loop cuts whenever the next two chunks could
-  // overflow it)
-  auto cut = [&]() {
+  // cut the buffer back to its best entries: inside the loop (whenever the next two
+  // chunks could overflow it) to the k best and at most kCutSlack more, which stops the
+  // radix passes early; after the loop to exactly the k best
+  auto cut = [&](int slack) {
     if constexpr (CAPC > 0) {
       if (ncand > a.k) {
-        tau = wave_shrink_pairs<CAPC / 64>(ckw, ciw, ncand, a.k, hist[wv]);
+        int kept;
+        tau = wave_shrink_pairs<CAPC / 64>(ckw, ciw, ncand, a.k, slack, hist[wv], kept);
         have_tau = true;
-        ncand = a.k;
+        ncand = kept;
       }
     }
   };
@@ -474,7 +493,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
   for (int c = 0; c < nchunks; c += 2) {
     // the next two chunks (at most 2 kNE entries) must fit in the candidate buffer
     if constexpr (CAPC > 0) {
-      if (ncand > CAPC - 2 * kNE) cut();
+      if (ncand > CAPC - 2 * kNE) cut(kCutSlack);
     }
     chunk(c, std::integral_constant<int, 0>{});
     if (c + 1 < nchunks) chunk(c + 1, std::integral_constant<int, 1>{});
@@ -488,7 +507,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
       wave_topk_reg<CAP / 64>(scw, (int)Eq, a.k, hist[wv], a.topk_idx + q * a.k,
                               a.topk_score ? a.topk_score + q * a.k : nullptr, a.topk_cnt + q);
     } else {
-      cut();
+      cut(0);
       // ncand = min(k, Eq): every entry entered before the first cut, k stay after it
       int32_t* oi = a.topk_idx + q * a.k;
       float* os = a.topk_score ? a.topk_score + q * a.k : nullptr;
