@@ -826,6 +826,8 @@ def test_decode_step_bitwise_reproducible():
     ("equal", 40000, 8, 512),        # every score equal: the first k entries, every cut a tie
     ("rising", 40000, 8, 512),       # every entry beats the buffer: a cut every few chunks
     ("falling", 40000, 8, 512),      # after the first cut nothing enters
+    ("integer", 60000, 24, 512),     # exact integer scores with many ties: the whole selection
+    ("integer", 131008, 12, 1024),   # the same with the larger buffer at E = 32752 .. 32755
 ])
 def test_indexer_stream_bf16(case, t0, T, k):
     """Prefill chunks whose queries see more than 4096 entries: each wave streams its
@@ -838,6 +840,11 @@ def test_indexer_stream_bf16(case, t0, T, k):
     if case == "random":
         qI = rng.standard_normal((T, n_hI, cI))
         KI = rng.standard_normal((E + 3, cI))
+    elif case == "integer":
+        # integers in [-2, 2] and weights in quarters: every product and sum on both sides is
+        # exact, so the GPU and oracle scores are equal and ties are frequent
+        qI = rng.integers(-2, 3, (T, n_hI, cI)).astype(np.float64)
+        KI = rng.integers(-2, 3, (E + 3, cI)).astype(np.float64)
     else:
         u = np.abs(rng.standard_normal(cI)) + 0.5
         qI = np.broadcast_to(u, (T, n_hI, cI)).copy()
@@ -848,6 +855,8 @@ def test_indexer_stream_bf16(case, t0, T, k):
     qI = synth.formats.bf16_bits(qI)
     KI = synth.formats.bf16_bits(KI)
     wI = rng.random((T, n_hI)).astype(np.float32)
+    if case == "integer":
+        wI = (rng.integers(0, 5, (T, n_hI)) / 4).astype(np.float32)
     log(f"indexer stream bf16 {case} t0={t0} T={T} k={k} E={E}")
     idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
     torch.cuda.synchronize()
@@ -862,8 +871,9 @@ def test_indexer_stream_bf16(case, t0, T, k):
         check_topk(got_i, cnt[0, r:r + 1].cpu().numpy(), ref, t0=t0 + int(r), m=m, k=k,
                    gpu_scores=sc[0, r:r + 1].cpu().numpy(), what=f"{case} row {r}")
         if case != "random":
-            # identical bf16 rows give identical scores on both sides, so ties are exact
-            # and the lower entry must win them: the oracle's selection, bit for bit
+            # identical bf16 rows (or exact integer arithmetic) give identical scores on both
+            # sides, so ties are exact and the lower entry must win them: the oracle's
+            # selection, bit for bit
             ref_i, _ = oracle.topk(ref, t0=t0 + int(r), m=m, k=k)
             assert np.array_equal(got_i[0], ref_i[0]), f"{case} row {r}: selection differs"
         if case in ("equal", "falling"):
