@@ -344,9 +344,12 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   };
 
   // ---- per-lane LDS byte offsets (everything step-dependent is an immediate) --
-  // score reads: row 32 cc + l32, channels 256 kx + 16 s + 8 hl .. + 7, i.e. chunk
-  // 32 kx + 16 (s >> 3) + (2 (s & 7) + hl), swizzled within its 256-byte group
-  const int srow = 32 * cc + l32;
+  // score reads: row 32 cc + (l32 ^ 16 kx), channels 256 kx + 16 s + 8 hl .. + 7, i.e.
+  // chunk 32 kx + 16 (s >> 3) + (2 (s & 7) + hl), swizzled within its 256-byte group.
+  // The channel-half kx = 1 reads the two 16-row halves of its tile swapped, so that in
+  // both halves the rows the wave keeps after the trade (16 kx .. 16 kx + 15 of the tile)
+  // land in the first eight accumulator elements.
+  const int srow = 32 * cc + (l32 ^ (16 * kx));
   int sb[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) sb[u] = srow * kRowBytes + (((2 * u + hl) ^ swz(srow)) << 4) + 512 * kx;
@@ -549,16 +552,13 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         // trade halves with the other channel half of the tile (wave wv ^ 1): send the
-        // elements it owns, keep elements 8 kx .. 8 kx + 7
-        // (bit selects with a wave-uniform mask: a conditional on kx becomes indexed
-        // register moves)
+        // elements it owns (elements 8 .. 15, its rows 16 (1 - kx) .. + 15), keep elements
+        // 0 .. 7 (rows 16 kx .. 16 kx + 15, by the swapped score reads)
         float own[8], snd[8];
-        const uint32_t km = 0u - (uint32_t)kx;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint32_t lo = __float_as_uint(S[i]), hi = __float_as_uint(S[8 + i]);
-          own[i] = __uint_as_float((hi & km) | (lo & ~km));
-          snd[i] = __uint_as_float((lo & km) | (hi & ~km));
+          own[i] = S[i];
+          snd[i] = S[8 + i];
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
