@@ -301,24 +301,26 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   // of the sequence's own window
   const int64_t kv_bstride = a.pages ? 0 : a.E_cap;  // a pool has no per-sequence stride
   const int64_t kv_rows = a.pages ? ((int64_t)1 << 31) - 1 : a.E_cap;
+  // Per-lane arithmetic in 32 bits (list positions, entries and window rows are below
+  // 2^31); the per-item terms are wave-uniform.
   auto row_addr = [&](const Item& it, int64_t r0, int raw) -> uint64_t {
     const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)it.b * kv_bstride * kC);
     const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)it.b * a.n_lrows * kC);
     const int64_t wbase = decode ? it.lo : a.lrow_base;
     int myid = -1 - (int)(it.t - wbase);  // past the list end: the query's own window row
-    const int64_t rr = r0 + kRowsPerWave * wv + (lane & 7);
-    if (rr < it.nrows) {
-      const int64_t u = it.ub + rr;
-      if (u < it.ncomp) {
+    const int rr = (int)r0 + kRowsPerWave * wv + (lane & 7);
+    if (rr < (int)it.nrows) {
+      const int u = (int)it.ub + rr;
+      const int ncomp = (int)it.ncomp;
+      if (u < ncomp) {
         if constexpr (dense) {
-          myid = a.pages ? (int)(((int64_t)raw << a.page_shift) | (u & (((int64_t)1 << a.page_shift) - 1)))
-                         : (int)u;
+          myid = a.pages ? ((raw << a.page_shift) | (u & ((1 << a.page_shift) - 1))) : u;
         } else {
           // out-of-range indices must not fault
-          myid = (int)min(max((int64_t)raw, (int64_t)0), kv_rows - 1);
+          myid = min(max(raw, 0), (int)(kv_rows - 1));
         }
       } else {
-        myid = -1 - (int)(it.lo + (u - it.ncomp) - wbase);
+        myid = -1 - ((int)(it.lo - wbase) + (u - ncomp));
       }
     }
     return myid >= 0 ? (uint64_t)kvc_b + (uint64_t)myid * kRowBytes
@@ -326,16 +328,18 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
   };
   // row 8 wv + r of a chunk into chunk buffer dst; lane i carries chunk i of the global
   // row into LDS chunk i ^ swz(8 wv + r)
+  const uint32_t lane16 = (uint32_t)lane << 4;
   auto gather_row = [&](uint64_t addr, char* dst, int r) {
     // readlane returns int: go through uint32_t so the low half is not sign-extended
     const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(addr >> 32), r) << 32) |
                         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)addr, r);
-    // the lane offset is formed at each use from an opaque copy: hoisted, the eight
-    // per-row offsets would hold eight registers across the loop
-    uint32_t lb = (uint32_t)lane << 4;
-    asm volatile("" : "+v"(lb));
-    dma_b128(reinterpret_cast<const char*>(ra), lb ^ ((uint32_t)swz(kRowsPerWave * wv + r) << 4),
-             dst + (kRowsPerWave * wv + r) * kRowBytes);
+    // the lane offset is formed at each use by one instruction the compiler cannot hoist
+    // (hoisted, the eight per-row offsets would hold eight registers across the loop)
+    uint32_t lo;
+    asm volatile("v_xor_b32 %0, %1, %2"
+                 : "=v"(lo)
+                 : "s"((uint32_t)swz(kRowsPerWave * wv + r) << 4), "v"(lane16));
+    dma_b128(reinterpret_cast<const char*>(ra), lo, dst + (kRowsPerWave * wv + r) * kRowBytes);
   };
   auto fill = [&](const Item& it, char* dst, int64_t r0, int raw) {
     const uint64_t addr = row_addr(it, r0, raw);
