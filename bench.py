@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "565fabe4596555ca1ea93d50e244dfb6a392e4fd1d69407b89fa07d4de14b89f",
-           "fetch_bytes": 857273100, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "220cc3c7bea292ef7a99893f2fc6280ff017db7e79c64cdb6fd0049fb3418e26",
+           "fetch_bytes": 857072153, "write_bytes": 536870912}
 
 
 def parse():
