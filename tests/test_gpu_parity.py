@@ -880,6 +880,32 @@ def test_indexer_stream_bf16(case, t0, T, k):
             assert np.array_equal(got_i[0], np.arange(k)), f"{case} row {r}: not the first k"
 
 
+@pytest.mark.parametrize("t0,T,k", [(0, 2048, 64), (8000, 200, 512)])
+def test_indexer_fused_integer_exact(t0, T, k):
+    """The fused path with every score in LDS (up to 2048 and 4096 visible entries):
+    integer operands and quarter weights make every product and sum exact on both sides,
+    so the selection, ties to the lower entry included, is the oracle's bit for bit."""
+    rng = np.random.default_rng(t0 + T + k)
+    n_hI, cI, m = 64, 128, 4
+    E = (t0 + T) // m
+    qI = synth.formats.bf16_bits(rng.integers(-2, 3, (T, n_hI, cI)).astype(np.float64))
+    KI = synth.formats.bf16_bits(rng.integers(-2, 3, (E + 5, cI)).astype(np.float64))
+    wI = (rng.integers(0, 5, (T, n_hI)) / 4).astype(np.float32)
+    log(f"indexer fused integer t0={t0} T={T} k={k} E={E}")
+    idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
+    torch.cuda.synchronize()
+    Kd = f64(KI, "bf16")
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+                                     np.random.default_rng(5).integers(0, T, 16)]))
+    for r in rows:
+        Er = (t0 + int(r) + 1) // m
+        ref = _oracle_scores(f64(qI[r:r + 1], "bf16"), Kd[:max(Er, 1)], wI[r:r + 1].astype(np.float64),
+                             t0 + int(r), m, Er)
+        ref_i, ref_c = oracle.topk(ref, t0=t0 + int(r), m=m, k=k)
+        assert int(cnt[0, r]) == int(ref_c[0]), f"row {r}: count"
+        assert np.array_equal(idx[0, r].cpu().numpy(), ref_i[0]), f"row {r}: selection differs"
+
+
 # ------------------------------------------------ 128K-context chunked CSA prefill --- #
 
 def test_csa_prefill_128k_chunked_sampled():
