@@ -220,30 +220,27 @@ __device__ void wave_topk_reg(const float* sc, int E, int k, uint32_t* hist, int
 }
 
 // Candidate buffer of one wave for long key lists: the n > k (key, entry) pairs in
-// ckey/cidx[0..n), in ascending entry order, are cut to the best ones (larger key first,
+// cp[0..n), in ascending entry order, are cut to the best ones (larger key first,
 // ties to the lower entry), kept in ascending entry order in [0, kept).  slack = 0: the k
 // best (kept = k).  slack > 0: the k best and at most slack more keys of the k-th key's
 // radix bin (the passes stop once that bin is small enough).  Returns the smallest key
 // kept: a later entry (higher index) whose key does not exceed it finds at least k kept
 // keys as large with lower indices, so it can never be selected.  One wave; n <= 64 PER;
-// ckey and cidx 16-byte aligned.
+// cp 16-byte aligned.
 template <int PER>
-__device__ uint32_t wave_shrink_pairs(uint32_t* ckey, int32_t* cidx, int n, int k, int slack,
-                                      uint32_t* hist, int& kept) {
-  static_assert(PER % 4 == 0, "pairs are read four at a time");
+__device__ uint32_t wave_shrink_pairs(uint2* cp, int n, int k, int slack, uint32_t* hist, int& kept) {
+  static_assert(PER % 2 == 0, "pairs are read two at a time");
   const int lane = threadIdx.x & 63;
   const int base = lane * PER;  // lane l holds pairs [l PER, l PER + PER): 16-byte reads
   uint32_t key[PER];
   int32_t ent[PER];
 #pragma unroll
-  for (int j = 0; j < PER; j += 4) {
-    const u32x4 k4 = *reinterpret_cast<const u32x4*>(ckey + base + j);
-    const u32x4 e4 = *reinterpret_cast<const u32x4*>(cidx + base + j);
+  for (int j = 0; j < PER; j += 2) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(cp + base + j);  // two (key, entry) pairs
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool v = base + j + i < n;
-      key[j + i] = v ? k4[i] : 0u;
-      ent[j + i] = (int32_t)e4[i];
+    for (int i = 0; i < 2; ++i) {
+      key[j + i] = base + j + i < n ? q[2 * i] : 0u;
+      ent[j + i] = (int32_t)q[2 * i + 1];
     }
   }
   uint32_t kth, pmask;
@@ -253,8 +250,7 @@ __device__ uint32_t wave_shrink_pairs(uint32_t* ckey, int32_t* cidx, int n, int 
   // every lane has loaded its pairs before any slot is rewritten (slot <= position)
   __builtin_amdgcn_wave_barrier();
   radix_emit<PER>(key, n, PER, kth, pmask, need_eq, [&](int j, int pos) {
-    ckey[pos] = key[j];
-    cidx[pos] = ent[j];
+    cp[pos] = make_uint2(key[j], (uint32_t)ent[j]);
     kmin = min(kmin, key[j]);
   });
 #pragma unroll
@@ -274,8 +270,9 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     IndexerArgs a) {
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * kNE * kRowB];
   __shared__ float sc[kQ][CAPC > 0 ? 1 : CAP];
-  __shared__ __attribute__((aligned(16))) uint32_t ckey[kQ][CAPC > 0 ? CAPC : 1];
-  __shared__ __attribute__((aligned(16))) int32_t cidx[kQ][CAPC > 0 ? CAPC : 1];
+  // candidate (key, entry) pairs, and one spare slot per lane past CAPC for the lanes
+  // that do not enter
+  __shared__ __attribute__((aligned(16))) uint2 cpair[kQ][CAPC > 0 ? CAPC + 64 : 1];
   __shared__ uint32_t hist[kQ][256];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -307,11 +304,11 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     const int e = 16 * wv + 4 * r + (lane >> 4);
     lofs[r] = ((uint32_t)e << 8) | ((uint32_t)((lane & 15) ^ (e & 15)) << 4);
   }
-  // load r of this wave into buffer NB (M0 = its LDS address), from byte voff of the keys
-  auto load = [lw = lds_wave, kp = kb](auto nb_t, auto r_t, uint32_t voff) {
+  // load r of this wave into buffer NB (M0 = its LDS address), from byte voff past base
+  auto load = [lw = lds_wave](auto nb_t, auto r_t, const char* base, uint32_t voff) {
     constexpr int OFF = decltype(nb_t)::value * kNE * kRowB + decltype(r_t)::value * 1024;
     asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
-                 :: "s"(lw), "i"(OFF), "v"(voff), "s"(kp) : "memory");
+                 :: "s"(lw), "i"(OFF), "v"(voff), "s"(base) : "memory");
   };
   auto fill = [&](auto nb_t, int s0) {
     using R0 = std::integral_constant<int, 0>;
@@ -319,11 +316,12 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     using R2 = std::integral_constant<int, 2>;
     using R3 = std::integral_constant<int, 3>;
     if (s0 + kNE <= ewg) {
-      const uint32_t sb = (uint32_t)s0 << 8;
-      load(nb_t, R0{}, sb + lofs[0]);
-      load(nb_t, R1{}, sb + lofs[1]);
-      load(nb_t, R2{}, sb + lofs[2]);
-      load(nb_t, R3{}, sb + lofs[3]);
+      // the tile's first key as the scalar base: the lane offsets stay fixed
+      const char* tb = kb + (size_t)s0 * kRowB;
+      load(nb_t, R0{}, tb, lofs[0]);
+      load(nb_t, R1{}, tb, lofs[1]);
+      load(nb_t, R2{}, tb, lofs[2]);
+      load(nb_t, R3{}, tb, lofs[3]);
     } else {
       // the last tile: rows past the visible entries load entry ewg - 1 (masked later)
       uint32_t v[4];
@@ -332,10 +330,10 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
         const int se = min(s0 + 16 * wv + 4 * r + (lane >> 4), ewg - 1);
         v[r] = ((uint32_t)se << 8) | (lofs[r] & 0xF0u);
       }
-      load(nb_t, R0{}, v[0]);
-      load(nb_t, R1{}, v[1]);
-      load(nb_t, R2{}, v[2]);
-      load(nb_t, R3{}, v[3]);
+      load(nb_t, R0{}, kb, v[0]);
+      load(nb_t, R1{}, kb, v[1]);
+      load(nb_t, R2{}, kb, v[2]);
+      load(nb_t, R3{}, kb, v[3]);
     }
   };
   const int nchunks = (int)((Ewg + kNE - 1) / kNE);
@@ -367,8 +365,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) bb[ks] = jj * kRowB + ((kchunk(ks, g) ^ jj) << 4);
   float* scw = sc[wv];
-  uint32_t* ckw = ckey[wv];
-  int32_t* ciw = cidx[wv];
+  uint2* cpw = cpair[wv];
   int ncand = 0;            // candidates in this wave's buffer (CAPC > 0)
   uint32_t tau = 0u;        // a scored entry enters when its key exceeds tau ...
   bool have_tau = false;    // ... once the buffer has been cut at least once
@@ -409,16 +406,19 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     if constexpr (CAPC == 0) {
       if (e < elim) scw[e] = u;
     } else {
-      // the pair's entries lie in ascending order over the ballot's lanes: compaction
-      const uint32_t key = score_key(u);
-      const bool pass = e < elim && (!have_tau || key > tau);
+      // the pair's entries lie in ascending order over the ballot's lanes: compaction.
+      // The order key of score_key without its fold of -0 into +0: u is never -0 (every
+      // head sum starts from +0, and an exact zero sum rounds to +0).
+      const uint32_t ub = __float_as_uint(u);
+      const uint32_t key = ub ^ ((uint32_t)((int32_t)ub >> 31) | 0x80000000u);
+      // (bitwise: both masks come from compares, with no branch between them)
+      const bool pass = (e < elim) & (!have_tau | (key > tau));
       const uint64_t bm = __ballot(pass);
-      if (pass) {
-        const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-        ckw[pos] = key;
-        ciw[pos] = (int32_t)e;
-      }
+      // every lane stores: a lane that does not enter writes its own spare slot past CAPC
+      const int pos = pass ? ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))
+                           : CAPC + lane;
+      cpw[pos] = make_uint2(key, e);
       ncand += __popcll(bm);
     }
   };
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
     if constexpr (CAPC > 0) {
       if (ncand > a.k) {
         int kept;
-        tau = wave_shrink_pairs<CAPC / 64>(ckw, ciw, ncand, a.k, slack, hist[wv], kept);
+        tau = wave_shrink_pairs<CAPC / 64>(cpw, ncand, a.k, slack, hist[wv], kept);
         have_tau = true;
         ncand = kept;
       }
@@ -513,8 +513,9 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
       float* os = a.topk_score ? a.topk_score + q * a.k : nullptr;
       for (int p = lane; p < a.k; p += 64) {
         const bool v = p < ncand;
-        oi[p] = v ? ciw[p] : -1;
-        if (os) os[p] = v ? key_score(ckw[p]) : 0.0f;
+        const uint2 pr = v ? cpw[p] : make_uint2(0u, 0u);
+        oi[p] = v ? (int32_t)pr.y : -1;
+        if (os) os[p] = v ? key_score(pr.x) : 0.0f;
       }
       if (lane == 0) a.topk_cnt[q] = ncand;
     }
