@@ -747,9 +747,12 @@ bool indexer_fused_supported(int64_t Emax, int T, int n_hI, int cI, int k, int d
 hipError_t launch_indexer_fused(const IndexerArgs& a, int64_t Emax, hipStream_t s) {
   const unsigned nblk = (unsigned)((a.T + kQ - 1) / kQ);
   const dim3 grid(nblk, (unsigned)a.batch);
+  // every score in LDS up to 2048 entries; beyond that the streaming buffer (two
+  // workgroups per CU) is faster than the 4096-score form (one), which serves only single
+  // queries and k > 1024
   if (Emax <= 2048)
     hipLaunchKernelGGL((indexer_prefill_bf16_kernel<2048, 0>), grid, dim3(256), 0, s, a);
-  else if (Emax <= 4096)
+  else if (Emax <= 4096 && (a.T == 1 || a.k > 1024))
     hipLaunchKernelGGL((indexer_prefill_bf16_kernel<4096, 0>), grid, dim3(256), 0, s, a);
   else if (a.k <= 512)
     hipLaunchKernelGGL((indexer_prefill_bf16_kernel<0, 1280>), grid, dim3(256), 0, s, a);
