@@ -880,11 +880,16 @@ def test_indexer_stream_bf16(case, t0, T, k):
             assert np.array_equal(got_i[0], np.arange(k)), f"{case} row {r}: not the first k"
 
 
-@pytest.mark.parametrize("t0,T,k", [(0, 2048, 64), (8000, 200, 512)])
+@pytest.mark.parametrize("t0,T,k", [
+    (0, 2048, 64),       # every score in LDS, up to 512 entries
+    (8000, 200, 512),    # 2000 .. 2050 entries: the 2048-score form, then the streaming buffer
+    (12000, 1, 512),     # one query over 3000 entries: the 4096-score form
+    (11990, 3, 1100),    # k > 1024 over ~3000 entries: the 4096-score form
+])
 def test_indexer_fused_integer_exact(t0, T, k):
-    """The fused path with every score in LDS (up to 2048 and 4096 visible entries):
-    integer operands and quarter weights make every product and sum exact on both sides,
-    so the selection, ties to the lower entry included, is the oracle's bit for bit."""
+    """The fused paths for up to 4096 visible entries: integer operands and quarter weights
+    make every product and sum exact on both sides, so the selection, ties to the lower
+    entry included, is the oracle's bit for bit."""
     rng = np.random.default_rng(t0 + T + k)
     n_hI, cI, m = 64, 128, 4
     E = (t0 + T) // m
@@ -895,7 +900,7 @@ def test_indexer_fused_integer_exact(t0, T, k):
     idx, cnt, sc = ops.indexer_topk(up(qI), up(KI), up(wI), dt="bf16", m=m, k=k, t0=t0)
     torch.cuda.synchronize()
     Kd = f64(KI, "bf16")
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+    rows = np.unique(np.concatenate([np.arange(min(T, 8)), np.arange(max(0, T - 8), T),
                                      np.random.default_rng(5).integers(0, T, 16)]))
     for r in rows:
         Er = (t0 + int(r) + 1) // m
