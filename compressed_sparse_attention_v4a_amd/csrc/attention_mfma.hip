@@ -581,20 +581,29 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
         }
         // candidates past the end of the list (last chunk only): element i is candidate
         // 32 cc + 16 kx + 8 (i >> 2) + 4 hl + (i & 3) of the chunk
-        if (__builtin_expect(r0 + kNC > cur.nrows, 0)) {
+        // (32-bit: list lengths are below 2^31, and the scalar unit compares 32-bit values)
+        if (__builtin_expect((int)r0 + kNC > (int)cur.nrows, 0)) {
           asm volatile("" ::: "memory");  // keep this a branch: only the last chunk is partial
           const int lim = (int)(cur.nrows - r0) - 32 * cc - 16 * kx - 4 * hl;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             if (8 * (i >> 2) + (i & 3) >= lim) sc[i] = -INFINITY;
         }
-        float lmax = sc[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, sc[i]);
+        // the maximum by three-input maxima written out: the scores are sums or -inf, never
+        // NaN, so the quieting copies the compiler adds before each fmaxf are not needed
+        float lmax;
+        asm("v_max3_f32 %0, %1, %2, %3\n\t"
+            "v_max3_f32 %0, %0, %4, %5\n\t"
+            "v_max3_f32 %0, %0, %6, %7\n\t"
+            "v_max_f32 %0, %0, %8"
+            : "=&v"(lmax)
+            : "v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]), "v"(sc[4]), "v"(sc[5]), "v"(sc[6]), "v"(sc[7]));
         {
           // the other half-wave's maximum for the same head (row swap, no LDS round trip)
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax), false, false);
-          lmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * qinv;  // qinv > 0: order kept
+          float m2;
+          asm("v_max_f32 %0, %1, %2" : "=v"(m2) : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
+          lmax = m2 * qinv;  // qinv > 0: order kept
         }
         mx_run = fmaxf(mx_run, lmax);
         if (c == 0) {
@@ -608,12 +617,11 @@ __global__ __launch_bounds__(kThreads, 1) void mqa_mfma_kernel(MqaArgs a) {
           ovf = ovf || lmax > m_ref + kLazy;
         }
         float pr[8];
-        float ls = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], qinv, -m_ref));
-          ls += pr[i];
-        }
+        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], qinv, -m_ref));
+        float ls = pr[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) ls += pr[i];
         l_part += ls;
         {
           const u32x4 pk = {pk_bf16(pr[0], pr[1]), pk_bf16(pr[2], pr[3]), pk_bf16(pr[4], pr[5]),
