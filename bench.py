@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "220cc3c7bea292ef7a99893f2fc6280ff017db7e79c64cdb6fd0049fb3418e26",
-           "fetch_bytes": 857072153, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "7b310bb3e67325a7a8c051d84495e829e6ebf488758a54851c083b7330c21017",
+           "fetch_bytes": 855860030, "write_bytes": 536870912}
 
 
 def parse():
