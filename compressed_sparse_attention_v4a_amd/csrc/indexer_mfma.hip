@@ -290,11 +290,12 @@ __global__ __launch_bounds__(256, (CAPC > 0 ? CAPC <= 1280 : CAP <= 2048) ? 2 : 
 
   // K tile fill: 16 instructions of 4 entries each; wave wv issues 4 of them (entries
   // 4 (4 wv + r) .. + 3).  The loads are written out (M0 = LDS destination, formed from this
-  // wave's part of the tile buffers plus an immediate; a 32-bit per-lane offset from the
-  // sequence's key base in scalar registers) so that the compiler does not wait for them
-  // before every later LDS read; the loop waits for them explicitly before the barrier
-  // that publishes the tile.  The offsets stay below 2^31: the launcher takes this kernel
-  // only for fewer than 2^23 visible entries.  Lanes of a load hold chunk position
+  // wave's part of the tile buffers plus an immediate; the tile's first key as the scalar
+  // base and a fixed 32-bit offset per lane, or, on the last tile, the sequence's first key
+  // and offsets clamped to the last visible entry) so that the compiler does not wait for
+  // them before every later LDS read; the loop waits for them explicitly before the
+  // barrier that publishes the tile.  The offsets stay below 2^31: the launcher takes this
+  // kernel only for fewer than 2^23 visible entries.  Lanes of a load hold chunk position
   // (lane & 15) ^ (entry & 15) of entry 4 (4 wv + r) + (lane >> 4).
   const int ewg = (int)Ewg;
   const uint32_t lds_wave = (uint32_t)(uintptr_t)(lds_void)kbuf + (uint32_t)wv * 4096u;
