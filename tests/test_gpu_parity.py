@@ -828,6 +828,8 @@ def test_decode_step_bitwise_reproducible():
     ("falling", 40000, 8, 512),      # after the first cut nothing enters
     ("integer", 60000, 24, 512),     # exact integer scores with many ties: the whole selection
     ("integer", 131008, 12, 1024),   # the same with the larger buffer at E = 32752 .. 32755
+    ("integer", 70001, 13, 512),     # ragged chunk: the last workgroup has one query, three idle waves
+    ("integer", 9001, 7, 512),       # 2250 .. 2251 entries (streamed since E > 2048), ragged
 ])
 def test_indexer_stream_bf16(case, t0, T, k):
     """Prefill chunks whose queries see more than 4096 entries: each wave streams its
