@@ -57,6 +57,8 @@ def parse():
                     help="only time one decode workload (5 cold + 5 warm rounds, for profiling)")
     ap.add_argument("--prefill-128k-only", action="store_true",
                     help="only time the 128K chunked CSA prefill")
+    ap.add_argument("--hca-only", action="store_true",
+                    help="only time the HCA prefill at n = 65536 (compressor and attention)")
     ap.add_argument("--flush-probe", action="store_true",
                     help="only measure a 128 MiB streaming read after no flush, after the "
                          "decode timing's 512 MiB write flush and after a 512 MiB read flush")
@@ -138,6 +140,12 @@ def main():
         from compressed_sparse_attention_v4a_amd import binding as B
         B.lib()
         print(json.dumps({"csa_prefill_n131072_chunked": prefill_128k_timing(torch.cuda.current_stream())}))
+        return
+    if args.hca_only:
+        import torch
+        from compressed_sparse_attention_v4a_amd import binding as B
+        B.lib()
+        print(json.dumps({"hca_prefill_n65536": hca_timing(torch.cuda.current_stream())}))
         return
     if args.decode_only:
         import torch

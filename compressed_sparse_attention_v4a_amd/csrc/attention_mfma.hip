@@ -870,6 +870,402 @@ __global__ __launch_bounds__(256) void kv576_gather_kernel(const uint8_t* kv, co
   *reinterpret_cast<uint4*>(staged + ((int64_t)b * k + u) * kC + ch0) = o;
 }
 
+
+// ---- HCA prefill: two consecutive positions per workgroup ---------------------------
+// In HCA ("CSA And HCA: Definition, State, And Cost Model", section 4) every position of
+// a block sees the same compressed prefix, and positions t and t + 1 share all but one
+// window row each, so one workgroup serves both (64 heads each) over the union of their
+// candidate lists: every gathered row feeds 128 (position, head) columns of the matrix
+// products instead of 64, and the per-chunk chain of landing, barrier and softmax is paid
+// once for both.  Candidate u of the union list is compressed entry u for u < n_B, else
+// window position lo_A + (u - n_B); position t does not see entry n_A..n_B - 1 (the block
+// that t + 1 completes) nor window position t + 1, and t + 1 does not see lo_A when its
+// window starts one later.  Those entries get a score of -inf for that position.
+//
+// Four waves, one per SIMD with the whole register file: wave w = 2 qq + hh owns heads
+// 32 hh .. 32 hh + 31 of position qq through both products, so waves share nothing but
+// the chunk buffers (one barrier per chunk):
+//   * S^T = K Q^T over all 512 channels: 2 candidate blocks x 32 k-steps of
+//     v_mfma_f32_32x32x16_bf16, query fragments resident (128 registers), loaded straight
+//     from global memory and prepared in registers (q * gamma, rotated at t; the factor
+//     scale * log2 e / rms(q) multiplies the float32 scores);
+//   * softmax in registers with the fixed reference maximum of the first chunk (and the
+//     in-place restart of the CSA kernel when a later chunk exceeds it by 2^64);
+//   * O^T = V^T P^T for all 512 channels: 16 accumulator tiles (256 accumulation
+//     registers); the score accumulators are already the P fragments of the four steps.
+constexpr int kPairWaves = 4;
+constexpr int kPairThreads = 64 * kPairWaves;
+constexpr int kPairRows = kNC / kPairWaves;  // rows of a chunk gathered by each wave
+
+// The score products accumulate in vector registers, written as inline assembly: with
+// the builtin, every product of a kernel that may use more than 256 registers takes the
+// accumulation-register form, and the 16 score registers do not fit beside the 256 of O.
+// A chain of products into the same full tile needs no wait states between them; the last
+// one waits out the product's latency before its result is read by vector instructions.
+__device__ __forceinline__ void mfma_v_first(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_last(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(acc) : "v"(a), "v"(b));
+}
+
+__global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * kChunkBytes];  // chunk buffers / output staging
+  __shared__ __attribute__((aligned(16))) float qg_s[kC];                 // query RMSNorm weights
+  __shared__ __attribute__((aligned(16))) float rope_c[2][kMaxRopeDims / 2], rope_s[2][kMaxRopeDims / 2];
+  __shared__ int flag_s[kPairWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qq = wv >> 1, hh = wv & 1;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int hgroups = a.n_h / kHG;
+  const int npairs = (a.T + 1) / 2;
+  const int64_t bh = (int64_t)a.batch * hgroups;
+  const int64_t item = blockIdx.x;
+  if (item >= bh * npairs) return;
+  // pairs run from the latest (longest lists) down
+  const int b = uni((int)((item % bh) / hgroups));
+  const int hgrp = uni((int)((item % bh) % hgroups));
+  const int qi0 = uni(2 * (npairs - 1 - (int)(item / bh)));
+  const bool pair = qi0 + 1 < a.T;  // an odd last position runs alone (both halves compute it)
+  const int64_t tA = a.t0 + qi0, tB = pair ? tA + 1 : tA;
+  const int64_t nA = (tA + 1) / a.m_prime, nB = (tB + 1) / a.m_prime;
+  const int64_t loA = tA - a.w + 1 > 0 ? tA - a.w + 1 : 0;
+  const int64_t loB = tB - a.w + 1 > 0 ? tB - a.w + 1 : 0;
+  // list positions, entries and window rows are below 2^31
+  const int nrows = uni((int)(nB + (tB - loA + 1)));
+  const int nchunks = uni((nrows + kNC - 1) / kNC);
+  const int ncomp = uni((int)nB);
+  // candidates this wave's position does not see: u in [xa, xb) and u >= lim
+  const int xa = uni(qq == 0 ? (int)nA : (int)nB);
+  const int xb = uni(qq == 0 ? (int)nB : (int)(nB + (loB - loA)));
+  const int lim = uni(qq == 0 && pair ? nrows - 1 : nrows);
+  const int64_t tq = qq ? tB : tA;
+  const int qi = pair ? qi0 + qq : qi0;
+
+  // ---- prologue: weights and chunk 0 (direct to LDS), query fragments (to registers) ----
+  // All of it is in flight together and waited for at once (the loads complete in order,
+  // so the query loads, issued last, bound the wait).
+  if (a.q_gamma) {
+    // 4-byte pieces (the weights need only float alignment): wave w loads 128 of them
+    dma_b32(a.q_gamma + 128 * wv, (uint32_t)lane << 2, qg_s + 128 * wv);
+    dma_b32(a.q_gamma + 128 * wv + 64, (uint32_t)lane << 2, qg_s + 128 * wv + 64);
+  } else {
+    qg_s[tid] = 1.0f;
+    qg_s[tid + kPairThreads] = 1.0f;
+  }
+  const char* kvc_b = reinterpret_cast<const char*>(a.kvc + (int64_t)b * a.E_cap * kC);
+  const char* kvl_b = reinterpret_cast<const char*>(a.kvl + (int64_t)b * a.n_lrows * kC);
+  const int lwin = (int)(loA - a.lrow_base);  // workspace row of window position lo_A
+  // address of list row r0 + 16 wv + (lane & 15) (lanes 0..15 matter); rows past the end
+  // of the list repeat its last row (their scores are masked)
+  auto row_addr = [&](int r0) __attribute__((always_inline)) -> uint64_t {
+    int u = r0 + kPairRows * wv + (lane & 15);
+    u = u < nrows ? u : nrows - 1;
+    return u < ncomp ? (uint64_t)kvc_b + (uint64_t)(uint32_t)u * kRowBytes
+                     : (uint64_t)kvl_b + (uint64_t)(uint32_t)(lwin + u - ncomp) * kRowBytes;
+  };
+  const uint32_t lane16 = (uint32_t)lane << 4;
+  // row 16 wv + r of a chunk: lane i carries chunk i ^ swz(r) of the global row into LDS
+  // chunk i (16 wv + r and r have the same low four bits)
+  auto gather_row = [&](uint64_t addr, char* dst, int r) __attribute__((always_inline)) {
+    const uint64_t ra = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(addr >> 32), r) << 32) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)addr, r);
+    uint32_t lo;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(lo) : "s"((uint32_t)swz(r) << 4), "v"(lane16));
+    // the LDS offset is uniform: keep it in a scalar register for M0
+    const int loff = uni((int)(dst - kvbuf) + (kPairRows * wv + r) * kRowBytes);
+    dma_b128(reinterpret_cast<const char*>(ra), lo, kvbuf + loff);
+  };
+  auto fill0 = [&]() __attribute__((always_inline)) {
+    const uint64_t addr = row_addr(0);
+#pragma unroll
+    for (int r = 0; r < kPairRows; ++r) gather_row(addr, kvbuf, r);
+  };
+  fill0();
+  // lane (hl, l32), k-step s: head 32 hh + l32, channels 16 s + 8 hl .. + 7
+  const int64_t qrow = ((int64_t)b * a.T + qi) * a.n_h + (int64_t)hgrp * kHG + 32 * hh + l32;
+  const u32x4* qsrc = reinterpret_cast<const u32x4*>(a.q + qrow * kC) + hl;
+  u32x4 qr[32];
+#pragma unroll
+  for (int s = 0; s < 32; ++s) qr[s] = qsrc[2 * s];
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < kMaxRopeDims) {
+    // angles of position tA (threads 0..31) and tB (32..63); identity without RoPE
+    const int p = tid >> 5, f = tid & 31;
+    float cs = 1.0f, sn = 0.0f;
+    if (a.rope_dims > 0) rope_cs_fast((double)(p ? tB : tA), a.rope.inv_freq[f], cs, sn);
+    rope_c[p][f] = cs;
+    rope_s[p][f] = sn;
+  }
+  wait_vmcnt<0>();
+  wait_lgkmcnt<0>();
+  block_sync();  // weights, angles and chunk 0 visible
+
+  bf16x8 qb[32];
+  float qinv;
+  {
+    float ss = 0.0f;
+    // The weights of k-step s + 2 are read once step s is done: the read address passes
+    // through an empty asm statement that takes step s's result, so the compiler cannot
+    // hoist all 64 reads (256 registers) to the top.
+    float4 gq[3][2];
+    auto gload = [&](int s, uint32_t dep) __attribute__((always_inline)) {
+      uint32_t off = (uint32_t)(16 * s + 8 * hl) * 4u;
+      asm volatile("" : "+v"(off) : "v"(dep));
+      const char* gp = reinterpret_cast<const char*>(qg_s) + off;
+      gq[s % 3][0] = *reinterpret_cast<const float4*>(gp);
+      gq[s % 3][1] = *reinterpret_cast<const float4*>(gp + 16);
+    };
+    gload(0, 0u);
+    gload(1, 0u);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const float4 g0 = gq[s % 3][0], g1 = gq[s % 3][1];
+      const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(qr[s][e] << 16), x1 = __uint_as_float(qr[s][e] & 0xFFFF0000u);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+        y[2 * e] = x0 * gm[2 * e];
+        y[2 * e + 1] = x1 * gm[2 * e + 1];
+      }
+      if (s >= 28) {
+        // pairs (16 s + 8 hl + 2 e, + 1) use frequency 8 (s - 28) + 4 hl + e
+        const float4 c4 = *reinterpret_cast<const float4*>(&rope_c[qq][8 * (s - 28) + 4 * hl]);
+        const float4 s4 = *reinterpret_cast<const float4*>(&rope_s[qq][8 * (s - 28) + 4 * hl]);
+        const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+        const float sj[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y0 = y[2 * e], y1 = y[2 * e + 1];
+          y[2 * e] = y0 * cj[e] - y1 * sj[e];
+          y[2 * e + 1] = y0 * sj[e] + y1 * cj[e];
+        }
+      }
+      const u32x4 pk = {pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]), pk_bf16(y[4], y[5]), pk_bf16(y[6], y[7])};
+      qb[s] = __builtin_bit_cast(bf16x8, pk);
+      if (s + 2 < 32) gload(s + 2, pk[0]);
+    }
+    ss += __shfl_xor(ss, 32, 64);  // the other half of the channels
+    qinv = a.q_gamma ? a.qscale / sqrtf(ss / (float)kC + a.eps) : a.qscale;
+  }
+
+  // ---- per-lane LDS offsets ---------------------------------------------------------
+  // score reads (A operand, row = candidate 32 cb + l32): k-step s reads chunk 2 s + hl,
+  // i.e. kb[s & 7] + 256 (s >> 3) + 32 KiB cb
+  int kb[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) kb[u] = l32 * kRowBytes + (((2 * u + hl) ^ swz(l32)) << 4);
+  // transposing V reads of channel tile T and step p: vb[T & 3][e] + 256 (T >> 2) + 16 KiB p
+  // (16-lane group G = lane >> 4, J = lane & 15 = 4 i + q: row 16 p + 8 e + 4 (G >> 1) + i,
+  // channels 32 T + 16 (G & 1) + 4 q .. + 3)
+  int vb[4][2];
+  {
+    const int G = lane >> 4, i = (lane & 15) >> 2, q = lane & 3;
+    const int x = 2 * (G & 1) + (q >> 1);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * e + 4 * (G >> 1) + i;
+        vb[t4][e] = row * kRowBytes + (((4 * t4 + x) ^ swz(row)) << 4) + 8 * (q & 1);
+      }
+  }
+
+  float m_ref = -INFINITY;  // head 32 hh + l32 of position qq (log2 units)
+  float mx_run = -INFINITY;
+
+  auto run = [&](f32x16 (&O)[16], float& l_part) __attribute__((always_inline)) -> bool {
+    {
+      const bf16x8 z8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      f32x16 z16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z16[i] = 0.0f;
+#pragma unroll
+      for (int T = 0; T < 16; ++T) O[T] = mfma32(z8, z8, z16);
+    }
+    l_part = 0.0f;
+    bool ovf = false;
+    // one chunk of 64 rows as two blocks of 32 (scores, softmax, P V each), so that one
+    // score accumulator tile is live at a time
+    auto chunk = [&](int c, auto more_t) __attribute__((always_inline)) {
+      constexpr bool more = decltype(more_t)::value;
+      const int r0 = c * kNC;
+      const char* buf = kvbuf + (c & 1) * kChunkBytes;
+      char* nbuf = kvbuf + ((c & 1) ^ 1) * kChunkBytes;
+      wait_vmcnt<0>();
+      block_sync();  // chunk c landed for every wave; chunk c - 1 fully consumed
+      uint64_t naddr = 0;
+      if constexpr (more) naddr = row_addr(r0 + kNC);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const char* bb = buf + 32 * kRowBytes * cb;
+        auto kread = [&](int s) __attribute__((always_inline)) -> bf16x8 { return lds_read_b128(bb, kb[s & 7] + 256 * (s >> 3)); };
+        f32x16 S;
+        constexpr int kAhead = 4;  // fragment reads in flight ahead of the products
+        bf16x8 ka[kAhead + 1];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) ka[i] = kread(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s2 = 0; s2 < 32; ++s2) {
+          if (s2 + kAhead < 32) ka[(s2 + kAhead) % (kAhead + 1)] = kread(s2 + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s2 == 0)
+            mfma_v_first(S, ka[0], qb[0]);
+          else if (s2 < 31)
+            mfma_v(S, ka[s2 % (kAhead + 1)], qb[s2]);
+          else
+            mfma_v_last(S, ka[s2 % (kAhead + 1)], qb[s2]);
+          // the next chunk's 16 rows of this wave go out one per two products of the
+          // first block, so that the last of them has three quarters of the chunk to land
+          if (more && cb == 0 && (s2 & 1)) gather_row(naddr, nbuf, s2 >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // element i: candidate r0 + 32 cb + 8 (i >> 2) + 4 hl + (i & 3), head l32
+        const int rb = r0 + 32 * cb;
+        if (__builtin_expect(rb + 32 > lim || (xa < xb && rb < xb && rb + 32 > xa), 0)) {
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int u = rb + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (u >= lim || (u >= xa && u < xb)) S[i] = -INFINITY;
+          }
+        }
+        float lmax = S[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, S[i]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax), false, false);
+          lmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * qinv;  // qinv > 0
+        }
+        mx_run = fmaxf(mx_run, lmax);
+        if (c == 0 && cb == 0) {
+          m_ref = fmaxf(m_ref, lmax);  // raised by a restart
+          if (m_ref == -INFINITY) m_ref = 0.0f;
+        } else {
+          ovf = ovf || lmax > m_ref + kLazy;
+        }
+        bf16x8 pb[2];
+        float ls = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          float pr[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(S[8 * p + e], qinv, -m_ref));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ls += pr[e];
+          const u32x4 pk = {pk_bf16(pr[0], pr[1]), pk_bf16(pr[2], pr[3]), pk_bf16(pr[4], pr[5]), pk_bf16(pr[6], pr[7])};
+          pb[p] = __builtin_bit_cast(bf16x8, pk);
+        }
+        l_part += ls;
+        // O^T[channel tile T][32 heads] += V^T P^T over the block's 2 steps of 16 candidates
+        auto vread = [&](int j) __attribute__((always_inline)) -> bf16x8 {  // j = 16 p + T, step 2 cb + p of the chunk
+          const int p = j >> 4, T = j & 15;
+          const u32x2 v1 = lds_read_tr(buf, vb[T & 3][0] + 256 * (T >> 2) + 16384 * (2 * cb + p));
+          const u32x2 v2 = lds_read_tr(buf, vb[T & 3][1] + 256 * (T >> 2) + 16384 * (2 * cb + p));
+          const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
+          return __builtin_bit_cast(bf16x8, cat);
+        };
+        bf16x8 vr[kAhead + 1];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) vr[i] = vread(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          if (j + kAhead < 32) vr[(j + kAhead) % (kAhead + 1)] = vread(j + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
+          O[j & 15] = mfma32(vr[j % (kAhead + 1)], pb[j >> 4], O[j & 15]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    for (int c = 0; c + 1 < nchunks; ++c) chunk(c, std::true_type{});
+    chunk(nchunks - 1, std::false_type{});
+    // an overflow is acted on once the pass is over (every wave restarts together)
+    {
+      const bool any = __ballot(ovf) != 0;
+      if (lane == 0) flag_s[wv] = any ? 1 : 0;
+    }
+    wait_lgkmcnt<0>();
+    block_sync();  // flags visible
+    if (!uni(flag_s[0] | flag_s[1] | flag_s[2] | flag_s[3])) return true;
+    m_ref = fmaxf(m_ref, mx_run);
+    return false;
+  };
+
+  f32x16 O[16];
+  float l_part;
+  for (;;) {
+    if (__builtin_expect(run(O, l_part), 1)) break;
+    wait_vmcnt<0>();
+    block_sync();  // every wave is done with the chunk buffers
+    fill0();
+  }
+
+  // ---- epilogue: normalise (+ sink), inverse RoPE, bf16 through LDS, whole-row stores --
+  float inv;
+  {
+    float den = l_part + __shfl_xor(l_part, 32, 64);
+    if (a.sink) den += __builtin_amdgcn_exp2f(a.sink[hgrp * kHG + 32 * hh + l32] * kLog2e - m_ref);
+    inv = 1.0f / den;
+  }
+  wait_vmcnt<0>();
+  block_sync();  // every wave is done with the chunk buffers
+  // wave wv stages its 32 heads x 512 channels in kvbuf[32 KiB wv ..]: row = head, the
+  // 16-byte chunk j of a row at position j ^ (head & 15)
+  char* tb = kvbuf + wv * 32768;
+  // lane (hl, l32) holds head l32 at channels 32 T + 8 j + 4 hl + (0..3) in O[T][4 j .. + 3]
+#pragma unroll
+  for (int T = 0; T < 16; ++T) {
+    uint32_t pk[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x[4] = {O[T][4 * j] * inv, O[T][4 * j + 1] * inv, O[T][4 * j + 2] * inv, O[T][4 * j + 3] * inv};
+      if (T >= 14) {
+        // pairs (ch, ch + 1), ch = 32 T + 8 j + 4 hl + 2 e, frequency (ch - 448) / 2
+        const int f = 16 * (T - 14) + 4 * j + 2 * hl;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float cs = rope_c[qq][f + e], sn = rope_s[qq][f + e];
+          const float x0 = x[2 * e], x1 = x[2 * e + 1];
+          x[2 * e] = x0 * cs + x1 * sn;
+          x[2 * e + 1] = x1 * cs - x0 * sn;
+        }
+      }
+      pk[j][0] = pk_bf16(x[0], x[1]);
+      pk[j][1] = pk_bf16(x[2], x[3]);
+    }
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      // the lower half keeps group 2 jp and takes the upper half's; the upper half keeps
+      // group 2 jp + 1 and takes the lower half's: channels 32 T + 16 jp + 8 hl .. + 7
+      const auto w0 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][0], pk[2 * jp + 1][0], false, false);
+      const auto w1 = __builtin_amdgcn_permlane32_swap(pk[2 * jp][1], pk[2 * jp + 1][1], false, false);
+      const u32x4 v = {w0[0], w1[0], w0[1], w1[1]};
+      const int cidx = 4 * T + 2 * jp + hl;
+      *reinterpret_cast<u32x4*>(tb + l32 * kRowBytes + ((cidx ^ (l32 & 15)) << 4)) = v;
+    }
+  }
+  asm volatile("" ::: "memory");  // LDS operations of a wave complete in order
+  if (qq == 0 || pair) {
+    uint16_t* dst = a.out + (((int64_t)b * a.T + qi) * a.n_h + (int64_t)hgrp * kHG + 32 * hh) * kC;
+#pragma unroll 4
+    for (int h = 0; h < 32; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tb + h * kRowBytes + ((lane ^ (h & 15)) << 4));
+      *reinterpret_cast<u32x4*>(dst + (int64_t)h * kC + 8 * lane) = v;
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- host side --
@@ -1073,11 +1469,14 @@ hipError_t launch_attention_mfma(const AttnArgs& a, void* ws, hipStream_t s) {
     return launch_attention_merge(a, part, s);
   }
   m.splits = 1;
+  if (a.mode == kModeHCA) {
+    // two consecutive positions per workgroup
+    const unsigned grid = (unsigned)((int64_t)a.batch * hgroups * ((a.T + 1) / 2));
+    hipLaunchKernelGGL(hca_pair_kernel, dim3(grid), dim3(kPairThreads), 0, s, m);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)((int64_t)a.batch * hgroups * a.T);
-  if (a.mode == kModeHCA)
-    hipLaunchKernelGGL(mqa_mfma_kernel<kModeHCA>, dim3(grid), dim3(kThreads), 0, s, m);
-  else
-    hipLaunchKernelGGL(mqa_mfma_kernel<kModeCSA>, dim3(grid), dim3(kThreads), 0, s, m);
+  hipLaunchKernelGGL(mqa_mfma_kernel<kModeCSA>, dim3(grid), dim3(kThreads), 0, s, m);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ def assert_close(got, ref, *, atol=0.0, rtol=0.0, what=""):
                              f"{i}: got {got[i]!r} ref {ref[i]!r} err {err[i]:.3g} bound {bound[i]:.3g}")
 
 
-def assert_attn_close(got, ref, *, atol, rel_rms, what=""):
+def assert_attn_close(got, ref, *, atol, rel_rms, rtol=0.0, what=""):
     """Attention outputs: every element within `atol` (the element-wise gate), and every
     output row (one query, one head: the last axis) within `rel_rms` of the row's RMS in RMS
     error, plus atol / 16 for rows that are nearly zero.
@@ -39,10 +39,12 @@ def assert_attn_close(got, ref, *, atol, rel_rms, what=""):
     averaged over hundreds of candidates are only ~0.05 in size, so a row that loses or
     double-counts a tenth of its softmax mass can stay within an absolute 2e-2.  The bf16
     path rounds the normalised query, the probabilities and the output to 8 significant
-    bits (2^-9 relative each), which puts its RMS error near 0.5 % of the row's RMS."""
+    bits (2^-9 relative each), which puts its RMS error near 0.5 % of the row's RMS.
+    `rtol` widens the element gate by a multiple of |ref| where one or two candidates carry
+    the whole softmax (see the callers)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    assert_close(got, ref, atol=atol, what=what)
+    assert_close(got, ref, atol=atol, rtol=rtol, what=what)
     n = ref.shape[-1]
     e = np.sqrt(np.mean((got - ref) ** 2, axis=-1))
     r = np.sqrt(np.mean(ref ** 2, axis=-1))

@@ -471,6 +471,48 @@ def test_hca_attn_bf16(n, n_h, c, mp, w, t0, sink):
                       rel_rms=REL_RMS_BF16, what="hca")
 
 
+@pytest.mark.parametrize("n,n_h,mp,w,t0,sink", [(301, 64, 1, 16, 199, True),
+                                                (257, 128, 4, 1, 0, False),
+                                                (130, 64, 2, 128, 1, True),
+                                                (67, 64, 128, 70, 990, False)])
+def test_hca_attn_position_pairs(n, n_h, mp, w, t0, sink):
+    """The matrix-core HCA kernel serves positions t and t + 1 together over the union of
+    their candidate lists (an odd last position alone).  Each case makes the two positions
+    of a pair differ: with m' = 1 or 2 (and at t + 1 = 1024 for m' = 128) the second sees
+    one more compressed entry than the first; with a window shorter than the position the
+    first sees one window row the second does not, and with w = 1 each sees only its own
+    row.  Odd starts and counts, two head groups, non-unit RMSNorm weights; the first and
+    last positions and those around entry completions are all checked.  With one or two
+    candidates per position the output is one or two rows themselves (up to ~5 in size
+    with these weights), not an average near zero, so the element gate adds 2^-7 |ref|: the
+    output, the probabilities and the query are each rounded to bf16 (2^-9 relative), and
+    each of those errors scales with the size of the rows that carry the softmax."""
+    c = 512
+    rng = np.random.default_rng(1000 + n)
+    E = (t0 + n) // mp
+    lb = max(0, t0 - w + 1)
+    sc = 1 / math.sqrt(c)
+    q = synth.formats.bf16_bits(sc * rng.standard_normal((n, n_h, c)))
+    kv = synth.formats.bf16_bits(rng.standard_normal((E + 1, c)))
+    local = synth.formats.bf16_bits(sc * rng.standard_normal((t0 + n - lb, c)))
+    g = (1.0 + 0.25 * rng.standard_normal(c)).astype(np.float32)
+    gk = (1.0 + 0.25 * rng.standard_normal(c)).astype(np.float32)
+    sk = rng.standard_normal(n_h).astype(np.float32) if sink else None
+    log(f"hca attn position pairs n={n} n_h={n_h} m'={mp} w={w} t0={t0}")
+    out = ops.hca_attn(up(q), up(kv), up(local), t0=t0, m_prime=mp, w=w, dt="bf16", loc_base=lb,
+                       sink=None if sk is None else up(sk), q_gamma=up(g), kv_gamma=up(gk),
+                       rope_dims=64)
+    torch.cuda.synchronize()
+    done = [r for r in range(n) if (t0 + r + 1) % mp in (0, 1, mp - 1)][:24]
+    rows = np.unique(np.concatenate([np.arange(12), np.arange(n - 12, n), np.array(done, int),
+                                     np.random.default_rng(5).integers(0, n, 24)]))
+    ref = oracle.attend_hca(f64(q, "bf16"), f64(kv, "bf16"), f64(local, "bf16"), loc_base=lb,
+                            t0=t0, m_prime=mp, w=w, sink=sk, q_gamma=g, kv_gamma=gk, q_norm=True,
+                            kv_norm=True, rope_dims=64, rows=rows)
+    assert_attn_close(decode_stored(out[0], "bf16")[rows], ref, atol=ATOL_BF16,
+                      rel_rms=REL_RMS_BF16, rtol=2.0 ** -7, what="hca pairs")
+
+
 def test_hca_prefill_flash_64k_sampled():
     """Full V4-Flash HCA prefill at n=65536: compressor then dense attention."""
     cfg = synth.configs.workload("hca_prefill_flash_64k")
