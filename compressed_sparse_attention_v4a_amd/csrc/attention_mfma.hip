@@ -948,9 +948,8 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
   const int64_t tq = qq ? tB : tA;
   const int qi = pair ? qi0 + qq : qi0;
 
-  // ---- prologue: weights and chunk 0 (direct to LDS), query fragments (to registers) ----
-  // All of it is in flight together and waited for at once (the loads complete in order,
-  // so the query loads, issued last, bound the wait).
+  // ---- prologue: query rows and weights (direct to LDS), query fragments (to registers),
+  // then chunk 0 (direct to LDS) in flight while the fragments are prepared ----
   if (a.q_gamma) {
     // 4-byte pieces (the weights need only float alignment): wave w loads 128 of them
     dma_b32(a.q_gamma + 128 * wv, (uint32_t)lane << 2, qg_s + 128 * wv);
@@ -987,14 +986,21 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
 #pragma unroll
     for (int r = 0; r < kPairRows; ++r) gather_row(addr, kvbuf, r);
   };
-  fill0();
-  // lane (hl, l32), k-step s: head 32 hh + l32, channels 16 s + 8 hl .. + 7
-  const int64_t qrow = ((int64_t)b * a.T + qi) * a.n_h + (int64_t)hgrp * kHG + 32 * hh + l32;
-  const u32x4* qsrc = reinterpret_cast<const u32x4*>(a.q + qrow * kC) + hl;
-  u32x4 qr[32];
+  // the 128 query rows (row R = 64 p + h: head h of position p, in chunk buffer p), one
+  // whole 1 KiB row per load, 16-byte chunks swizzled like candidate rows
+  {
+    const int qi1 = pair ? qi0 + 1 : qi0;
 #pragma unroll
-  for (int s = 0; s < 32; ++s) qr[s] = qsrc[2 * s];
-  __builtin_amdgcn_sched_barrier(0);
+    for (int r = 0; r < 32; ++r) {
+      const int R = 32 * wv + r;
+      const int qsel = R < kHG ? qi0 : qi1;
+      const char* src = reinterpret_cast<const char*>(
+          a.q + (((int64_t)b * a.T + qsel) * a.n_h + (int64_t)hgrp * kHG + (R & (kHG - 1))) * kC);
+      uint32_t lo;
+      asm volatile("v_xor_b32 %0, %1, %2" : "=v"(lo) : "s"((uint32_t)swz(r) << 4), "v"(lane16));
+      dma_b128(src, lo, kvbuf + R * kRowBytes);
+    }
+  }
   if (tid < kMaxRopeDims) {
     // angles of position tA (threads 0..31) and tB (32..63); identity without RoPE
     const int p = tid >> 5, f = tid & 31;
@@ -1005,35 +1011,48 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
   }
   wait_vmcnt<0>();
   wait_lgkmcnt<0>();
-  block_sync();  // weights, angles and chunk 0 visible
+  block_sync();  // query rows, weights and angles visible
+  // lane (hl, l32), k-step s: head 32 hh + l32 of position qq, channels 16 s + 8 hl .. + 7
+  // (the score reads' pattern on row 32 hh + l32 of chunk buffer qq)
+  u32x4 qr[32];
+  {
+    const char* qbase = kvbuf + qq * kChunkBytes + (32 * hh + l32) * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < 32; ++s)
+      qr[s] = __builtin_bit_cast(u32x4, lds_read_b128(qbase, ((((2 * (s & 7) + hl) ^ swz(l32)) << 4) + 256 * (s >> 3))));
+  }
+  wait_lgkmcnt<0>();
+  block_sync();  // every wave holds its fragments: the buffers take chunk 0
+  fill0();
 
   bf16x8 qb[32];
   float qinv;
   {
-    float ss = 0.0f;
-    // The weights of k-step s + 2 are read once step s is done: the read address passes
+    float ssp[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};  // eight short chains
+    // The weights of k-step s + kG are read once step s is done: the read address passes
     // through an empty asm statement that takes step s's result, so the compiler cannot
     // hoist all 64 reads (256 registers) to the top.
-    float4 gq[3][2];
+    constexpr int kG = 2;
+    float4 gq[kG + 1][2];
     auto gload = [&](int s, uint32_t dep) __attribute__((always_inline)) {
       uint32_t off = (uint32_t)(16 * s + 8 * hl) * 4u;
       asm volatile("" : "+v"(off) : "v"(dep));
       const char* gp = reinterpret_cast<const char*>(qg_s) + off;
-      gq[s % 3][0] = *reinterpret_cast<const float4*>(gp);
-      gq[s % 3][1] = *reinterpret_cast<const float4*>(gp + 16);
+      gq[s % (kG + 1)][0] = *reinterpret_cast<const float4*>(gp);
+      gq[s % (kG + 1)][1] = *reinterpret_cast<const float4*>(gp + 16);
     };
-    gload(0, 0u);
-    gload(1, 0u);
+#pragma unroll
+    for (int s = 0; s < kG; ++s) gload(s, 0u);
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
-      const float4 g0 = gq[s % 3][0], g1 = gq[s % 3][1];
+      const float4 g0 = gq[s % (kG + 1)][0], g1 = gq[s % (kG + 1)][1];
       const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       float y[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x0 = __uint_as_float(qr[s][e] << 16), x1 = __uint_as_float(qr[s][e] & 0xFFFF0000u);
-        ss = fmaf(x0, x0, ss);
-        ss = fmaf(x1, x1, ss);
+        ssp[2 * e] = fmaf(x0, x0, ssp[2 * e]);
+        ssp[2 * e + 1] = fmaf(x1, x1, ssp[2 * e + 1]);
         y[2 * e] = x0 * gm[2 * e];
         y[2 * e + 1] = x1 * gm[2 * e + 1];
       }
@@ -1052,8 +1071,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
       }
       const u32x4 pk = {pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]), pk_bf16(y[4], y[5]), pk_bf16(y[6], y[7])};
       qb[s] = __builtin_bit_cast(bf16x8, pk);
-      if (s + 2 < 32) gload(s + 2, pk[0]);
+      if (s + kG < 32) gload(s + kG, pk[0]);
     }
+    float ss = ((ssp[0] + ssp[1]) + (ssp[2] + ssp[3])) + ((ssp[4] + ssp[5]) + (ssp[6] + ssp[7]));
     ss += __shfl_xor(ss, 32, 64);  // the other half of the channels
     qinv = a.q_gamma ? a.qscale / sqrtf(ss / (float)kC + a.eps) : a.qscale;
   }
@@ -1105,19 +1125,22 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
       block_sync();  // chunk c landed for every wave; chunk c - 1 fully consumed
       uint64_t naddr = 0;
       if constexpr (more) naddr = row_addr(r0 + kNC);
+      constexpr int kAhead = 4;  // fragment reads in flight ahead of the products
+      // score fragment s of block cb (rows 32 cb ..)
+      auto kread = [&](int cb, int s) __attribute__((always_inline)) -> bf16x8 {
+        return lds_read_b128(buf, kb[s & 7] + 256 * (s >> 3) + 32 * kRowBytes * cb);
+      };
+      bf16x8 ka[kAhead + 1];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) ka[i] = kread(0, i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const char* bb = buf + 32 * kRowBytes * cb;
-        auto kread = [&](int s) __attribute__((always_inline)) -> bf16x8 { return lds_read_b128(bb, kb[s & 7] + 256 * (s >> 3)); };
+        // (the first fragments of block 1 were read during block 0's P V)
         f32x16 S;
-        constexpr int kAhead = 4;  // fragment reads in flight ahead of the products
-        bf16x8 ka[kAhead + 1];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) ka[i] = kread(i);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s2 = 0; s2 < 32; ++s2) {
-          if (s2 + kAhead < 32) ka[(s2 + kAhead) % (kAhead + 1)] = kread(s2 + kAhead);
+          if (s2 + kAhead < 32) ka[(s2 + kAhead) % (kAhead + 1)] = kread(cb, s2 + kAhead);
           __builtin_amdgcn_sched_barrier(0);
           if (s2 == 0)
             mfma_v_first(S, ka[0], qb[0]);
@@ -1130,6 +1153,19 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
           if (more && cb == 0 && (s2 & 1)) gather_row(naddr, nbuf, s2 >> 1);
           __builtin_amdgcn_sched_barrier(0);
         }
+        // the first V fragments of the block's P V go out before the softmax, which they do
+        // not depend on
+        auto vread = [&](int j) __attribute__((always_inline)) -> bf16x8 {  // j = 16 p + T, step 2 cb + p of the chunk
+          const int p = j >> 4, T = j & 15;
+          const u32x2 v1 = lds_read_tr(buf, vb[T & 3][0] + 256 * (T >> 2) + 16384 * (2 * cb + p));
+          const u32x2 v2 = lds_read_tr(buf, vb[T & 3][1] + 256 * (T >> 2) + 16384 * (2 * cb + p));
+          const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
+          return __builtin_bit_cast(bf16x8, cat);
+        };
+        bf16x8 vr[kAhead + 1];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) vr[i] = vread(i);
+        __builtin_amdgcn_sched_barrier(0);
         // element i: candidate r0 + 32 cb + 8 (i >> 2) + 4 hl + (i & 3), head l32
         const int rb = r0 + 32 * cb;
         if (__builtin_expect(rb + 32 > lim || (xa < xb && rb < xb && rb + 32 > xa), 0)) {
@@ -1168,22 +1204,13 @@ __global__ __launch_bounds__(kPairThreads, 1) void hca_pair_kernel(MqaArgs a) {
         }
         l_part += ls;
         // O^T[channel tile T][32 heads] += V^T P^T over the block's 2 steps of 16 candidates
-        auto vread = [&](int j) __attribute__((always_inline)) -> bf16x8 {  // j = 16 p + T, step 2 cb + p of the chunk
-          const int p = j >> 4, T = j & 15;
-          const u32x2 v1 = lds_read_tr(buf, vb[T & 3][0] + 256 * (T >> 2) + 16384 * (2 * cb + p));
-          const u32x2 v2 = lds_read_tr(buf, vb[T & 3][1] + 256 * (T >> 2) + 16384 * (2 * cb + p));
-          const u32x4 cat = {v1.x, v1.y, v2.x, v2.y};
-          return __builtin_bit_cast(bf16x8, cat);
-        };
-        bf16x8 vr[kAhead + 1];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) vr[i] = vread(i);
-        __builtin_amdgcn_sched_barrier(0);
+        // (the first V fragments were read before the softmax)
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
           if (j + kAhead < 32) vr[(j + kAhead) % (kAhead + 1)] = vread(j + kAhead);
           __builtin_amdgcn_sched_barrier(0);
           O[j & 15] = mfma32(vr[j % (kAhead + 1)], pb[j >> 4], O[j & 15]);
+          if (cb == 0 && j >= 32 - kAhead) ka[j - (32 - kAhead)] = kread(1, j - (32 - kAhead));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
