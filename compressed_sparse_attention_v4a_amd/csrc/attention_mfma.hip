@@ -1,5 +1,6 @@
 // Shared-KV MQA attention on the gfx950 matrix cores (bf16, c = 512, heads in
-// groups of 64): CSA prefill, CSA decode (candidate splits) and HCA prefill.
+// groups of 64): CSA prefill, CSA and HCA decode (candidate splits) in mqa_mfma_kernel,
+// HCA prefill in hca_pair_kernel (two positions per workgroup, further below).
 //
 // What it computes is the core attention of "CSA And HCA: Definition, State,
 // And Cost Model" (sections 3.2, 4, 5.1-5.3): per query position t and head h,
