@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0
 # counter reads on a plain device copy of known size (--copy-calibration).  Valid only
 # for the kernel source it was measured on: with any other source the figure is null.
 TRAFFIC_SOURCE = "compressed_sparse_attention_v4a_amd/csrc/attention_mfma.hip"
-TRAFFIC = {"sha256": "7b310bb3e67325a7a8c051d84495e829e6ebf488758a54851c083b7330c21017",
-           "fetch_bytes": 855860030, "write_bytes": 536870912}
+TRAFFIC = {"sha256": "6703895aaae0139fce09bcfcb0e5c353c9ab792dca25f4e3c05fd18b586d3406",
+           "fetch_bytes": 852578190, "write_bytes": 536870912}
 
 
 def parse():
