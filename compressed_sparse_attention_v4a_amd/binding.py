@@ -11,7 +11,8 @@ import ctypes as ct
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libv4a.so")
+# V4A_LIB names another build of the same library (the host-sanitizer checking build)
+LIB_PATH = os.environ.get("V4A_LIB") or os.path.join(_HERE, "libv4a.so")
 
 F32, BF16, FP8_E4M3, MXFP4, KV576 = 0, 1, 2, 3, 4
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4, "kv576": KV576}

@@ -31,10 +31,16 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for a checking build of the
+# host code (argument validation, layouts, the C ABI); device code is compiled as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + COMMON
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC] + COMMON + list(extra)
     if src.endswith(".hip"):
         cmd += ["-x", "hip"] + DEVICE
     else:
@@ -46,22 +52,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source and link the library.  sanitize=True builds the host code with
+    ASan and UBSan (a checking build for the host tests, written to `out`)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    extra = HOST_SANITIZE if sanitize else []
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + [
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + extra + objs + [
         "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(LIB)
-    return LIB
+        print(out)
+    return out
 
 
 if __name__ == "__main__":

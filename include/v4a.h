@@ -67,7 +67,13 @@ extern "C" {
  *                  bytes per row (576 at c = 512, rope_dims = 64).  Compressor output
  *                  and decode-step cache format only.
  */
-typedef enum { V4A_F32 = 0, V4A_BF16 = 1, V4A_FP8_E4M3 = 2, V4A_MXFP4 = 3, V4A_KV576 = 4 } v4a_dtype;
+/* V4A_DTYPE_RANGE_ only widens the enumeration to every 32-bit value, so that a caller's
+ * out-of-range code reaches the library's validation (V4A_ENOTSUP) as a valid value of the
+ * type; it is not a data type. */
+typedef enum {
+  V4A_F32 = 0, V4A_BF16 = 1, V4A_FP8_E4M3 = 2, V4A_MXFP4 = 3, V4A_KV576 = 4,
+  V4A_DTYPE_RANGE_ = 0x7fffffff
+} v4a_dtype;
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 V4A_API const char* v4a_last_error(void);

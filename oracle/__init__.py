@@ -39,8 +39,9 @@ _i64 = ct.POINTER(ct.c_int64)
 def lib():
     global _lib
     if _lib is None:
-        path = _build.library_path()
-        if not os.path.exists(path) or _build.is_stale():
+        # V4A_ORACLE_LIB names another build of the oracle (the sanitizer checking build)
+        path = os.environ.get("V4A_ORACLE_LIB") or _build.library_path()
+        if not os.environ.get("V4A_ORACLE_LIB") and (not os.path.exists(path) or _build.is_stale()):
             _build.build()
         L = ct.CDLL(path)
         I64, INT, DBL = ct.c_int64, ct.c_int, ct.c_double

@@ -17,11 +17,15 @@ def is_stale() -> bool:
     return not os.path.exists(lp) or os.path.getmtime(lp) < os.path.getmtime(SRC)
 
 
-def build() -> str:
-    out = library_path()
+def build(sanitize: bool = False, out: str | None = None) -> str:
+    """sanitize=True: an ASan + UBSan checking build (written to `out`), same arithmetic."""
+    out = out or library_path()
     tmp = out + ".tmp"
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer"] if sanitize else []
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Wextra", "-Wno-unused-parameter", "-shared", "-fPIC", SRC, "-o", tmp, "-lm"]
+           "-Wall", "-Wextra", "-Wno-unused-parameter"] + san + ["-shared", "-fPIC", SRC, "-o",
+                                                              tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
