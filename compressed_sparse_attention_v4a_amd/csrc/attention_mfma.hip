@@ -886,14 +886,15 @@ __global__ __launch_bounds__(256) void kv576_gather_kernel(const uint8_t* kv, co
 // Four waves, one per SIMD with the whole register file: wave w = 2 qq + hh owns heads
 // 32 hh .. 32 hh + 31 of position qq through both products, so waves share nothing but
 // the chunk buffers (one barrier per chunk):
-//   * S^T = K Q^T over all 512 channels: 2 candidate blocks x 32 k-steps of
-//     v_mfma_f32_32x32x16_bf16, query fragments resident (128 registers), loaded straight
-//     from global memory and prepared in registers (q * gamma, rotated at t; the factor
+//   * S^T = K Q^T over all 512 channels, one 32-row block of a 64-row chunk at a time:
+//     32 k-steps of v_mfma_f32_32x32x16_bf16, query fragments resident (128 registers;
+//     the rows land in LDS by whole-row direct loads, each wave reads its fragments and
+//     prepares them in registers: q * gamma, rotated at t; the factor
 //     scale * log2 e / rms(q) multiplies the float32 scores);
-//   * softmax in registers with the fixed reference maximum of the first chunk (and the
-//     in-place restart of the CSA kernel when a later chunk exceeds it by 2^64);
+//   * softmax in registers with the fixed reference maximum of the first block (and the
+//     in-place restart of the CSA kernel when a later block exceeds it by 2^64);
 //   * O^T = V^T P^T for all 512 channels: 16 accumulator tiles (256 accumulation
-//     registers); the score accumulators are already the P fragments of the four steps.
+//     registers); a block's score accumulator is already the P fragment of its two steps.
 constexpr int kPairWaves = 4;
 constexpr int kPairThreads = 64 * kPairWaves;
 constexpr int kPairRows = kNC / kPairWaves;  // rows of a chunk gathered by each wave
